@@ -1,0 +1,122 @@
+"""Planted mistakes: each test swaps one oracle function for a plausibly
+wrong variant (on the CPU only) and checks that at least one pin fails.
+This is evidence that the pins in test_oracle_pins.py constrain the oracle
+and are not restatements of it."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.hyb_oracle as ho
+import tests.test_oracle_pins as pins
+
+FAIL = (AssertionError, ValueError, IndexError)
+
+
+def _kept_ties_high(group_bits):
+    g = np.asarray(group_bits, dtype=np.uint16)
+    key = (g & 0x7FFF).astype(np.int64)
+    order = np.argsort(-(key * 4 + np.arange(4)), axis=-1, kind="stable")
+    return np.minimum(order[..., 0], order[..., 1]), np.maximum(order[..., 0], order[..., 1])
+
+
+def _kept_signed(group_bits):
+    g = np.asarray(group_bits, dtype=np.uint16).view(np.int16).astype(np.int64)
+    order = np.argsort(-(g * 4 + (3 - np.arange(4))), axis=-1, kind="stable")
+    return np.minimum(order[..., 0], order[..., 1]), np.maximum(order[..., 0], order[..., 1])
+
+
+def _nibble_swapped(i0, i1, meta):
+    i0 = np.asarray(i0, dtype=np.int64)
+    i1 = np.asarray(i1, dtype=np.int64)
+    if meta == "idx2":
+        return (i1 | (i0 << 2)).astype(np.uint8)
+    return ((1 << i0) | (1 << i1)).astype(np.uint8)
+
+
+def _value_index_j_swapped(s, r, g, j, b1, b2):
+    return (s * (b1 * b2 // 2) + (r // 16) * 8 * b2 + (g // 16) * 512
+            + ((g % 16) // 4) * 128 + (r % 16) * 8 + (g % 4) * 2 + (1 - j))
+
+
+def _meta_word_blocks_outer(s, r, g, b1, b2):
+    return (s * (b1 * b2 // 16) + (r // 16) * b2
+            + (g // 16) * 64 + ((g % 16) // 4) * 16 + r % 16)
+
+
+def _dense_index_rows_cols(s, r, c, b1, b2):
+    return (s * b1 * b2 + (r // 16) * 16 * b2 + (c // 32) * 512
+            + (r % 16) * 32 + c % 32)
+
+
+def _ref_transposed(wp_bits, x_bits, dtype):
+    w = ho.widen(wp_bits, dtype)
+    x = ho.widen(np.atleast_2d(np.asarray(x_bits, dtype=np.uint16)), dtype)
+    return x @ w, np.abs(x) @ np.abs(w)
+
+
+def _ref_reversed_rows(wp_bits, x_bits, dtype):
+    w = ho.widen(wp_bits, dtype)
+    x = ho.widen(np.atleast_2d(np.asarray(x_bits, dtype=np.uint16)), dtype)
+    return (x @ w.T)[:, ::-1], np.abs(x) @ np.abs(w).T
+
+
+def _ref_drop_last(wp_bits, x_bits, dtype):
+    w = ho.widen(wp_bits, dtype)[:, :-1]
+    x = ho.widen(np.atleast_2d(np.asarray(x_bits, dtype=np.uint16)), dtype)[:, :-1]
+    return x @ w.T, np.abs(x) @ np.abs(w).T
+
+
+def _ref_signed_bound(wp_bits, x_bits, dtype):
+    w = ho.widen(wp_bits, dtype)
+    x = ho.widen(np.atleast_2d(np.asarray(x_bits, dtype=np.uint16)), dtype)
+    return x @ w.T, np.abs(x @ w.T)
+
+
+def _prune_keeps_three(w_bits, tile_map, b1, b2):
+    w = np.asarray(w_bits, dtype=np.uint16)
+    n, k = w.shape
+    tn_count, tk_count = ho.check_shape(n, k, b1, b2)
+    tmap = np.asarray(tile_map, dtype=np.uint8).reshape(tn_count, tk_count)
+    out = w.copy()
+    for tn in range(tn_count):
+        for tk in range(tk_count):
+            if tmap[tn, tk]:
+                g = out[tn * b1:(tn + 1) * b1, tk * b2:(tk + 1) * b2].reshape(b1, b2 // 4, 4)
+                key = (g & 0x7FFF).astype(np.int64)
+                low = np.argmin(key * 4 + np.arange(4), axis=-1)
+                np.put_along_axis(g, low[..., None], np.uint16(0), axis=-1)
+    return out
+
+
+@pytest.mark.parametrize("name,func", [("kept_positions", _kept_ties_high),
+                                       ("kept_positions", _kept_signed),
+                                       ("nibble", _nibble_swapped)])
+def test_group_rule_mutations_caught(monkeypatch, golden_dir, name, func):
+    monkeypatch.setattr(ho, name, func)
+    monkeypatch.setattr(oracle, name, func)
+    with pytest.raises(FAIL):
+        pins.test_golden_groups(golden_dir)
+
+
+@pytest.mark.parametrize("name,func", [("value_index", _value_index_j_swapped),
+                                       ("meta_word_index", _meta_word_blocks_outer),
+                                       ("dense_index", _dense_index_rows_cols)])
+def test_layout_mutations_caught(monkeypatch, name, func):
+    monkeypatch.setattr(ho, name, func)
+    with pytest.raises(FAIL):
+        pins.test_layout_restatement(32, 128, "idx2")
+
+
+@pytest.mark.parametrize("func", [_ref_transposed, _ref_reversed_rows, _ref_drop_last, _ref_signed_bound])
+def test_reference_mutations_caught(monkeypatch, func):
+    monkeypatch.setattr(ho, "ref_matmul", func)
+    monkeypatch.setattr(oracle, "ref_matmul", func)
+    with pytest.raises(FAIL):
+        pins.test_ref_matmul_fsum("bf16")
+
+
+def test_prune_mutation_caught(monkeypatch):
+    monkeypatch.setattr(ho, "prune", _prune_keeps_three)
+    monkeypatch.setattr(oracle, "prune", _prune_keeps_three)
+    with pytest.raises(FAIL):
+        pins.test_invariants(3, "idx2")

@@ -1,0 +1,357 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+hand-derived group cases (tests/golden), an exhaustive brute force of the
+kept-pair rule, a restatement of the HYB1 stream layout in lane/chunk terms,
+exact matmul closed forms, math.fsum brute force, and the invariants the pages
+state (PATCH section 2: dense tiles untouched, sparse tiles exactly half kept,
+six patterns; SparseDecoding abstract: fixed stride, bitmask metadata)."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from matmul_pack_b1_amd import workloads as wl
+
+
+def load_golden_groups(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "groups_2of4.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            dtype = parts[0]
+            bits = [int(h, 16) for h in parts[1:5]]
+            i0, i1 = int(parts[5]), int(parts[6])
+            idx2, mask4 = int(parts[7], 16), int(parts[8], 16)
+            rows.append((dtype, bits, i0, i1, idx2, mask4))
+    return rows
+
+
+# ----------------------------------------------------------- group rule ----
+
+def test_golden_groups(golden_dir):
+    rows = load_golden_groups(golden_dir)
+    assert len(rows) >= 20
+    for dtype, bits, i0, i1, idx2, mask4 in rows:
+        a, b = oracle.kept_positions(np.array(bits, dtype=np.uint16))
+        assert (int(a), int(b)) == (i0, i1), (dtype, [hex(x) for x in bits])
+        assert int(oracle.nibble(a, b, "idx2")) == idx2
+        assert int(oracle.nibble(a, b, "mask4")) == mask4
+
+
+def _float_magnitude_rank(bits, dtype):
+    """Magnitude as an orderable float: NaN -> +inf+1 rank, computed from the
+    widened value (independent of the integer-key trick)."""
+    v = float(oracle.widen(np.array([bits], dtype=np.uint16), dtype)[0])
+    if math.isnan(v):
+        return (2, 0.0)
+    if math.isinf(v):
+        return (1, 0.0)
+    return (0, abs(v))
+
+
+def test_kept_rule_exhaustive_alphabet():
+    """All 8^4 groups over an alphabet with ties, +-0, subnormals, +-Inf and
+    NaN: the oracle's integer-key rule equals a float-magnitude sort."""
+    for dtype, alphabet in (
+        ("bf16", [0x0000, 0x8000, 0x0001, 0x8001, 0x3F80, 0xBF80, 0x7F80, 0x7FC0]),
+        ("f16", [0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0xBC00, 0x7C00, 0x7E00]),
+    ):
+        groups = np.array(list(itertools.product(alphabet, repeat=4)), dtype=np.uint16)
+        i0, i1 = oracle.kept_positions(groups)
+        for g, a, b in zip(groups.tolist(), i0.tolist(), i1.tolist()):
+            ranks = [_float_magnitude_rank(x, dtype) for x in g]
+            order = sorted(range(4), key=lambda p: (tuple(-v for v in ranks[p]), p))
+            assert (a, b) == tuple(sorted(order[:2])), (dtype, [hex(x) for x in g])
+
+
+def test_six_patterns_and_bijection():
+    """Exactly six valid nibbles per kind (PATCH: one of six patterns), and
+    idx2 <-> mask4 is a bijection between them."""
+    idx2 = {int(oracle.nibble(a, b, "idx2")) for a, b in itertools.combinations(range(4), 2)}
+    mask4 = {int(oracle.nibble(a, b, "mask4")) for a, b in itertools.combinations(range(4), 2)}
+    assert idx2 == {0x4, 0x8, 0xC, 0x9, 0xD, 0xE}
+    assert mask4 == {0x3, 0x5, 0x9, 0x6, 0xA, 0xC}
+    for m in mask4:
+        assert bin(m).count("1") == 2
+    for kind in oracle.META_KINDS:
+        for nib in range(16):
+            valid = nib in (idx2 if kind == "idx2" else mask4)
+            if valid:
+                a, b = oracle.positions_from_nibble(np.array([nib]), kind)
+                assert int(oracle.nibble(a[0], b[0], kind)) == nib
+            else:
+                with pytest.raises(ValueError):
+                    oracle.positions_from_nibble(np.array([nib]), kind)
+
+
+# ------------------------------------------------------ layout restatement --
+
+def _layout_by_lanes(w, tile_map, b1, b2, meta):
+    """Independent pure-Python statement of the HYB1 streams, written in
+    chunk/lane terms instead of index formulas:
+      a dense tile is a sequence of 1 KiB chunks; chunks walk the tile's
+      16-row slabs top to bottom and, inside a slab, 32-column blocks left to
+      right; chunk lane L (0..63) holds 8 consecutive columns
+      8*(L//16) .. +7 of the block, of slab row L % 16;
+      a sparse tile is a sequence of 1 KiB value chunks over 16-row slabs and
+      64-column blocks; lane L holds the 8 kept values of the four groups
+      4*(L//16) .. +3 of the block, row L % 16, each group's pair in position
+      order; the slab's metadata is 64 lanes x (b2/64) 16-bit words, lane L's
+      words for blocks 0, 1, ... back to back, nibble q of a word for the
+      lane's q-th group."""
+    n, k = w.shape
+    tn_count, tk_count = n // b1, k // b2
+    dense, val, words, tidx = [], [], [], []
+    for tn in range(tn_count):
+        for tk in range(tk_count):
+            tile = w[tn * b1:(tn + 1) * b1, tk * b2:(tk + 1) * b2]
+            if not tile_map[tn, tk]:
+                tidx.append(sum(1 for x in tidx if x >= 0))
+                for slab in range(b1 // 16):
+                    for blk in range(b2 // 32):
+                        for lane in range(64):
+                            row = slab * 16 + lane % 16
+                            col = blk * 32 + 8 * (lane // 16)
+                            dense.extend(int(v) for v in tile[row, col:col + 8])
+                continue
+            tidx.append(~sum(1 for x in tidx if x < 0))
+            for slab in range(b1 // 16):
+                lane_words = [[0] * (b2 // 64) for _ in range(64)]
+                for blk in range(b2 // 64):
+                    for lane in range(64):
+                        row = slab * 16 + lane % 16
+                        for q in range(4):
+                            col = blk * 64 + 16 * (lane // 16) + 4 * q
+                            grp = [int(v) for v in tile[row, col:col + 4]]
+                            order = sorted(range(4), key=lambda p: (-(grp[p] & 0x7FFF), p))
+                            a, b = sorted(order[:2])
+                            val.extend([grp[a], grp[b]])
+                            nib = (a | (b << 2)) if meta == "idx2" else ((1 << a) | (1 << b))
+                            lane_words[lane][blk] |= nib << (4 * q)
+                for lane in range(64):
+                    words.extend(lane_words[lane])
+    return (np.array(dense, dtype=np.uint16), np.array(val, dtype=np.uint16),
+            np.array(words, dtype="<u2").view(np.uint8), np.array(tidx, dtype=np.int32))
+
+
+@pytest.mark.parametrize("b1,b2", [(16, 64), (32, 128), (16, 256)])
+@pytest.mark.parametrize("meta", ["idx2", "mask4"])
+def test_layout_restatement(b1, b2, meta):
+    rng = np.random.default_rng([b1, b2, len(meta)])
+    n, k = 2 * b1, 2 * b2
+    w = rng.integers(0, 1 << 16, size=(n, k), dtype=np.uint16)
+    tmap = np.array([[1, 0], [0, 1]], dtype=np.uint8)
+    got = oracle.pack(w, tmap, b1, b2, meta)
+    d, v, m, t = _layout_by_lanes(w, tmap, b1, b2, meta)
+    np.testing.assert_array_equal(got["dense"], d)
+    np.testing.assert_array_equal(got["val"], v)
+    np.testing.assert_array_equal(got["meta"], m)
+    np.testing.assert_array_equal(got["tidx"], t)
+
+
+def test_byte_totals_8b_up_projection():
+    """14336x4096 bf16, 128x128 tiles, 70% of 3584 tiles sparse: 2509 sparse
+    tiles; a sparse tile costs 9/16 of a dense one (half the values plus one
+    nibble per four entries)."""
+    mat = wl.workload(2).matrices[0]
+    tmap = mat.tile_map()
+    p = oracle.plan(mat.n, mat.k, mat.b1, mat.b2, tmap)
+    assert p["n_sparse"] == 2509 and p["n_dense"] == 1075
+    assert p["dense_bytes"] == 35_225_600
+    assert p["val_bytes"] == 41_107_456
+    assert p["meta_bytes"] == 5_138_432
+    assert p["dense_bytes"] + p["val_bytes"] + p["meta_bytes"] == 81_471_488
+    assert oracle.sparsity(tmap, 128, 128, mat.n, mat.k) == pytest.approx(0.5 * 2509 / 3584)
+
+
+# ------------------------------------------------- prune / pack invariants --
+
+def _random_case(seed, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    b1 = int(rng.choice([16, 32, 64]))
+    b2 = int(rng.choice([64, 128]))
+    tn, tk = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    n, k = tn * b1, tk * b2
+    vals = rng.standard_normal((n, k)).astype(np.float32) * 0.02
+    w = wl.float32_to_bits(vals, dtype)
+    # sprinkle exact ties and signed zeros
+    w[rng.random((n, k)) < 0.05] = 0x8000
+    w[rng.random((n, k)) < 0.05] = w[0, 0]
+    tmap = (rng.random((tn, tk)) < 0.5).astype(np.uint8)
+    return w, tmap, b1, b2
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("meta", ["idx2", "mask4"])
+def test_invariants(seed, meta):
+    w, tmap, b1, b2 = _random_case(seed, "bf16" if seed % 2 else "f16")
+    n, k = w.shape
+    wp = oracle.prune(w, tmap, b1, b2)
+    P = oracle.pack(w, tmap, b1, b2, meta)
+    dropped = 0
+    for tn in range(tmap.shape[0]):
+        for tk in range(tmap.shape[1]):
+            src = w[tn * b1:(tn + 1) * b1, tk * b2:(tk + 1) * b2]
+            dst = wp[tn * b1:(tn + 1) * b1, tk * b2:(tk + 1) * b2]
+            if not tmap[tn, tk]:
+                np.testing.assert_array_equal(src, dst)       # dense untouched
+                continue
+            gs = src.reshape(b1, b2 // 4, 4).astype(np.int64)
+            gd = dst.reshape(b1, b2 // 4, 4).astype(np.int64)
+            i0, i1 = oracle.kept_positions(gs.astype(np.uint16))
+            pos = np.arange(4)
+            kept = (pos == i0[..., None]) | (pos == i1[..., None])
+            assert np.all(gd[~kept] == 0)
+            assert np.all(gd[kept] == gs[kept])
+            assert np.all(np.count_nonzero(gd & 0x7FFF, axis=-1) <= 2)
+            # kept keys dominate dropped keys
+            ks = gs & 0x7FFF
+            kmin_kept = np.where(kept, ks, 1 << 20).min(axis=-1)
+            kmax_drop = np.where(~kept, ks, -1).max(axis=-1)
+            assert np.all(kmin_kept >= kmax_drop)
+            dropped += int((~kept).sum())
+    # overall sparsity counts dropped positions: half of each sparse tile
+    assert dropped == int(tmap.sum()) * b1 * b2 // 2
+    assert dropped / (n * k) == oracle.sparsity(tmap, b1, b2, n, k)
+    # byte totals
+    p = P["plan"]
+    assert P["dense"].nbytes == p["n_dense"] * b1 * b2 * 2
+    assert P["val"].nbytes == p["n_sparse"] * b1 * b2
+    assert P["meta"].nbytes == p["n_sparse"] * b1 * b2 // 8
+    # round trip and idempotence
+    u = oracle.unpack(P["dense"], P["val"], P["meta"], P["tidx"], n, k, b1, b2, meta)
+    np.testing.assert_array_equal(u, wp)
+    P2 = oracle.pack(u, tmap, b1, b2, meta)
+    for key in ("dense", "val", "meta", "tidx"):
+        np.testing.assert_array_equal(P2[key], P[key])
+    # all nibbles valid
+    words = P["meta"].view("<u2")
+    for q in range(4):
+        nib = (words >> (4 * q)) & 0xF
+        oracle.positions_from_nibble(nib, meta)
+
+
+def test_idx2_mask4_same_values():
+    w, tmap, b1, b2 = _random_case(99)
+    a = oracle.pack(w, tmap, b1, b2, "idx2")
+    b = oracle.pack(w, tmap, b1, b2, "mask4")
+    np.testing.assert_array_equal(a["dense"], b["dense"])
+    np.testing.assert_array_equal(a["val"], b["val"])
+    wa, wb = a["meta"].view("<u2"), b["meta"].view("<u2")
+    for q in range(4):
+        ia = oracle.positions_from_nibble((wa >> (4 * q)) & 0xF, "idx2")
+        ib = oracle.positions_from_nibble((wb >> (4 * q)) & 0xF, "mask4")
+        np.testing.assert_array_equal(ia[0], ib[0])
+        np.testing.assert_array_equal(ia[1], ib[1])
+
+
+def test_already_2of4_is_kept_whole():
+    """A weight that is already 2:4 in every sparse tile (e.g. a mask learned
+    upstream) loses no non-zero entry."""
+    w, tmap, b1, b2 = _random_case(7)
+    w = w & 0x7FFF | 0x0001  # all non-zero
+    wp = oracle.prune(w, tmap, b1, b2)
+    np.testing.assert_array_equal(oracle.prune(wp, tmap, b1, b2), wp)
+
+
+def test_shape_rejections():
+    with pytest.raises(ValueError):
+        oracle.plan(100, 128, 16, 64, np.zeros(0, np.uint8))
+    with pytest.raises(ValueError):
+        oracle.plan(64, 100, 16, 64, np.zeros(0, np.uint8))
+    with pytest.raises(ValueError):
+        oracle.plan(64, 128, 16, 48, np.zeros(0, np.uint8))
+    with pytest.raises(ValueError):
+        oracle.plan(32, 128, 16, 64, np.full(4, 2, np.uint8))
+    p = oracle.plan(0, 0, 16, 64, np.zeros(0, np.uint8))
+    assert p["n_dense"] == p["n_sparse"] == 0
+
+
+# ------------------------------------------------------------- reference ----
+
+def _fsum_ref(wp_bits, x_bits, dtype):
+    w = oracle.widen(wp_bits, dtype)
+    x = oracle.widen(x_bits, dtype)
+    m, n = x.shape[0], w.shape[0]
+    y = np.zeros((m, n))
+    s = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            prods = [float(a) * float(b) for a, b in zip(w[j], x[i])]
+            y[i, j] = math.fsum(prods)
+            s[i, j] = math.fsum(abs(p) for p in prods)
+    return y, s
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ref_matmul_fsum(dtype):
+    rng = np.random.default_rng(5)
+    n, k, m = 32, 128, 3
+    w = wl.float32_to_bits(rng.standard_normal((n, k)).astype(np.float32) * 0.02, dtype)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), dtype)
+    tmap = np.array([[1, 0], [0, 1]], dtype=np.uint8)
+    wp = oracle.prune(w, tmap, 16, 64)
+    y, s = oracle.ref_matmul(wp, x, dtype)
+    yb, sb = _fsum_ref(wp, x, dtype)
+    assert np.all(np.abs(y - yb) <= 1e-12 * sb)
+    assert np.allclose(s, sb, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ref_matmul_one_hot(dtype):
+    """x = e_c  =>  y[n] = W'[n, c] exactly."""
+    rng = np.random.default_rng(6)
+    n, k = 32, 128
+    w = wl.float32_to_bits(rng.standard_normal((n, k)).astype(np.float32) * 0.02, dtype)
+    wp = oracle.prune(w, np.array([[1, 0], [1, 1]], np.uint8), 16, 64)
+    one = 0x3F80 if dtype == "bf16" else 0x3C00
+    for c in (0, 1, 63, 64, 127):
+        x = np.zeros((1, k), np.uint16)
+        x[0, c] = one
+        y, _ = oracle.ref_matmul(wp, x, dtype)
+        np.testing.assert_array_equal(y[0], oracle.widen(wp[:, c], dtype))
+
+
+def test_ref_matmul_integers_exact():
+    """Small integers in W and X: every partial sum is an exact integer."""
+    rng = np.random.default_rng(8)
+    n, k, m = 48, 256, 4
+    wi = rng.integers(-3, 4, size=(n, k)).astype(np.float32)
+    xi = rng.integers(-3, 4, size=(m, k)).astype(np.float32)
+    w = wl.float32_to_bits(wi, "bf16")
+    x = wl.float32_to_bits(xi, "bf16")
+    tmap = np.ones((3, 4), np.uint8)
+    tmap[0, 0] = 0
+    wp = oracle.prune(w, tmap, 16, 64)
+    y, s = oracle.ref_matmul(wp, x, "bf16")
+    wpf = oracle.widen(wp, "bf16")
+    exact = np.array([[sum(int(a) * int(b) for a, b in zip(wpf[j], xi[i])) for j in range(n)]
+                      for i in range(m)], dtype=np.float64)
+    np.testing.assert_array_equal(y, exact)
+
+
+def test_ref_matmul_zero_input():
+    w = wl.float32_to_bits(np.ones((16, 64), np.float32), "bf16")
+    y, s = oracle.ref_matmul(w, np.zeros((2, 64), np.uint16), "bf16")
+    assert np.all(y == 0) and np.all(s == 0)
+    assert not np.any(np.signbit(y))
+
+
+def test_ref_matmul_orientation():
+    """Non-square W: y has one entry per output row n, so a transposed
+    operand cannot even be shaped right; check one entry by hand."""
+    w = np.zeros((16, 64), np.uint16)
+    w[3, 5] = 0x4000   # 2.0
+    w[3, 6] = 0xBF80   # -1.0
+    x = np.zeros((1, 64), np.uint16)
+    x[0, 5] = 0x4040   # 3.0
+    x[0, 6] = 0x4080   # 4.0
+    y, s = oracle.ref_matmul(w, x, "bf16")
+    assert y.shape == (1, 16)
+    assert y[0, 3] == 2.0 * 3.0 - 4.0 and s[0, 3] == 10.0
+    assert np.count_nonzero(y) == 1
