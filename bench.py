@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the tile-hybrid dense / 2:4 GEMV on one MI355X.
+
+Default workload: Llama-3.1-8B-shaped up projection, W 14336 x 4096 bf16,
+128 x 128 tiles, 2509 of 3584 tiles 2:4 sparse (35.0% sparsity), decode
+batch M = 1.  A step is one pass of every row of the hot path on one batch:
+  gemv      hybrid decode product, M = 1                    <- the metric
+  dense     the same kernel with the all-dense tile map     <- speedup base
+  gemm      prefill product, M = 64, matrix-core kernel
+  unpack    hybrid streams -> W'
+  pack      W -> hybrid streams (rotating copy)
+The timed region runs the K steps row by row (all GEMVs, then the GEMMs,
+unpacks and packs) so no GEMV competes with the write-back of a packing
+kernel's output.  Each kernel is bracketed by HIP events on the stream it
+runs on; `value` is the hybrid GEMV's algorithmic bytes per launch divided
+by its mean event duration.  Packed copies rotate through more than 1 GiB per
+kind (stepping by 3 copies) so the 256 MB last-level cache holds nothing
+from the previous use of a copy.
+
+Prints one JSON line.  `python bench.py --sweep` also measures the other
+workloads (stderr table plus --sweep-json file).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "hybrid 2:4/dense GEMV µs + achieved HBM GB/s at 8B MLP shape; speedup vs dense"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_BF16_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(layout, m: int, y_bytes: int = 4) -> int:
+    """Algorithmic bytes of one product: weights as stored, tile index,
+    activations read once, outputs written once."""
+    return (layout.dense_bytes + layout.val_bytes + layout.meta_bytes + layout.tidx_bytes
+            + 2 * m * layout.k + y_bytes * m * layout.n)
+
+
+def alg_flops(layout, m: int) -> int:
+    """2 flops per stored (kept) weight per token."""
+    tile = layout.b1 * layout.b2
+    return 2 * m * (tile * layout.n_dense + tile * layout.n_sparse // 2)
+
+
+class Timer:
+    """Per-launch HIP event pairs on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+
+    def ms(self, name):
+        return [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
+
+
+def copies_for(nbytes: int, rotate_bytes: int) -> int:
+    return max(2, -(-rotate_bytes // max(nbytes, 1)))
+
+
+def setup_matrix(hb, torch, mat, tmap, meta, rotate_bytes, dev):
+    w_bits = mat.weight_bits()
+    w = hb.bits_to_tensor(w_bits, mat.dtype, dev)
+    first = hb.pack(w, tmap, mat.b1, mat.b2, meta)
+    n_copies = copies_for(first.weight_bytes(), rotate_bytes)
+    copies = [first] + [hb.pack(w, tmap, mat.b1, mat.b2, meta) for _ in range(n_copies - 1)]
+    torch.cuda.synchronize()
+    return w, w_bits, copies
+
+
+def cpu_baseline(mat, w_bits, tmap, x_bits, layout, budget_s=12.0):
+    """The oracle as it stands (unpack to dense + float64 product), timed on
+    this host's cores on the full workload matrix."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    P = oracle.pack(w_bits, tmap, mat.b1, mat.b2, "idx2")
+    times, unp, mm = [], [], []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 5):
+        t0 = time.perf_counter()
+        wp = oracle.unpack(P["dense"], P["val"], P["meta"], P["tidx"], mat.n, mat.k, mat.b1, mat.b2, "idx2")
+        t1 = time.perf_counter()
+        oracle.ref_matmul(wp, x_bits, mat.dtype)
+        t2 = time.perf_counter()
+        times.append(t2 - t0)
+        unp.append(t1 - t0)
+        mm.append(t2 - t1)
+        if time.perf_counter() > t_end and len(times) >= 1:
+            break
+    med = statistics.median(times)
+    return {
+        "value": round(alg_bytes(layout, x_bits.shape[0]) / med / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"whole {mat.n}x{mat.k} matrix, M={x_bits.shape[0]}: oracle unpack + float64 "
+                   f"X.W'^T and |X|.|W'|^T, median of {len(times)} runs "
+                   f"({statistics.median(unp):.3f} s unpack + {statistics.median(mm):.3f} s matmul)"),
+        "seconds_per_pass": round(med, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--meta", default="idx2", choices=["idx2", "mask4"])
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--gemm-m", type=int, default=64)
+    ap.add_argument("--only", default="", help="comma list of rows to run (pack,gemv,dense,unpack,gemm)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-json", default="")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from matmul_pack_b1_amd import binding as hb
+    from matmul_pack_b1_amd import workloads as wl
+    hb.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    rotate = int(args.rotate_gib * (1 << 30))
+    rows = set(args.only.split(",")) if args.only else {"pack", "gemv", "dense", "unpack", "gemm"}
+
+    mat = wl.workload(2).matrices[0]
+    tmap = mat.tile_map()
+    dmap = np.zeros_like(tmap)
+    log(f"[bench] setting up {mat.n}x{mat.k} {mat.dtype}, {int(tmap.sum())}/{tmap.size} sparse tiles")
+    w, w_bits, hyb = setup_matrix(hb, torch, mat, tmap, args.meta, rotate, dev)
+    _, _, dense = setup_matrix(hb, torch, mat, dmap, args.meta, rotate, dev) if "dense" in rows else (None, None, [])
+    L = hyb[0].layout
+    x_bits = mat.activation_bits(1)
+    x = hb.bits_to_tensor(x_bits, mat.dtype, dev)
+    xg = hb.bits_to_tensor(mat.activation_bits(args.gemm_m), mat.dtype, dev)
+    y = torch.empty((1, mat.n), dtype=torch.float32, device=dev)
+    yg = torch.empty((args.gemm_m, mat.n), dtype=torch.float32, device=dev)
+    wout = torch.empty((mat.n, mat.k), dtype=w.dtype, device=dev)
+    log(f"[bench] {len(hyb)} hybrid copies ({hyb[0].weight_bytes()} B each), {len(dense)} dense copies")
+
+    nh = len(hyb)
+
+    # One step = one batch through every row.  The rows are timed in separate
+    # phases of the timed region (all GEMVs first, then the GEMMs, unpacks
+    # and packs), so that no GEMV starts while the write-back of a previous
+    # kernel's output is still draining to HBM.
+    def phase(name, i, timer):
+        if name == "gemv":
+            timer.run("gemv", lambda: hb.gemv(hyb[(i * 3) % nh], x, out=y))
+        elif name == "dense":
+            timer.run("dense", lambda: hb.gemv(dense[(i * 3) % len(dense)], x, out=y))
+        elif name == "gemm":
+            timer.run("gemm", lambda: hb.gemm_mfma(hyb[(i * 3 + 1) % nh], xg, out=yg))
+        elif name == "unpack":
+            timer.run("unpack", lambda: hb.unpack(hyb[(i * 3 + 2) % nh], out=wout))
+        elif name == "pack":
+            timer.run("pack", lambda: hb.pack(w, tmap, mat.b1, mat.b2, args.meta, out=hyb[(i * 3 + 2) % nh]))
+
+    def run_steps(first, count, timer):
+        for i in range(first, first + count):
+            for name in ("gemv", "dense"):
+                if name in rows:
+                    phase(name, i, timer)
+        for name in ("gemm", "unpack", "pack"):
+            if name in rows:
+                for i in range(first, first + count):
+                    phase(name, i, timer)
+
+    warm = Timer(torch)
+    run_steps(0, args.warmup, warm)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(args.warmup, args.steps, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
+
+    res_rows = {}
+    for name in ("pack", "gemv", "dense", "unpack", "gemm"):
+        ms = timer.ms(name)
+        if not ms:
+            continue
+        res_rows[name] = {"us_mean": round(1e3 * statistics.mean(ms), 3),
+                          "us_median": round(1e3 * statistics.median(ms), 3),
+                          "us_p10": round(1e3 * float(np.percentile(ms, 10)), 3),
+                          "us_p90": round(1e3 * float(np.percentile(ms, 90)), 3)}
+    gb = alg_bytes(L, 1)
+    out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(1e3 * wall / max(args.steps, 1), 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if "gemv" in res_rows:
+        us = res_rows["gemv"]["us_mean"]
+        out["value"] = round(gb / (us * 1e-6) / 1e9, 2)
+        res_rows["gemv"].update({"alg_bytes": gb, "GBps": out["value"]})
+    else:
+        out["value"] = None
+    if "dense" in res_rows:
+        Ld = dense[0].layout
+        gbd = alg_bytes(Ld, 1)
+        res_rows["dense"].update({"alg_bytes": gbd, "GBps": round(gbd / (res_rows["dense"]["us_mean"] * 1e-6) / 1e9, 2)})
+        if "gemv" in res_rows:
+            out["gemv_us"] = res_rows["gemv"]["us_mean"]
+            out["dense_us"] = res_rows["dense"]["us_mean"]
+            out["speedup_vs_dense"] = round(res_rows["dense"]["us_mean"] / res_rows["gemv"]["us_mean"], 4)
+            out["byte_ratio_dense_over_hybrid"] = round(gbd / gb, 4)
+    if "pack" in res_rows:
+        rd = mat.n * mat.k * 2 + hyb[0].weight_bytes()
+        res_rows["pack"].update({"alg_bytes": rd, "GBps": round(rd / (res_rows["pack"]["us_mean"] * 1e-6) / 1e9, 2)})
+    if "unpack" in res_rows:
+        rd = mat.n * mat.k * 2 + hyb[0].weight_bytes()
+        res_rows["unpack"].update({"alg_bytes": rd, "GBps": round(rd / (res_rows["unpack"]["us_mean"] * 1e-6) / 1e9, 2)})
+    if "gemm" in res_rows:
+        fl = alg_flops(L, args.gemm_m)
+        res_rows["gemm"].update({"m": args.gemm_m, "alg_flops": fl,
+                                 "TFLOPs": round(fl / (res_rows["gemm"]["us_mean"] * 1e-6) / 1e12, 2),
+                                 "GBps": round(alg_bytes(L, args.gemm_m) / (res_rows["gemm"]["us_mean"] * 1e-6) / 1e9, 2)})
+    out["config"] = {"workload": f"Llama-3.1-8B up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles, "
+                                 f"{L.n_sparse}/{L.tiles_n * L.tiles_k} tiles 2:4 ({args.meta}), decode M=1",
+                     "n": mat.n, "k": mat.k, "tile": [mat.b1, mat.b2], "n_sparse_tiles": L.n_sparse,
+                     "n_tiles": L.tiles_n * L.tiles_k, "batch": 1, "meta": args.meta,
+                     "rotating_copies": {"hybrid": len(hyb), "dense": len(dense)}}
+    out["rows"] = res_rows
+    if out["value"] is not None:
+        out["roofline"] = {"bound": "hbm", "achieved": out["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(out["value"] / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "k_gemv<1,128,bf16>", "alg_bytes_per_launch": gb}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(mat, w_bits, tmap, x_bits, L)
+    if args.sweep:
+        out["sweep_file"] = sweep(hb, torch, wl, dev, rotate, args)
+    print(json.dumps(out), flush=True)
+
+
+def sweep(hb, torch, wl, dev, rotate, args):
+    """All workloads: GEMV / GEMM time against the same kernel all-dense."""
+    results = []
+
+    def timed(fn, iters, copies):
+        ev = []
+        for i in range(iters + 5):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn(copies[i % len(copies)])
+            e.record()
+            if i >= 5:
+                ev.append((s, e))
+        torch.cuda.synchronize()
+        return statistics.mean([s.elapsed_time(e) for s, e in ev]) * 1e3
+
+    for cfg in (1, 2, 3, 4, 5):
+        W = wl.workload(cfg)
+        for mat in W.matrices:
+            tmap = mat.tile_map()
+            for kind, mp in (("hybrid", tmap), ("dense", np.zeros_like(tmap))):
+                if cfg == 4 and kind == "dense":
+                    continue  # the 0%-sparse case is the dense baseline
+                log(f"[sweep] config {cfg} {mat.name} {kind}")
+                w_, _, copies = setup_matrix(hb, torch, mat, mp, "idx2", rotate, dev)
+                del w_
+                L = copies[0].layout
+                for m in W.batches:
+                    x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
+                    y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+                    fns = [("gemm", lambda P: hb.gemm(P, x, out=y))]
+                    if m > 16:
+                        fns = [("gemm_mfma", lambda P: hb.gemm_mfma(P, x, out=y))]
+                    elif cfg == 5:
+                        fns.append(("gemm_mfma", lambda P: hb.gemm_mfma(P, x, out=y)))
+                    for fname, fn in fns:
+                        us = timed(fn, 50, copies)
+                        results.append({"config": cfg, "matrix": mat.name, "kind": kind, "m": m, "fn": fname,
+                                        "us": round(us, 3), "alg_bytes": alg_bytes(L, m),
+                                        "GBps": round(alg_bytes(L, m) / us / 1e3, 1),
+                                        "alg_flops": alg_flops(L, m),
+                                        "TFLOPs": round(alg_flops(L, m) / us / 1e6, 2),
+                                        "n_sparse": L.n_sparse, "tiles": L.tiles_n * L.tiles_k})
+                        log(f"  m={m:5d} {fname:9s} {kind:6s} {us:9.2f} us  {results[-1]['GBps']:8.1f} GB/s  "
+                            f"{results[-1]['TFLOPs']:7.2f} TF/s")
+                del copies
+                torch.cuda.empty_cache()
+    path = args.sweep_json or os.path.join(HERE, "gpurun_out", "sweep.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(results, f, indent=1)
+    return path
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * hyb.h -- C ABI of libhyb: tile-hybrid dense / 2:4 sparse weights for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  A weight matrix W (n x k, out x in, row-major) is cut
+ * into b1 x b2 tiles; each tile is either dense or 2:4 sparse, chosen per tile
+ * by a caller-supplied map (PATCH: Learnable Tile-level Hybrid Sparsity for
+ * LLMs, gist.science, section 2 "Meccanismo Principale").  In a sparse tile
+ * every row keeps, in each aligned group of four columns, two entries -- one
+ * of the six two-of-four patterns (same page, section 2 "Distribuzioni
+ * Apprendibili") -- and the matrix is stored compressed: two values per group
+ * plus a 4-bit code, a constant number of slots per group (SparseDecoding,
+ * ai.info, authors' abstract: bitmask-indexed N:M storage read with a fixed
+ * stride).  The products y = W' x (decode, 1..16 tokens) and Y = X W'^T
+ * (prefill) read that compressed form; W' is W with the dropped entries set
+ * to zero, so results equal the plain product with W'.
+ *
+ * Which two entries are kept: the two largest |w| of the group, |w| compared
+ * as the integer (bits & 0x7FFF), equal magnitudes going to the lower column
+ * (magnitude projection: 3BASiL, gist.science, section 2 "Aggiornamenti
+ * Chiusi"; the pages learn this choice instead, which needs training data).
+ *
+ * Stream format "HYB1" (element indices count 16-bit words):
+ *   tile t = tn*tiles_k + tk; dense tiles take dense slots 0,1,.. and sparse
+ *   tiles sparse slots 0,1,.. in increasing t; tidx[t] = slot for a dense
+ *   tile and ~slot for a sparse one.
+ *   dense  slot s, element (r, c):
+ *       s*b1*b2 + (r/16)*16*b2 + (c/32)*512 + ((c%32)/8)*128 + (r%16)*8 + c%8
+ *   values slot s, row r, group g (columns 4g..4g+3), kept j = 0, 1 (ascending
+ *       column):  s*b1*b2/2 + (r/16)*8*b2 + (g/16)*512 + ((g%16)/4)*128
+ *                 + (r%16)*8 + (g%4)*2 + j
+ *   meta   16-bit little-endian words; the group's nibble is in word
+ *       s*b1*b2/16 + (r/16)*b2 + (((g%16)/4)*16 + r%16)*(b2/64) + g/16
+ *       at bits 4*(g%4)..4*(g%4)+3;  HYB_META_IDX2: i0 | i1<<2,
+ *       HYB_META_MASK4: 1<<i0 | 1<<i1  (i0 < i1 the kept columns).
+ *   Every 1 KiB of the dense or value stream is one 16-row slab piece that a
+ *   64-lane wavefront loads with one 16-byte load per lane.
+ *
+ * Conventions.
+ *   - All pointers to device memory are plain device addresses (from
+ *     hipMalloc or any allocator on the same device); the library never
+ *     allocates or frees device memory and keeps no mutable global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls enqueue work and return; the caller synchronises.
+ *   - Every argument is checked on the host before anything is enqueued; a
+ *     failed check returns a non-zero status, enqueues nothing and leaves a
+ *     message for hyb_last_error() (thread-local).
+ *   - Outputs must not overlap inputs.
+ *   - Entries of tidx that name a slot outside [0, n_dense) or
+ *     [0, n_sparse) are not reported; the kernels skip such tiles (they add
+ *     nothing and write nothing) so they never read outside the streams.
+ *     Metadata nibbles outside the six valid codes give unspecified values
+ *     for that group (never an out-of-bounds access).
+ */
+#ifndef HYB_H_
+#define HYB_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hyb_status;
+enum {
+  HYB_OK = 0,
+  HYB_ERR_INVALID_ARG = 1, /* null pointer, bad stride, bad alignment, bad value */
+  HYB_ERR_SHAPE = 2,       /* n % b1 or k % b2 non-zero, negative sizes, m out of range */
+  HYB_ERR_DTYPE = 3,       /* unknown element or output type */
+  HYB_ERR_UNSUPPORTED = 4, /* tile size outside {64, 128, 256} */
+  HYB_ERR_FORMAT = 5,      /* layout magic / version / sizes inconsistent */
+  HYB_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+};
+
+enum { HYB_F16 = 1, HYB_BF16 = 2, HYB_F32 = 3 };    /* element types */
+enum { HYB_META_IDX2 = 1, HYB_META_MASK4 = 2 };      /* metadata codes */
+
+#define HYB_MAGIC 0x31425948u /* "HYB1" little-endian */
+#define HYB_VERSION 1u
+#define HYB_ABI_VERSION 1
+
+/* Plain-old-data description of one packed matrix; filled by hyb_plan and
+ * also usable as a serialised header (all fields fixed-width). */
+typedef struct {
+  uint32_t magic, version; /* HYB_MAGIC, HYB_VERSION */
+  int64_t n, k;            /* W is n x k (out_features x in_features) */
+  int32_t b1, b2;          /* tile rows x tile columns */
+  int32_t dtype, meta;     /* HYB_F16 | HYB_BF16; HYB_META_IDX2 | HYB_META_MASK4 */
+  int64_t tiles_n, tiles_k, n_dense, n_sparse;
+  int64_t dense_bytes, val_bytes, meta_bytes, tidx_bytes;
+} hyb_layout;
+
+/* Device addresses of the four streams of one packed matrix (owned by the
+ * caller).  dense, val and meta must be 16-byte aligned; tidx 4-byte
+ * aligned.  A stream of zero bytes may be NULL. */
+typedef struct {
+  void* dense;
+  void* val;
+  void* meta;
+  int32_t* tidx;
+} hyb_packed;
+
+/* Plan a packed layout (host only, no device work; the tile-map step of
+ * PATCH section 2 "Meccanismo Principale").
+ *   n, k      matrix shape, n % b1 == 0 and k % b2 == 0 (0 allowed)
+ *   b1, b2    tile shape; any positive b1 % 16 == 0, b2 % 64 == 0 is planned,
+ *             the device calls accept b1, b2 in {64, 128, 256}
+ *   tile_map  host uint8[tiles_n * tiles_k], row-major over the tile grid,
+ *             0 = dense, 1 = 2:4 sparse; may be NULL when there are no tiles
+ *   out       receives the layout (byte sizes of the four streams)
+ *   tidx_out  host int32[tiles_n * tiles_k] receiving the tile index, or NULL
+ * The caller allocates the streams and copies tidx_out to packed.tidx. */
+hyb_status hyb_plan(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t dtype,
+                    int32_t meta, const uint8_t* tile_map, hyb_layout* out,
+                    int32_t* tidx_out);
+
+/* Pack W into the streams of `dst` (the pruning and compression of PATCH
+ * section 2 with the magnitude rule above; SparseDecoding abstract for the
+ * fixed-stride bitmask storage).
+ *   w     device, n x k elements of layout->dtype, row stride ldw >= k
+ *         elements, 16-byte aligned, ldw % 8 == 0
+ *   dst   device streams sized as in *layout; dst->tidx must already hold
+ *         the tile index from hyb_plan
+ * Bit-exact: the streams depend only on the bits of W and the map. */
+hyb_status hyb_pack(const hyb_layout* layout, const void* w, int64_t ldw,
+                    const hyb_packed* dst, void* stream);
+
+/* Rebuild W' (n x k, row stride ldw) from packed streams: dense tiles as
+ * stored, sparse groups with their two values at the coded columns and +0.0
+ * at the other two.  Same alignment rules as hyb_pack. */
+hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_out,
+                      int64_t ldw, void* stream);
+
+/* Decode product, 0 <= m <= 16 tokens: Y[i, :] = W' X[i, :] for i < m
+ * (SparseDecoding abstract: the decode-phase sparse matrix x vector product
+ * over the compressed matrix).
+ *   x       device, m x k of layout->dtype, row stride ldx >= k (elements),
+ *           16-byte aligned, ldx % 8 == 0
+ *   y       device, m x n, row stride ldy >= n, element type y_dtype in
+ *           {HYB_F32, layout->dtype}; 16-bit outputs are rounded to nearest
+ *           even from the fp32 sum
+ * Products are exact in fp32 and summed in fp32; m == 0 returns HYB_OK with
+ * nothing enqueued. */
+hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                    int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                    void* stream);
+
+/* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
+ * sparse tiles on the matrix units, dense tiles on dense kernels).  Same
+ * arguments as hyb_gemv; m <= 16 runs the decode kernel, larger m the
+ * matrix-core kernel. */
+hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                    int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                    void* stream);
+
+/* Matrix-core kernel only, any m >= 0 (no switch to the decode kernel);
+ * exposed so that the crossover can be measured.  Same arguments. */
+hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                         int32_t m, int64_t ldx, void* y, int32_t y_dtype,
+                         int64_t ldy, void* stream);
+
+const char* hyb_status_str(hyb_status s); /* static string, never NULL */
+const char* hyb_last_error(void);         /* thread-local detail, "" if none */
+int32_t hyb_abi_version(void);            /* HYB_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYB_H_ */

@@ -1,0 +1,273 @@
+"""Thin ctypes binding over libhyb.so (the C ABI in include/hyb.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no CPU fallback -- if libhyb.so is missing or a call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libhyb.so")
+
+HYB_OK = 0
+HYB_F16, HYB_BF16, HYB_F32 = 1, 2, 3
+HYB_META_IDX2, HYB_META_MASK4 = 1, 2
+HYB_MAGIC = 0x31425948
+HYB_VERSION = 1
+MAX_GEMV_M = 16
+
+META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4}
+DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
+
+EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemm", "hyb_gemm_mfma",
+            "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+
+
+class HybLayout(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("b1", ctypes.c_int32), ("b2", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("meta", ctypes.c_int32),
+        ("tiles_n", ctypes.c_int64), ("tiles_k", ctypes.c_int64),
+        ("n_dense", ctypes.c_int64), ("n_sparse", ctypes.c_int64),
+        ("dense_bytes", ctypes.c_int64), ("val_bytes", ctypes.c_int64),
+        ("meta_bytes", ctypes.c_int64), ("tidx_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class HybPacked(ctypes.Structure):
+    _fields_ = [("dense", ctypes.c_void_p), ("val", ctypes.c_void_p),
+                ("meta", ctypes.c_void_p), ("tidx", ctypes.c_void_p)]
+
+
+class HybError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}: {detail}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhyb.so (built in-tree by matmul_pack_b1_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m matmul_pack_b1_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.hyb_plan.argtypes = [I64, I64, I32, I32, I32, I32, P, ctypes.POINTER(HybLayout), P]
+    L.hyb_plan.restype = I32
+    L.hyb_pack.argtypes = [ctypes.POINTER(HybLayout), P, I64, ctypes.POINTER(HybPacked), P]
+    L.hyb_pack.restype = I32
+    L.hyb_unpack.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I64, P]
+    L.hyb_unpack.restype = I32
+    for name in ("hyb_gemv", "hyb_gemm", "hyb_gemm_mfma"):
+        f = getattr(L, name)
+        f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I32, I64, P]
+        f.restype = I32
+    L.hyb_status_str.argtypes = [I32]
+    L.hyb_status_str.restype = ctypes.c_char_p
+    L.hyb_last_error.argtypes = []
+    L.hyb_last_error.restype = ctypes.c_char_p
+    L.hyb_abi_version.argtypes = []
+    L.hyb_abi_version.restype = I32
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().hyb_status_str(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().hyb_last_error().decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != HYB_OK:
+        raise HybError(status, where, last_error())
+
+
+# ------------------------------------------------------------------ plan ----
+
+def plan(n: int, k: int, b1: int, b2: int, dtype: str, meta: str, tile_map) -> tuple[HybLayout, np.ndarray]:
+    """Host-only layout planning.  Returns (layout, int32 tile index)."""
+    tm = np.ascontiguousarray(np.asarray(tile_map, dtype=np.uint8).reshape(-1))
+    tidx = np.zeros(max(tm.size, 1), dtype=np.int32)
+    L = HybLayout()
+    st = lib().hyb_plan(int(n), int(k), int(b1), int(b2), DTYPE_CODES.get(dtype, -1),
+                        META_CODES.get(meta, -1), tm.ctypes.data if tm.size else None,
+                        ctypes.byref(L), tidx.ctypes.data)
+    check(st, "hyb_plan")
+    return L, tidx[: L.tiles_n * L.tiles_k]
+
+
+# ------------------------------------------------------- torch plumbing -----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_name(t) -> str:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float16:
+        return "f16"
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_rows(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    if t.numel() and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+
+
+@dataclass
+class PackedWeight:
+    """One packed matrix: its layout plus four device buffers."""
+    layout: HybLayout
+    dense: object
+    val: object
+    meta: object
+    tidx: object
+    dtype: str
+    meta_kind: str
+
+    @property
+    def shape(self):
+        return (self.layout.n, self.layout.k)
+
+    @property
+    def device(self):
+        return self.tidx.device
+
+    def packed_struct(self) -> HybPacked:
+        return HybPacked(_ptr(self.dense), _ptr(self.val), _ptr(self.meta), _ptr(self.tidx))
+
+    def weight_bytes(self) -> int:
+        L = self.layout
+        return L.dense_bytes + L.val_bytes + L.meta_bytes
+
+
+def allocate(layout: HybLayout, tidx_host: np.ndarray, device, dtype: str, meta: str) -> PackedWeight:
+    torch = _torch()
+    def buf(nbytes):
+        return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+    tidx = torch.from_numpy(np.ascontiguousarray(tidx_host, dtype=np.int32)).to(device)
+    return PackedWeight(layout, buf(layout.dense_bytes), buf(layout.val_bytes), buf(layout.meta_bytes),
+                        tidx, dtype, meta)
+
+
+def pack(w, tile_map, b1: int, b2: int, meta: str = "idx2", out: PackedWeight | None = None) -> PackedWeight:
+    """Pack a device matrix w (n x k, bf16 or fp16) with the given tile map
+    (uint8 [n/b1, k/b2], 1 = 2:4 sparse).  `out` reuses existing buffers."""
+    _check_rows(w, "w")
+    dtype = _dtype_name(w)
+    n, k = w.shape
+    if out is None:
+        L, tidx = plan(n, k, b1, b2, dtype, meta, tile_map)
+        out = allocate(L, tidx, w.device, dtype, meta)
+    P = out.packed_struct()
+    st = lib().hyb_pack(ctypes.byref(out.layout), _ptr(w), int(w.stride(0)) if w.numel() else int(k),
+                        ctypes.byref(P), _stream(w.device))
+    check(st, "hyb_pack")
+    return out
+
+
+def unpack(P: PackedWeight, out=None):
+    """W' (n x k, same dtype) rebuilt on the device from the packed streams."""
+    torch = _torch()
+    n, k = P.shape
+    tdt = torch.bfloat16 if P.dtype == "bf16" else torch.float16
+    if out is None:
+        out = torch.empty((n, k), dtype=tdt, device=P.device)
+    _check_rows(out, "out")
+    st = lib().hyb_unpack(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(out),
+                          int(out.stride(0)) if out.numel() else int(k), _stream(P.device))
+    check(st, "hyb_unpack")
+    return out
+
+
+def _out_code(P: PackedWeight, out_dtype) -> int:
+    torch = _torch()
+    if out_dtype in (None, torch.float32):
+        return HYB_F32
+    if out_dtype == torch.bfloat16 and P.dtype == "bf16":
+        return HYB_BF16
+    if out_dtype == torch.float16 and P.dtype == "f16":
+        return HYB_F16
+    raise TypeError(f"output dtype {out_dtype} must be float32 or the weight dtype")
+
+
+def _product(fn_name: str, P: PackedWeight, x, out_dtype=None, out=None):
+    torch = _torch()
+    _check_rows(x, "x")
+    m = x.shape[0]
+    n, k = P.shape
+    code = _out_code(P, out_dtype)
+    tdt = {HYB_F32: torch.float32, HYB_BF16: torch.bfloat16, HYB_F16: torch.float16}[code]
+    if out is None:
+        out = torch.empty((m, n), dtype=tdt, device=x.device)
+    fn = getattr(lib(), fn_name)
+    st = fn(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
+            int(x.stride(0)) if x.numel() else int(k), _ptr(out), code,
+            int(out.stride(0)) if out.numel() else int(n), _stream(x.device))
+    check(st, fn_name)
+    return out
+
+
+def gemv(P: PackedWeight, x, out_dtype=None, out=None):
+    """Decode product Y = X W'^T for 1..16 tokens (rows of x)."""
+    return _product("hyb_gemv", P, x, out_dtype, out)
+
+
+def gemm(P: PackedWeight, x, out_dtype=None, out=None):
+    """Y = X W'^T for any number of tokens (decode kernel for <= 16)."""
+    return _product("hyb_gemm", P, x, out_dtype, out)
+
+
+def gemm_mfma(P: PackedWeight, x, out_dtype=None, out=None):
+    """Y = X W'^T on the matrix-core kernel regardless of the token count."""
+    return _product("hyb_gemm_mfma", P, x, out_dtype, out)
+
+
+def bits_to_tensor(bits: np.ndarray, dtype: str, device):
+    """Upload uint16 bit patterns as a bf16 / fp16 device tensor."""
+    torch = _torch()
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return t.to(device).view(tdt)
+
+
+def tensor_to_bits(t) -> np.ndarray:
+    """Download a 16-bit device tensor as uint16 bit patterns."""
+    torch = _torch()
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,247 @@
+// Host side of the C ABI: layout planning and argument checks.  Nothing here
+// touches the device except the final kernel launch through hyb_internal.h,
+// so every error path can be exercised without a GPU.
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "hyb_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hyb_status fail(hyb_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hyb_status ok() {
+  g_last_error.clear();
+  return HYB_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool device_tile(int32_t b) { return b == 64 || b == 128 || b == 256; }
+
+int elem_size(int32_t dt) { return dt == HYB_F32 ? 4 : 2; }
+
+// Shape and type checks shared by hyb_plan and the layout validator.
+hyb_status check_geometry(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t dtype,
+                          int32_t meta) {
+  if (dtype != HYB_F16 && dtype != HYB_BF16)
+    return fail(HYB_ERR_DTYPE, "dtype %d is not HYB_F16 or HYB_BF16", dtype);
+  if (meta != HYB_META_IDX2 && meta != HYB_META_MASK4)
+    return fail(HYB_ERR_INVALID_ARG, "meta %d is not HYB_META_IDX2 or HYB_META_MASK4", meta);
+  if (b1 <= 0 || b2 <= 0 || b1 % 16 != 0 || b2 % 64 != 0)
+    return fail(HYB_ERR_SHAPE, "tile %dx%d: need b1 %% 16 == 0 and b2 %% 64 == 0", b1, b2);
+  if (n < 0 || k < 0) return fail(HYB_ERR_SHAPE, "negative shape %lldx%lld", (long long)n, (long long)k);
+  if (n % b1 != 0 || k % b2 != 0)
+    return fail(HYB_ERR_SHAPE, "shape %lldx%lld is not a whole number of %dx%d tiles",
+                (long long)n, (long long)k, b1, b2);
+  // Keep every stream index inside int64 with room to spare.
+  if (n > (int64_t(1) << 31) || k > (int64_t(1) << 31) || n * k > (int64_t(1) << 40))
+    return fail(HYB_ERR_SHAPE, "shape %lldx%lld too large", (long long)n, (long long)k);
+  return HYB_OK;
+}
+
+void fill_sizes(hyb_layout* L) {
+  const int64_t tile = int64_t(L->b1) * L->b2;
+  L->dense_bytes = L->n_dense * tile * 2;
+  L->val_bytes = L->n_sparse * tile;
+  L->meta_bytes = L->n_sparse * tile / 8;
+  L->tidx_bytes = L->tiles_n * L->tiles_k * 4;
+}
+
+// Full consistency check of a caller-held layout (magic, version, sizes).
+hyb_status check_layout(const hyb_layout* L, bool device_call) {
+  if (!L) return fail(HYB_ERR_INVALID_ARG, "layout is NULL");
+  if (L->magic != HYB_MAGIC || L->version != HYB_VERSION)
+    return fail(HYB_ERR_FORMAT, "layout magic/version 0x%08x/%u, expected 0x%08x/%u", L->magic,
+                L->version, HYB_MAGIC, HYB_VERSION);
+  hyb_status st = check_geometry(L->n, L->k, L->b1, L->b2, L->dtype, L->meta);
+  if (st != HYB_OK) return st;
+  if (L->tiles_n != L->n / L->b1 || L->tiles_k != L->k / L->b2 || L->n_dense < 0 ||
+      L->n_sparse < 0 || L->n_dense + L->n_sparse != L->tiles_n * L->tiles_k)
+    return fail(HYB_ERR_FORMAT, "layout tile counts are inconsistent");
+  hyb_layout ref = *L;
+  fill_sizes(&ref);
+  if (ref.dense_bytes != L->dense_bytes || ref.val_bytes != L->val_bytes ||
+      ref.meta_bytes != L->meta_bytes || ref.tidx_bytes != L->tidx_bytes)
+    return fail(HYB_ERR_FORMAT, "layout byte sizes are inconsistent");
+  if (device_call && !(device_tile(L->b1) && device_tile(L->b2)))
+    return fail(HYB_ERR_UNSUPPORTED, "device kernels need b1, b2 in {64, 128, 256}, got %dx%d",
+                L->b1, L->b2);
+  return HYB_OK;
+}
+
+hyb_status check_packed(const hyb_layout* L, const hyb_packed* P) {
+  if (!P) return fail(HYB_ERR_INVALID_ARG, "packed streams descriptor is NULL");
+  if (L->dense_bytes > 0 && (!P->dense || !aligned(P->dense, 16)))
+    return fail(HYB_ERR_INVALID_ARG, "dense stream is NULL or not 16-byte aligned");
+  if (L->val_bytes > 0 && (!P->val || !aligned(P->val, 16)))
+    return fail(HYB_ERR_INVALID_ARG, "value stream is NULL or not 16-byte aligned");
+  if (L->meta_bytes > 0 && (!P->meta || !aligned(P->meta, 16)))
+    return fail(HYB_ERR_INVALID_ARG, "metadata stream is NULL or not 16-byte aligned");
+  if (L->tidx_bytes > 0 && (!P->tidx || !aligned(P->tidx, 4)))
+    return fail(HYB_ERR_INVALID_ARG, "tile index is NULL or not 4-byte aligned");
+  return HYB_OK;
+}
+
+hyb_status check_matrix_arg(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name) {
+  if (rows == 0 || cols == 0) return HYB_OK;
+  if (!p) return fail(HYB_ERR_INVALID_ARG, "%s is NULL", name);
+  if (ld < cols) return fail(HYB_ERR_INVALID_ARG, "%s row stride %lld < %lld", name, (long long)ld, (long long)cols);
+  if (!aligned(p, 16) || ld % 8 != 0)
+    return fail(HYB_ERR_INVALID_ARG, "%s must be 16-byte aligned with a row stride multiple of 8", name);
+  return HYB_OK;
+}
+
+hyb_status check_product(const hyb_layout* L, const hyb_packed* P, const void* x, int32_t m,
+                         int64_t ldx, const void* y, int32_t y_dtype, int64_t ldy, int32_t max_m) {
+  hyb_status st = check_layout(L, true);
+  if (st != HYB_OK) return st;
+  if (m < 0 || m > max_m) return fail(HYB_ERR_SHAPE, "m = %d outside [0, %d]", m, max_m);
+  if (y_dtype != HYB_F32 && y_dtype != L->dtype)
+    return fail(HYB_ERR_DTYPE, "y_dtype %d must be HYB_F32 or the weight dtype %d", y_dtype, L->dtype);
+  if (m == 0) return HYB_OK;
+  st = check_packed(L, P);
+  if (st != HYB_OK) return st;
+  st = check_matrix_arg(x, m, L->k, ldx, "x");
+  if (st != HYB_OK) return st;
+  if (L->n > 0) {
+    if (!y) return fail(HYB_ERR_INVALID_ARG, "y is NULL");
+    if (ldy < L->n) return fail(HYB_ERR_INVALID_ARG, "y row stride %lld < n = %lld", (long long)ldy, (long long)L->n);
+    if (!aligned(y, elem_size(y_dtype))) return fail(HYB_ERR_INVALID_ARG, "y is not aligned to its element size");
+  }
+  return HYB_OK;
+}
+
+hyb_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HYB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hyb_abi_version(void) { return HYB_ABI_VERSION; }
+
+const char* hyb_status_str(hyb_status s) {
+  switch (s) {
+    case HYB_OK: return "HYB_OK";
+    case HYB_ERR_INVALID_ARG: return "HYB_ERR_INVALID_ARG";
+    case HYB_ERR_SHAPE: return "HYB_ERR_SHAPE";
+    case HYB_ERR_DTYPE: return "HYB_ERR_DTYPE";
+    case HYB_ERR_UNSUPPORTED: return "HYB_ERR_UNSUPPORTED";
+    case HYB_ERR_FORMAT: return "HYB_ERR_FORMAT";
+    case HYB_ERR_HIP: return "HYB_ERR_HIP";
+    default: return "HYB_ERR_UNKNOWN";
+  }
+}
+
+const char* hyb_last_error(void) { return g_last_error.c_str(); }
+
+hyb_status hyb_plan(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t dtype, int32_t meta,
+                    const uint8_t* tile_map, hyb_layout* out, int32_t* tidx_out) {
+  if (!out) return fail(HYB_ERR_INVALID_ARG, "out is NULL");
+  hyb_status st = check_geometry(n, k, b1, b2, dtype, meta);
+  if (st != HYB_OK) return st;
+  const int64_t tn = n / b1, tk = k / b2, T = tn * tk;
+  if (T > 0 && !tile_map) return fail(HYB_ERR_INVALID_ARG, "tile_map is NULL");
+  if (T >= (int64_t(1) << 31)) return fail(HYB_ERR_SHAPE, "too many tiles");
+  int64_t nd = 0, ns = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    if (tile_map[t] > 1)
+      return fail(HYB_ERR_INVALID_ARG, "tile_map[%lld] = %u, must be 0 or 1", (long long)t, tile_map[t]);
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    if (tile_map[t]) {
+      if (tidx_out) tidx_out[t] = ~int32_t(ns);
+      ++ns;
+    } else {
+      if (tidx_out) tidx_out[t] = int32_t(nd);
+      ++nd;
+    }
+  }
+  hyb_layout L{};
+  L.magic = HYB_MAGIC;
+  L.version = HYB_VERSION;
+  L.n = n;
+  L.k = k;
+  L.b1 = b1;
+  L.b2 = b2;
+  L.dtype = dtype;
+  L.meta = meta;
+  L.tiles_n = tn;
+  L.tiles_k = tk;
+  L.n_dense = nd;
+  L.n_sparse = ns;
+  fill_sizes(&L);
+  *out = L;
+  return ok();
+}
+
+hyb_status hyb_pack(const hyb_layout* layout, const void* w, int64_t ldw, const hyb_packed* dst,
+                    void* stream) {
+  hyb_status st = check_layout(layout, true);
+  if (st != HYB_OK) return st;
+  if (layout->n == 0 || layout->k == 0) return ok();
+  st = check_packed(layout, dst);
+  if (st != HYB_OK) return st;
+  st = check_matrix_arg(w, layout->n, layout->k, ldw, "w");
+  if (st != HYB_OK) return st;
+  return hip_status(hyb::launch_pack(*layout, w, ldw, *dst, static_cast<hipStream_t>(stream)),
+                    "pack launch");
+}
+
+hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_out, int64_t ldw,
+                      void* stream) {
+  hyb_status st = check_layout(layout, true);
+  if (st != HYB_OK) return st;
+  if (layout->n == 0 || layout->k == 0) return ok();
+  st = check_packed(layout, src);
+  if (st != HYB_OK) return st;
+  st = check_matrix_arg(w_out, layout->n, layout->k, ldw, "w_out");
+  if (st != HYB_OK) return st;
+  return hip_status(hyb::launch_unpack(*layout, *src, w_out, ldw, static_cast<hipStream_t>(stream)),
+                    "unpack launch");
+}
+
+hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                    int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, hyb::kMaxGemvM);
+  if (st != HYB_OK) return st;
+  if (m == 0 || layout->n == 0) return ok();
+  if (int64_t(m) * ldx * 2 >= (int64_t(1) << 31))
+    return fail(HYB_ERR_UNSUPPORTED, "decode kernel needs m * ldx * 2 < 2^31 bytes of x");
+  return hip_status(hyb::launch_gemv(*layout, *w, x, m, ldx, y, y_dtype, ldy,
+                                     static_cast<hipStream_t>(stream)),
+                    "gemv launch");
+}
+
+hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                         int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
+  if (st != HYB_OK) return st;
+  if (m == 0 || layout->n == 0) return ok();
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy,
+                                     static_cast<hipStream_t>(stream)),
+                    "gemm launch");
+}
+
+hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                    int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  if (m >= 0 && m <= hyb::kMaxGemvM) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Internal interface between the host-side argument checks (hyb_api.cpp) and
+// the kernel launchers (hyb_kernels.hip).  Everything reaching a launcher has
+// already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/hyb.h"
+
+namespace hyb {
+
+// Decode kernel handles up to this many tokens per launch.
+constexpr int kMaxGemvM = 16;
+
+hipError_t launch_pack(const hyb_layout& L, const void* w, int64_t ldw, const hyb_packed& P,
+                       hipStream_t s);
+hipError_t launch_unpack(const hyb_layout& L, const hyb_packed& P, void* w, int64_t ldw,
+                         hipStream_t s);
+hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
+                       int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
+                       int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
+
+}  // namespace hyb

@@ -1,0 +1,399 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars: pack / unpack bit-exact; products within |y - y_ref| <= 2e-3 * s per
+element (s = sum_k |w x|), plus bitwise closed forms (one-hot, small
+integers, zero input).  Large workloads are checked on whole sampled tile
+rows that the oracle prunes and multiplies on its own."""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from matmul_pack_b1_amd import binding as hb
+from matmul_pack_b1_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+REL = 2e-3
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return torch
+
+
+def note(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return _torch().device("cuda:0")
+
+
+def upload(bits, dtype):
+    return hb.bits_to_tensor(bits, dtype, dev())
+
+
+def assert_close(y, yref, s, extra=0.0, what=""):
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - yref)
+    bound = REL * s + extra
+    bad = err > bound
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside bound; first at {tuple(i)}: "
+                             f"y={y[tuple(i)]!r} ref={yref[tuple(i)]!r} s={s[tuple(i)]!r}")
+
+
+def pack_gpu(w_bits, tmap, b1, b2, dtype, meta):
+    torch = _torch()
+    w = upload(w_bits, dtype)
+    P = hb.pack(w, tmap, b1, b2, meta)
+    torch.cuda.synchronize()
+    return P
+
+
+def streams(P):
+    return {
+        "dense": P.dense.cpu().numpy().view(np.uint16),
+        "val": P.val.cpu().numpy().view(np.uint16),
+        "meta": P.meta.cpu().numpy(),
+        "tidx": P.tidx.cpu().numpy(),
+    }
+
+
+def random_case(seed, n, k, b1, b2, dtype, frac=0.5, sigma=0.02):
+    rng = np.random.default_rng(seed)
+    w = wl.float32_to_bits(rng.standard_normal((n, k)).astype(np.float32) * sigma, dtype)
+    tmap = (rng.random((n // b1, k // b2)) < frac).astype(np.uint8)
+    return w, tmap
+
+
+@functools.lru_cache(maxsize=4)
+def workload_matrix(config, index):
+    mat = wl.workload(config).matrices[index]
+    return mat, mat.weight_bits(), mat.tile_map()
+
+
+def sample_tile_rows(mat, count, seed=0):
+    rng = np.random.default_rng(seed)
+    tn = mat.n // mat.b1
+    return np.sort(rng.choice(tn, size=min(count, tn), replace=False))
+
+
+def oracle_rows(w_bits, tmap, mat, tile_rows, x_bits):
+    """Oracle y/s for the rows of the chosen tile rows only."""
+    rows = np.concatenate([np.arange(t * mat.b1, (t + 1) * mat.b1) for t in tile_rows])
+    sub = oracle.prune(w_bits[rows], tmap[tile_rows], mat.b1, mat.b2)
+    y, s = oracle.ref_matmul(sub, x_bits, mat.dtype)
+    return rows, y, s
+
+
+# ------------------------------------------------------------- pack -------
+
+@pytest.mark.parametrize("b1,b2", [(64, 64), (64, 128), (128, 128), (128, 256), (256, 64), (256, 256)])
+@pytest.mark.parametrize("meta", ["idx2", "mask4"])
+def test_pack_unpack_random(b1, b2, meta):
+    dtype = "bf16" if b2 != 256 else "f16"
+    note(f"pack random {b1}x{b2} {meta} {dtype}")
+    w, tmap = random_case(b1 + b2, 3 * b1, 3 * b2, b1, b2, dtype)
+    # sprinkle ties, signed zeros, subnormals, Inf and NaN
+    rng = np.random.default_rng(1)
+    for v in (0x8000, 0x0000, 0x0001, 0x8003, 0x7C00 if dtype == "f16" else 0x7F80, 0xFFC0):
+        w[rng.random(w.shape) < 0.02] = v
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    ref = oracle.pack(w, tmap, b1, b2, meta)
+    got = streams(P)
+    for key in ("dense", "val", "meta", "tidx"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    u = hb.tensor_to_bits(hb.unpack(P))
+    np.testing.assert_array_equal(u, oracle.prune(w, tmap, b1, b2))
+
+
+@pytest.mark.parametrize("config,index,meta", [(1, 0, "idx2"), (1, 0, "mask4"), (2, 0, "idx2"),
+                                               (2, 0, "mask4"), (5, 0, "idx2"), (3, 1, "mask4")])
+def test_pack_unpack_workloads(config, index, meta):
+    mat, w, tmap = workload_matrix(config, index)
+    note(f"pack workload {config}/{mat.name} {meta}")
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, meta)
+    ref = oracle.pack(w, tmap, mat.b1, mat.b2, meta)
+    got = streams(P)
+    for key in ("dense", "val", "meta", "tidx"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    u = hb.tensor_to_bits(hb.unpack(P))
+    np.testing.assert_array_equal(u, oracle.prune(w, tmap, mat.b1, mat.b2))
+
+
+# ------------------------------------------------------------- GEMV -------
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 11, 16])
+@pytest.mark.parametrize("b1,b2,dtype,meta", [(64, 64, "bf16", "idx2"), (128, 128, "f16", "mask4"),
+                                              (64, 256, "bf16", "mask4"), (256, 128, "bf16", "idx2")])
+def test_gemv_random(m, b1, b2, dtype, meta):
+    note(f"gemv random m={m} {b1}x{b2} {dtype} {meta}")
+    torch = _torch()
+    w, tmap = random_case(m * 7 + b2, 2 * b1, 5 * b2, b1, b2, dtype)
+    x = wl.float32_to_bits(np.random.default_rng(m).standard_normal((m, 5 * b2)).astype(np.float32), dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    y = hb.gemv(P, upload(x, dtype))
+    torch.cuda.synchronize()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x, dtype)
+    assert_close(y.cpu().numpy(), yref, s, what="gemv")
+
+
+@pytest.mark.parametrize("config,index,m", [(1, 0, 1), (2, 0, 1), (2, 0, 4), (2, 0, 16),
+                                            (3, 0, 1), (3, 1, 4), (3, 2, 16), (3, 3, 1),
+                                            (3, 4, 4), (3, 5, 16), (3, 6, 1), (3, 6, 16)])
+def test_gemv_workloads(config, index, m):
+    torch = _torch()
+    mat, w, tmap = workload_matrix(config, index)
+    note(f"gemv workload {config}/{mat.name} m={m}")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    y = hb.gemv(P, upload(x, mat.dtype)).cpu().numpy()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, mat.b1, mat.b2), x, mat.dtype)
+    assert_close(y, yref, s, what=f"config {config} {mat.name} m={m}")
+
+
+@pytest.mark.parametrize("index", range(6))
+def test_gemv_70b_endpoints_sampled(index):
+    """28672x8192 and 8192x28672 at 0%, 100% and checkerboard sparse tiles,
+    full-size launch, checked on 8 sampled tile rows."""
+    torch = _torch()
+    mat = wl.workload(4).matrices[index]
+    note(f"gemv 70B {mat.name}")
+    w, tmap = mat.weight_bits(), mat.tile_map()
+    x = mat.activation_bits(1)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    y = hb.gemv(P, upload(x, mat.dtype)).cpu().numpy()
+    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 8, index), x)
+    assert_close(y[:, rows], yref, s, what=mat.name)
+    expect = {"dense": 0, "sparse": tmap.size}.get(mat.name.split("_")[1], tmap.size // 2)
+    assert P.layout.n_sparse == expect
+
+
+def test_gemv_output_16bit():
+    torch = _torch()
+    mat, w, tmap = workload_matrix(2, 0)
+    note("gemv bf16 output")
+    x = mat.activation_bits(3)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    y = hb.gemv(P, upload(x, "bf16"), out_dtype=torch.bfloat16)
+    yb = oracle.widen(hb.tensor_to_bits(y), "bf16")
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, mat.b1, mat.b2), x, "bf16")
+    half_ulp = np.abs(yref) * 2.0 ** -8 + 1e-30
+    assert_close(yb, yref, s, extra=half_ulp, what="bf16 out")
+
+
+# ------------------------------------------------------------- GEMM -------
+
+@pytest.mark.parametrize("m", [17, 33, 64, 100, 130, 257])
+@pytest.mark.parametrize("b1,b2,dtype,meta", [(64, 64, "bf16", "idx2"), (128, 128, "f16", "mask4"),
+                                              (256, 256, "bf16", "mask4"), (64, 128, "bf16", "idx2")])
+def test_gemm_random(m, b1, b2, dtype, meta):
+    note(f"gemm random m={m} {b1}x{b2} {dtype} {meta}")
+    torch = _torch()
+    n = 3 * b1 if b1 == 64 else 2 * b1   # 192 rows exercises a half-empty 128-row block
+    k = 3 * b2
+    w, tmap = random_case(m + b1, n, k, b1, b2, dtype)
+    x = wl.float32_to_bits(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32), dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    y = hb.gemm(P, upload(x, dtype))
+    torch.cuda.synchronize()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x, dtype)
+    assert_close(y.cpu().numpy(), yref, s, what="gemm")
+
+
+@pytest.mark.parametrize("m", [16, 64, 256, 2048])
+def test_gemm_qwen14b_sampled(m):
+    """17408x5120, 64x64 tiles, 60% sparse tiles; M from 16 to 2048 through
+    hyb_gemm (decode kernel at 16) and the matrix-core kernel for every M."""
+    torch = _torch()
+    mat, w, tmap = workload_matrix(5, 0)
+    note(f"gemm qwen14b m={m}")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    xt = upload(x, mat.dtype)
+    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 6, m), x)
+    y = hb.gemm(P, xt).cpu().numpy()
+    assert_close(y[:, rows], yref, s, what=f"gemm m={m}")
+    y2 = hb.gemm_mfma(P, xt).cpu().numpy()
+    assert_close(y2[:, rows], yref, s, what=f"gemm_mfma m={m}")
+
+
+def test_gemm_output_16bit():
+    torch = _torch()
+    note("gemm fp16 output")
+    w, tmap = random_case(3, 256, 512, 128, 128, "f16")
+    x = wl.float32_to_bits(np.random.default_rng(3).standard_normal((96, 512)).astype(np.float32), "f16")
+    P = pack_gpu(w, tmap, 128, 128, "f16", "idx2")
+    y = hb.gemm(P, upload(x, "f16"), out_dtype=torch.float16)
+    yb = oracle.widen(hb.tensor_to_bits(y), "f16")
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, 128, 128), x, "f16")
+    assert_close(yb, yref, s, extra=np.abs(yref) * 2.0 ** -11 + 2.0 ** -25, what="f16 out")
+
+
+# ------------------------------------------------------- exact pins -------
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm_mfma"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_one_hot_columns_exact(kernel, dtype):
+    """x = e_c gives column c of W' bit for bit (subnormals included)."""
+    torch = _torch()
+    note(f"one-hot {kernel} {dtype}")
+    b1, b2 = 64, 128
+    w, tmap = random_case(11, 2 * b1, 2 * b2, b1, b2, dtype)
+    w[::7, ::5] = 0x0001   # smallest subnormal
+    cols = np.array([0, 1, 63, 64, 100, 127, 128, 255])
+    one = 0x3F80 if dtype == "bf16" else 0x3C00
+    m = len(cols) if kernel == "gemv" else 32
+    x = np.zeros((m, 2 * b2), np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = one
+    P = pack_gpu(w, tmap, b1, b2, dtype, "mask4")
+    fn = hb.gemv if kernel == "gemv" else hb.gemm_mfma
+    y = fn(P, upload(x, dtype)).cpu().numpy()
+    wp = oracle.prune(w, tmap, b1, b2)
+    for i, c in enumerate(cols):
+        np.testing.assert_array_equal(y[i], oracle.widen(wp[:, c], dtype).astype(np.float32))
+    assert np.all(y[len(cols):] == 0)
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm_mfma"])
+def test_small_integers_exact(kernel):
+    torch = _torch()
+    note(f"integers {kernel}")
+    rng = np.random.default_rng(12)
+    b1, b2 = 128, 64
+    n, k, m = 256, 640, (5 if kernel == "gemv" else 70)
+    w = wl.float32_to_bits(rng.integers(-3, 4, size=(n, k)).astype(np.float32), "bf16")
+    x = wl.float32_to_bits(rng.integers(-3, 4, size=(m, k)).astype(np.float32), "bf16")
+    tmap = (rng.random((n // b1, k // b2)) < 0.5).astype(np.uint8)
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    fn = hb.gemv if kernel == "gemv" else hb.gemm_mfma
+    y = fn(P, upload(x, "bf16")).cpu().numpy()
+    yref, _ = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x, "bf16")
+    np.testing.assert_array_equal(y.astype(np.float64), yref)
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm_mfma"])
+def test_zero_input_gives_plus_zero(kernel):
+    torch = _torch()
+    note(f"zero input {kernel}")
+    w, tmap = random_case(13, 128, 256, 64, 128, "bf16")
+    P = pack_gpu(w, tmap, 64, 128, "bf16", "idx2")
+    x = torch.zeros((4 if kernel == "gemv" else 40, 256), dtype=torch.bfloat16, device=dev())
+    fn = hb.gemv if kernel == "gemv" else hb.gemm_mfma
+    y = fn(P, x).cpu().numpy()
+    assert np.all(y == 0) and not np.any(np.signbit(y))
+
+
+# ------------------------------------------------------------ edges -------
+
+def test_empty_and_degenerate():
+    torch = _torch()
+    note("edges")
+    # k = 0: no tiles along K, the product is an empty sum
+    P = pack_gpu(np.zeros((128, 0), np.uint16), np.zeros((2, 0), np.uint8), 64, 64, "bf16", "idx2")
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=dev())
+    y = torch.full((3, 128), 7.0, device=dev())
+    hb.gemv(P, x, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    y = torch.full((40, 128), 7.0, device=dev())
+    hb.gemm_mfma(P, torch.zeros((40, 0), dtype=torch.bfloat16, device=dev()), out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    # m = 0 leaves y untouched
+    w, tmap = random_case(14, 64, 64, 64, 64, "bf16")
+    P = pack_gpu(w, tmap, 64, 64, "bf16", "idx2")
+    y = torch.full((0, 64), 1.0, device=dev())
+    hb.gemv(P, torch.zeros((0, 64), dtype=torch.bfloat16, device=dev()), out=y)
+    # n = 0
+    P0 = pack_gpu(np.zeros((0, 128), np.uint16), np.zeros((0, 2), np.uint8), 64, 64, "bf16", "idx2")
+    hb.gemv(P0, torch.zeros((2, 128), dtype=torch.bfloat16, device=dev()))
+    # all-dense and all-sparse maps
+    for val in (0, 1):
+        w, _ = random_case(15, 128, 256, 64, 128, "bf16")
+        tmap = np.full((2, 2), val, np.uint8)
+        P = pack_gpu(w, tmap, 64, 128, "bf16", "idx2")
+        x = wl.float32_to_bits(np.random.default_rng(val).standard_normal((2, 256)).astype(np.float32), "bf16")
+        y = hb.gemv(P, upload(x, "bf16")).cpu().numpy()
+        yref, s = oracle.ref_matmul(oracle.prune(w, tmap, 64, 128), x, "bf16")
+        assert_close(y, yref, s, what=f"map={val}")
+    torch.cuda.synchronize()
+
+
+def test_strided_rows():
+    """x and y with row strides larger than their widths."""
+    torch = _torch()
+    note("strides")
+    w, tmap = random_case(16, 128, 256, 64, 128, "bf16")
+    P = pack_gpu(w, tmap, 64, 128, "bf16", "idx2")
+    x = wl.float32_to_bits(np.random.default_rng(2).standard_normal((3, 256)).astype(np.float32), "bf16")
+    xbig = torch.zeros((3, 264), dtype=torch.bfloat16, device=dev())
+    xbig[:, :256] = upload(x, "bf16")
+    ybig = torch.full((3, 200), 5.0, device=dev())
+    hb.gemv(P, xbig[:, :256], out=ybig[:, :128])
+    torch.cuda.synchronize()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, 64, 128), x, "bf16")
+    assert_close(ybig[:, :128].cpu().numpy(), yref, s, what="strided")
+    assert torch.all(ybig[:, 128:] == 5.0)
+
+
+def test_corrupt_tile_index_is_skipped():
+    """tidx entries naming slots outside the streams are skipped by the
+    kernels' own bounds checks (no access outside the buffers)."""
+    torch = _torch()
+    note("corrupt tidx")
+    w, tmap = random_case(17, 128, 256, 64, 128, "bf16")
+    P = pack_gpu(w, tmap, 64, 128, "bf16", "idx2")
+    tid = P.tidx.cpu().numpy().copy()
+    bad = tid.copy()
+    bad[0] = 1 << 30          # dense slot far out of range
+    bad[-1] = -(1 << 30)      # sparse slot far out of range
+    P.tidx.copy_(torch.from_numpy(bad))
+    x = wl.float32_to_bits(np.random.default_rng(3).standard_normal((2, 256)).astype(np.float32), "bf16")
+    y = hb.gemv(P, upload(x, "bf16")).cpu().numpy()
+    y2 = hb.gemm_mfma(P, upload(x, "bf16")).cpu().numpy()
+    # the rows of the remaining tiles are still right
+    keep = tmap.copy()
+    wp = oracle.prune(w, tmap, 64, 128)
+    wp[0:64, 0:128] = 0
+    wp[64:128, 128:256] = 0
+    yref, s = oracle.ref_matmul(wp, x, "bf16")
+    assert_close(y, yref, s, what="gemv corrupt")
+    assert_close(y2, yref, s, what="gemm corrupt")
+    del keep
+
+
+def test_deterministic():
+    torch = _torch()
+    note("determinism")
+    mat, w, tmap = workload_matrix(2, 0)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    x = upload(mat.activation_bits(4), "bf16")
+    a = hb.gemv(P, x).cpu().numpy()
+    b = hb.gemv(P, x).cpu().numpy()
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_all_dense_matches_torch_matmul():
+    """Independent check of the dense path: hipBLAS via torch.matmul."""
+    torch = _torch()
+    note("dense vs torch.matmul")
+    mat, w, _ = workload_matrix(2, 0)
+    tmap = np.zeros((mat.tiles_n, mat.tiles_k), np.uint8)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    x = upload(mat.activation_bits(2), "bf16")
+    y = hb.gemv(P, x)
+    wt = upload(w, "bf16").float()
+    yt = x.float() @ wt.t()
+    s = x.float().abs() @ wt.abs().t()
+    assert torch.all((y - yt).abs() <= 4e-3 * s + 1e-6)
