@@ -233,6 +233,10 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
   if (st != HYB_OK) return st;
   if (m == 0 || layout->n == 0) return ok();
+  if (ldx * 2 * 256 >= (int64_t(1) << 31))
+    return fail(HYB_ERR_UNSUPPORTED, "matrix-core kernel needs ldx < 4194304 elements");
+  if ((int64_t(m) + 15) / 16 > 65535 * 8)
+    return fail(HYB_ERR_UNSUPPORTED, "m = %d too large for one launch", m);
   return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy,
                                      static_cast<hipStream_t>(stream)),
                     "gemm launch");

@@ -37,6 +37,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
+typedef __attribute__((ext_vector_type(16))) __bf16 bf16x16_t;
+typedef __attribute__((ext_vector_type(16))) _Float16 half16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 // ------------------------------------------------------------- helpers ----
@@ -483,191 +485,266 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ d
 
 // ---------------------------------------------------------------- GEMM ----
 //
-// Y[m, n] = sum_k X[m, k] W'[n, k] for any M, on 16x16x32 MFMA.
-// Workgroup tile 128 (n) x 128 (m), 4 wavefronts in a 2 x 2 grid, each
-// 64 (n) x 64 (m) = 4 x 4 MFMA blocks.  The k loop walks 64-column blocks.
-// A operands (W') come straight from the streams into registers -- a dense
-// chunk already is the A layout; a sparse chunk is expanded in registers
-// with v_perm to the 16 columns its lane owns, and the B operand (X, staged
-// in LDS, double buffered) is read with the matching column permutation, so
-// the products are those of W' in any case.
+// Y[m, n] = sum_k X[m, k] W'[n, k] for any M on the matrix cores.
+// A workgroup is 4 wavefronts arranged WN (along n) x WK (along K).  Each
+// wavefront owns 64 rows (four 16-row slabs) and, over its share of the K
+// steps, multiplies them with the workgroup's BM = 16 * MB tokens.  A K step
+// is 64 columns.  A dense slab piece is two 16x16x32 MFMA A operands taken
+// straight from the dense stream; a sparse slab piece is one
+// v_smfmac_*_16x16x64 A operand (32 kept values per row) with its 2-bit
+// indices: the stored value chunk and its idx2 word are exactly that
+// instruction's operand layout, so sparse tiles run on the sparse matrix
+// cores at twice the dense rate with no expansion.  Both kinds take the same
+// B operands (X[m][8q..8q+7] and X[m][32+8q..32+8q+7] for lane group q),
+// read from a double-buffered LDS tile of X.  A operands are raw buffer
+// loads one K step ahead (branch-free, as in the decode kernel).  With
+// WK > 1 the partial sums of the K groups are added in a fixed order through
+// LDS, so results are reproducible.
 
-struct GemmParams {
-  const uint4* dense;
-  const uint4* val;
-  const uint16_t* meta;
-  const int32_t* tidx;
-  const uint16_t* x;
-  int64_t ldx;
-  void* y;
-  int64_t ldy;
-  int64_t n, tiles_k, n_dense, n_sparse;
-  int b1, m, ydt, meta_kind;
+struct GemmDims {
+  int64_t ldx, ldy;
+  int32_t n, m, tiles_k, n_dense, n_sparse;
+  int b1, ydt;
 };
 
-constexpr int kGemmBN = 128, kGemmBM = 128, kGemmBK = 64;
-constexpr int kXsStride = kGemmBK + 8;  // padded LDS row (elements)
+struct GemmAStage {
+  uint4 a[4][2];     // per slab: dense chunks 2kb, 2kb+1, or the sparse value chunk in a[.][0]
+  uint32_t word[4];  // per slab: the sparse chunk's metadata word
+};
 
-template <int B2, int DT>
-__global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGemmBM * kXsStride];
+template <int DT>
+__device__ __forceinline__ f32x4_t smfmac16x16x64(uint4 a, uint4 b0, uint4 b1, uint32_t idx, f32x4_t c) {
+  const uint32_t bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  if constexpr (DT == HYB_BF16) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                     __builtin_bit_cast(bf16x16_t, bb), c, idx, 0, 0);
+  } else {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
+                                                    __builtin_bit_cast(half16_t, bb), c, idx, 0, 0);
+  }
+}
+
+// 2-bit index word (i0 | i1 << 2 per group) from a metadata word.
+template <int META>
+__device__ __forceinline__ uint32_t idx2_word(uint32_t word) {
+  if constexpr (META == HYB_META_IDX2) {
+    return word & 0xFFFFu;
+  } else {
+    uint32_t out = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t i0, i1;
+      nibble_positions_t<HYB_META_MASK4>((word >> (4 * g)) & 0xFu, i0, i1);
+      out |= ((i0 & 3u) | ((i1 & 3u) << 2)) << (4 * g);
+    }
+    return out;
+  }
+}
+
+// A operands of one K step for the wavefront's four slabs.  The resources
+// cover the four slab pieces of the tile; the second chunk of a sparse slab
+// and the metadata of a dense one fall outside and read as zero with no
+// memory access, as does everything for an out-of-range slot.
+template <int B2>
+__device__ __forceinline__ void gemm_load_a(GemmAStage& st, int32_t ti, int kb,
+                                            const uint4* __restrict__ dense,
+                                            const uint4* __restrict__ val,
+                                            const uint16_t* __restrict__ meta, const GemmDims& d,
+                                            int rs0, int lane) {
+  const bool is_dense = ti >= 0;
+  const int32_t slot = is_dense ? ti : ~ti;
+  const bool ok = is_dense ? (slot < d.n_dense) : (slot < d.n_sparse);
+  const int64_t tile = int64_t(d.b1) * B2;
+  const int32_t slab_bytes = is_dense ? 32 * B2 : 16 * B2;
+  const char* base = is_dense
+      ? reinterpret_cast<const char*>(dense) + (int64_t(slot) * tile + int64_t(rs0) * 16 * B2) * 2
+      : reinterpret_cast<const char*>(val) + (int64_t(slot) * (tile / 2) + int64_t(rs0) * 8 * B2) * 2;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, ok ? 4 * slab_bytes : 0);
+  const int32_t c0 = is_dense ? 2 * kb * 1024 : kb * 1024;
+  const int32_t c1 = is_dense ? c0 + 1024 : 0x40000000;
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    st.a[sl][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+        r, sl * slab_bytes + c0 + lane * 16, 0, HYB_W_AUX));
+    st.a[sl][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+        r, sl * slab_bytes + c1 + lane * 16, 0, HYB_W_AUX));
+  }
+  const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs0) * B2) * 2;
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(mbase, (ok && !is_dense) ? 4 * 2 * B2 : 0);
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl)
+    st.word[sl] = __builtin_amdgcn_raw_buffer_load_b16(mr, sl * 2 * B2 + lane * (B2 / 32) + kb * 2, 0, 0);
+}
+
+template <int WK, int MB, int WN>
+struct GemmSmem {
+  static constexpr int kRow = 72;  // padded X row in the LDS tile (elements)
+  static constexpr int kXsBytes = WK * 2 * 16 * MB * kRow * 2;
+  static constexpr int kRedBytes = (WK - 1) * WN * 4 * MB * 64 * 16;
+  static constexpr int kBytes = kXsBytes > kRedBytes ? kXsBytes : kRedBytes;
+};
+
+template <int B2, int DT, int META, int WN, int WK, int MB>
+__global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
+                                              const uint4* __restrict__ val,
+                                              const uint16_t* __restrict__ meta,
+                                              const int32_t* __restrict__ tidx,
+                                              const uint16_t* __restrict__ x,
+                                              void* __restrict__ y, GemmDims d) {
+  static_assert(WN * WK == 4, "four wavefronts per workgroup");
+  using Smem = GemmSmem<WK, MB, WN>;
+  constexpr int BM = 16 * MB;
+  constexpr int kRow = Smem::kRow;
+  constexpr int kStepsPerTile = B2 / 64;
+  __shared__ __attribute__((aligned(16))) char smem[Smem::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN, wk = wave / WN;
   const int q = lane >> 4;
-  const int64_t n0 = int64_t(blockIdx.x) * kGemmBN + wn * 64;  // first row of this wave
-  const int64_t m0 = int64_t(blockIdx.y) * kGemmBM;
-  const bool rows_ok = n0 < p.n;
-  const int64_t tn = n0 / p.b1;
-  const int rs0 = int((n0 - tn * p.b1) / 16);
-  const int32_t* trow = p.tidx + tn * p.tiles_k;
-  constexpr int kb_per_tile = B2 / kGemmBK;
-  const int64_t steps = p.tiles_k * kb_per_tile;
-  const int64_t dense_tile = int64_t(p.b1) * B2 / 8;
-  const int64_t val_tile = int64_t(p.b1) * B2 / 16;
-  const int64_t meta_tile = int64_t(p.b1) * B2 / 16;
+  const int32_t n0 = int32_t(blockIdx.x) * 64 * WN + wn * 64;   // first row of this wavefront
+  const int32_t m0 = int32_t(blockIdx.y) * BM;
+  const bool rows_ok = n0 < d.n;
+  const int32_t tn = n0 / d.b1;
+  const int rs0 = (n0 - tn * d.b1) / 16;
+  const int32_t steps = d.tiles_k * kStepsPerTile;
+  const int32_t s0 = (wk * steps) / WK;
+  const int32_t cnt = ((wk + 1) * steps) / WK - s0;
+  const int32_t iters = (steps + WK - 1) / WK;   // same trip count in every K group
+  const int32_t* __restrict__ trow = tidx + int64_t(tn) * d.tiles_k;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem) + wk * 2 * BM * kRow;
 
-  // raw A data for one k step: 4 slabs x (2 dense chunks | 1 value chunk + word)
-  struct ARaw {
-    uint4 a[4][2];
-    uint32_t word[4];
-    int kind;  // 0 dense, 1 sparse, 2 skip
+  // X tile loads of this K group: BM rows x 64 columns = BM * 8 pieces over
+  // the 64 * WN threads of the group; rows >= M read as zero.
+  constexpr int kPieces = BM * 8;
+  constexpr int kXr = (kPieces + 64 * WN - 1) / (64 * WN);
+  const int gt = wn * 64 + lane;  // thread index inside the K group
+  const int32_t mrows = d.m - m0 < BM ? d.m - m0 : BM;
+  auto load_x = [&](int32_t it, uint4 (&xr)[kXr]) {
+    const bool live = it < cnt;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(x + int64_t(m0) * d.ldx + int64_t(s0 + it) * 64,
+                                               live ? int32_t(mrows * d.ldx * 2) : 0);
+#pragma unroll
+    for (int i = 0; i < kXr; ++i) {
+      const int pc = gt + 64 * WN * i;
+      const int row = pc >> 3, c8 = pc & 7;
+      const int off = (pc < kPieces) ? int(row * d.ldx * 2) + c8 * 16 : 0x40000000;
+      xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
   };
-
-  auto load_a = [&](int64_t step, ARaw& r) {
-    const int64_t tk = step / kb_per_tile;
-    const int kb = int(step - tk * kb_per_tile);
-    const int32_t ti = rows_ok ? __builtin_amdgcn_readfirstlane(trow[tk]) : 0;
-    r.kind = 2;
-    if (!rows_ok) return;
-    if (ti >= 0) {
-      if (ti >= p.n_dense) return;
-      r.kind = 0;
-      const uint4* src = p.dense + ti * dense_tile + lane;
+  auto store_x = [&](int buf, const uint4 (&xr)[kXr]) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) r.a[sl][h] = src[(int64_t(rs0 + sl) * 2 * B2) + (2 * kb + h) * 64];
-      }
-    } else {
-      const int64_t s = ~int64_t(ti);
-      if (s >= p.n_sparse) return;
-      r.kind = 1;
-      const uint4* src = p.val + s * val_tile + lane;
-      const uint16_t* msrc = p.meta + s * meta_tile + lane * (B2 / 64) + kb;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        r.a[sl][0] = src[int64_t(rs0 + sl) * B2 + kb * 64];
-        r.word[sl] = msrc[int64_t(rs0 + sl) * B2];
+    for (int i = 0; i < kXr; ++i) {
+      const int pc = gt + 64 * WN * i;
+      if (pc < kPieces) {
+        const int row = pc >> 3, c8 = pc & 7;
+        *reinterpret_cast<uint4*>(xs + buf * BM * kRow + row * kRow + c8 * 8) = xr[i];
       }
     }
   };
-
-  // X tile for one k step: 128 rows x 64 columns = 1024 pieces of 16 B.
-  auto load_x = [&](int64_t step, uint4 (&xr)[4]) {
-    const int64_t k0 = step * kGemmBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pc = tid + 256 * i;
-      const int r = pc >> 3, c8 = pc & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + r < p.m) v = *reinterpret_cast<const uint4*>(p.x + (m0 + r) * p.ldx + k0 + c8 * 8);
-      xr[i] = v;
-    }
-  };
-  auto store_x = [&](int buf, const uint4 (&xr)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pc = tid + 256 * i;
-      const int r = pc >> 3, c8 = pc & 7;
-      *reinterpret_cast<uint4*>(&xs[buf][r * kXsStride + c8 * 8]) = xr[i];
-    }
+  constexpr int32_t kNone = INT32_MIN;
+  auto tile_index = [&](int32_t it) -> int32_t {
+    if (!rows_ok || it >= cnt) return kNone;
+    return trow[(s0 + it) / kStepsPerTile];
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][MB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  ARaw anext;
-  uint4 xr[4];
-  if (steps > 0) {
-    load_a(0, anext);
-    load_x(0, xr);
-    store_x(0, xr);
-  }
-  __syncthreads();
-
-  for (int64_t step = 0; step < steps; ++step) {
-    const int buf = int(step & 1);
-    ARaw acur = anext;
-    if (step + 1 < steps) {
-      load_a(step + 1, anext);
-      load_x(step + 1, xr);
-    }
-    if (acur.kind != 2) {
-      uint4 a[4][2];
-      if (acur.kind == 0) {
+  auto compute = [&](const GemmAStage& a, int32_t ti, int buf) {
+    if (ti == kNone) return;
+    const bool is_dense = ti >= 0;
+    if (is_dense ? (ti >= d.n_dense) : (~ti >= d.n_sparse)) return;
+    uint32_t idx[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) idx[sl] = idx2_word<META>(a.word[sl]);
+    const uint16_t* xb = xs + buf * BM * kRow;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint16_t* xrow = xb + (mb * 16 + (lane & 15)) * kRow + q * 8;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(xrow);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(xrow + 32);
+      if (is_dense) {
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-          a[sl][0] = acur.a[sl][0];
-          a[sl][1] = acur.a[sl][1];
+          acc[sl][mb] = mfma16x16x32<DT>(a.a[sl][0], b0, acc[sl][mb]);
+          acc[sl][mb] = mfma16x16x32<DT>(a.a[sl][1], b1, acc[sl][mb]);
         }
       } else {
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-          const uint4 v = acur.a[sl][0];
-          const uint32_t pv[4] = {v.x, v.y, v.z, v.w};
-          uint32_t o[8];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint32_t i0, i1;
-            nibble_positions((acur.word[sl] >> (4 * g)) & 0xFu, p.meta_kind, i0, i1);
-            o[2 * g] = __builtin_amdgcn_perm(0u, pv[g], scatter_selector(0, i0, i1));
-            o[2 * g + 1] = __builtin_amdgcn_perm(0u, pv[g], scatter_selector(2, i0, i1));
-          }
-          a[sl][0] = make_uint4(o[0], o[1], o[2], o[3]);
-          a[sl][1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
-      }
-      // B operand column offset of this lane for MFMA half h:
-      // dense chunk h covers columns 32h + 8q..+7; expanded sparse half h
-      // covers columns 16q + 8h..+7.
-      const int kofs0 = acur.kind == 0 ? q * 8 : q * 16;
-      const int kstep = acur.kind == 0 ? 32 : 8;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const uint16_t* xrow = &xs[buf][(wm * 64 + mb * 16 + (lane & 15)) * kXsStride];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4 b = *reinterpret_cast<const uint4*>(xrow + kofs0 + h * kstep);
-#pragma unroll
-          for (int sl = 0; sl < 4; ++sl) acc[sl][mb] = mfma16x16x32<DT>(a[sl][h], b, acc[sl][mb]);
-        }
+        for (int sl = 0; sl < 4; ++sl) acc[sl][mb] = smfmac16x16x64<DT>(a.a[sl][0], b0, b1, idx[sl], acc[sl][mb]);
       }
     }
-    if (step + 1 < steps) store_x(buf ^ 1, xr);
+  };
+
+  // Two-stage ring, unrolled by two so stage registers are never copied.
+  GemmAStage A0, A1;
+  uint4 xr[kXr];
+  int32_t t0 = tile_index(0);
+  gemm_load_a<B2>(A0, t0, (s0 + 0) % kStepsPerTile, dense, val, meta, d, rs0, lane);
+  load_x(0, xr);
+  store_x(0, xr);
+  __syncthreads();
+  for (int32_t it = 0; it < iters; it += 2) {
+    const int32_t t1 = tile_index(it + 1);
+    gemm_load_a<B2>(A1, t1, (s0 + it + 1) % kStepsPerTile, dense, val, meta, d, rs0, lane);
+    load_x(it + 1, xr);
+    compute(A0, t0, 0);
+    store_x(1, xr);
     __syncthreads();
+    if (it + 1 >= iters) break;
+    t0 = tile_index(it + 2);
+    gemm_load_a<B2>(A0, t0, (s0 + it + 2) % kStepsPerTile, dense, val, meta, d, rs0, lane);
+    load_x(it + 2, xr);
+    compute(A1, t1, 1);
+    store_x(0, xr);
+    __syncthreads();
+  }
+
+  // Partial sums of K groups 1..WK-1 go through LDS to group 0, which adds
+  // them in group order.
+  if constexpr (WK > 1) {
+    float* red = reinterpret_cast<float*>(smem);
+    if (wk > 0) {
+      float* dst = red + ((wk - 1) * WN + wn) * (4 * MB * 64 * 4);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          *reinterpret_cast<f32x4_t*>(dst + ((sl * MB + mb) * 64 + lane) * 4) = acc[sl][mb];
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int g = 1; g < WK; ++g) {
+      const float* src = red + ((g - 1) * WN + wn) * (4 * MB * 64 * 4);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[sl][mb] += *reinterpret_cast<const f32x4_t*>(src + ((sl * MB + mb) * 64 + lane) * 4);
+    }
   }
 
   if (!rows_ok) return;
   // acc[sl][mb] lane L holds rows n0 + 16 sl + 4 (L/16) + 0..3 of token
-  // m0 + 64 wm + 16 mb + L%16.
-  const bool vec_ok = (p.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.y) & 15) == 0);
+  // m0 + 16 mb + L%16.
+  const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int64_t m = m0 + wm * 64 + mb * 16 + (lane & 15);
-    if (m >= p.m) continue;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t m = int64_t(m0) + mb * 16 + (lane & 15);
+    if (m >= d.m) continue;
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
-      const int64_t n = n0 + sl * 16 + q * 4;
+      const int64_t n = int64_t(n0) + sl * 16 + q * 4;
       const f32x4_t v = acc[sl][mb];
-      const int64_t base = m * p.ldy + n;
-      if (p.ydt == HYB_F32) {
-        float* dst = static_cast<float*>(p.y) + base;
+      const int64_t base = m * d.ldy + n;
+      if (d.ydt == HYB_F32) {
+        float* dst = static_cast<float*>(y) + base;
         if (vec_ok) {
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
@@ -675,13 +752,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           for (int e = 0; e < 4; ++e) dst[e] = v[e];
         }
       } else {
-        uint16_t o[4];
+        uint16_t* dst = static_cast<uint16_t*>(y) + base;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = p.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
-        uint16_t* dst = static_cast<uint16_t*>(p.y) + base;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = o[e];
+        for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
       }
     }
   }
@@ -802,42 +875,59 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
   return hipGetLastError();
 }
 
+namespace {
+
+template <int B2, int DT, int META, int WN, int WK, int MB>
+hipError_t gemm_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+  const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
+  if (gm > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid(unsigned((L.n + 64 * WN - 1) / (64 * WN)), unsigned(gm));
+  hipLaunchKernelGGL((k_gemm<B2, DT, META, WN, WK, MB>), grid, dim3(256), 0, s, q.dense, q.val, q.meta,
+                     q.tidx, q.x, q.y, d);
+  return hipGetLastError();
+}
+
+// Workgroup shape by token count: few tokens -> the four wavefronts split
+// K (more workgroups, weights streamed once); many tokens -> they split n
+// and share each X tile.
+template <int B2, int DT, int META>
+hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+  if (m <= 64) return gemm_go<B2, DT, META, 1, 4, 4>(L, q, m, d, s);
+  if (m <= 128) return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
+  return gemm_go<B2, DT, META, 4, 1, 8>(L, q, m, d, s);
+}
+
+template <int DT, int META>
+hipError_t gemm_b2(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+  switch (L.b2) {
+    case 64: return gemm_shape<64, DT, META>(L, q, m, d, s);
+    case 128: return gemm_shape<128, DT, META>(L, q, m, d, s);
+    default: return gemm_shape<256, DT, META>(L, q, m, d, s);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
                        void* y, int y_dtype, int64_t ldy, hipStream_t s) {
-  GemmParams p{};
-  p.dense = static_cast<const uint4*>(P.dense);
-  p.val = static_cast<const uint4*>(P.val);
-  p.meta = static_cast<const uint16_t*>(P.meta);
-  p.tidx = P.tidx;
-  p.x = static_cast<const uint16_t*>(x);
-  p.ldx = ldx;
-  p.y = y;
-  p.ldy = ldy;
-  p.n = L.n;
-  p.tiles_k = L.tiles_k;
-  p.n_dense = L.n_dense;
-  p.n_sparse = L.n_sparse;
-  p.b1 = L.b1;
-  p.m = m;
-  p.ydt = y_dtype;
-  p.meta_kind = L.meta;
-  const int64_t gm = (int64_t(m) + kGemmBM - 1) / kGemmBM;
-  if (gm > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(unsigned((L.n + kGemmBN - 1) / kGemmBN), unsigned(gm));
+  GemvPtrs q{static_cast<const uint4*>(P.dense), static_cast<const uint4*>(P.val),
+             static_cast<const uint16_t*>(P.meta), P.tidx, static_cast<const uint16_t*>(x), y};
+  GemmDims d{};
+  d.ldx = ldx;
+  d.ldy = ldy;
+  d.n = int32_t(L.n);
+  d.m = m;
+  d.tiles_k = int32_t(L.tiles_k);
+  d.n_dense = int32_t(L.n_dense);
+  d.n_sparse = int32_t(L.n_sparse);
+  d.b1 = L.b1;
+  d.ydt = y_dtype;
   if (L.dtype == HYB_BF16) {
-    switch (L.b2) {
-      case 64: hipLaunchKernelGGL((k_gemm<64, HYB_BF16>), grid, dim3(256), 0, s, p); break;
-      case 128: hipLaunchKernelGGL((k_gemm<128, HYB_BF16>), grid, dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL((k_gemm<256, HYB_BF16>), grid, dim3(256), 0, s, p); break;
-    }
-  } else {
-    switch (L.b2) {
-      case 64: hipLaunchKernelGGL((k_gemm<64, HYB_F16>), grid, dim3(256), 0, s, p); break;
-      case 128: hipLaunchKernelGGL((k_gemm<128, HYB_F16>), grid, dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL((k_gemm<256, HYB_F16>), grid, dim3(256), 0, s, p); break;
-    }
+    return L.meta == HYB_META_IDX2 ? gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, s)
+                                   : gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, s);
   }
-  return hipGetLastError();
+  return L.meta == HYB_META_IDX2 ? gemm_b2<HYB_F16, HYB_META_IDX2>(L, q, m, d, s)
+                                 : gemm_b2<HYB_F16, HYB_META_MASK4>(L, q, m, d, s);
 }
 
 }  // namespace hyb
