@@ -159,6 +159,15 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
                          int32_t m, int64_t ldx, void* y, int32_t y_dtype,
                          int64_t ldy, void* stream);
 
+/* Measurement aid (no part of the product computation): reads `bytes`
+ * bytes at `p` (device, 16-byte aligned) with the same non-temporal 16-byte
+ * buffer loads the decode kernel uses, `grid` workgroups of 256 threads, and
+ * writes one word per thread to `sink` (device, grid * 256 uint32).  It
+ * gives the practical HBM read rate of this device for a given size, the
+ * reference the decode kernel's rate is compared with (the spec peak is the
+ * other).  bytes in [0, 2^31), grid in [1, 65535]. */
+hyb_status hyb_stream_read(const void* p, int64_t bytes, uint32_t* sink, int32_t grid, void* stream);
+
 const char* hyb_status_str(hyb_status s); /* static string, never NULL */
 const char* hyb_last_error(void);         /* thread-local detail, "" if none */
 int32_t hyb_abi_version(void);            /* HYB_ABI_VERSION */

@@ -27,7 +27,7 @@ META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4}
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemm", "hyb_gemm_mfma",
-            "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+            "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
 
 
 class HybLayout(ctypes.Structure):
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I32, I64, P]
         f.restype = I32
+    L.hyb_stream_read.argtypes = [P, I64, P, I32, P]
+    L.hyb_stream_read.restype = I32
     L.hyb_status_str.argtypes = [I32]
     L.hyb_status_str.restype = ctypes.c_char_p
     L.hyb_last_error.argtypes = []
@@ -257,6 +259,16 @@ def gemm(P: PackedWeight, x, out_dtype=None, out=None):
 def gemm_mfma(P: PackedWeight, x, out_dtype=None, out=None):
     """Y = X W'^T on the matrix-core kernel regardless of the token count."""
     return _product("hyb_gemm_mfma", P, x, out_dtype, out)
+
+
+def stream_read(buf, nbytes: int, sink, grid: int) -> None:
+    """Measurement aid: read `nbytes` of the device tensor `buf` with the
+    decode kernel's load pattern (hyb_stream_read); `sink` holds grid*256
+    uint32/int32 entries."""
+    if sink.numel() < grid * 256:
+        raise ValueError("sink too small")
+    st = lib().hyb_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(grid), _stream(buf.device))
+    check(st, "hyb_stream_read")
 
 
 def bits_to_tensor(bits: np.ndarray, dtype: str, device):

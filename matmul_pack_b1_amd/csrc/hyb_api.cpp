@@ -248,4 +248,13 @@ hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 
+hyb_status hyb_stream_read(const void* p, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+  if (bytes < 0 || bytes >= (int64_t(1) << 31)) return fail(HYB_ERR_SHAPE, "bytes must be in [0, 2^31)");
+  if (grid < 1 || grid > 65535) return fail(HYB_ERR_INVALID_ARG, "grid must be in [1, 65535]");
+  if (!sink || !aligned(sink, 4)) return fail(HYB_ERR_INVALID_ARG, "sink is NULL or misaligned");
+  if (bytes > 0 && (!p || !aligned(p, 16))) return fail(HYB_ERR_INVALID_ARG, "p is NULL or not 16-byte aligned");
+  return hip_status(hyb::launch_stream_read(p, bytes, sink, grid, static_cast<hipStream_t>(stream)),
+                    "stream read launch");
+}
+
 }  // extern "C"

@@ -18,6 +18,7 @@ hipError_t launch_unpack(const hyb_layout& L, const hyb_packed& P, void* w, int6
                          hipStream_t s);
 hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
                        int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
+hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
                        int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
 

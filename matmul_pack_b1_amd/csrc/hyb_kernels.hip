@@ -760,7 +760,37 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
   }
 }
 
+// --------------------------------------------------------- stream read ----
+//
+// Practical read-rate reference: each wavefront reads four contiguous 1 KiB
+// chunks per trip (16 B per lane, non-temporal, like the decode kernel),
+// grid-strided over the buffer.
+__global__ __launch_bounds__(256) void k_stream_read(const char* __restrict__ p, int64_t bytes,
+                                                     uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  constexpr int64_t kSpan = 4 * 1024;
+  uint32_t acc = 0;
+  for (int64_t base = wave * kSpan; base < bytes; base += nwaves * kSpan) {
+    const int32_t n = int32_t(bytes - base < kSpan ? bytes - base : kSpan);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(p + base, n);
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, i * 1024 + lane * 16, 0, HYB_W_AUX));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  }
+  sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, s, static_cast<const char*>(p), bytes, sink);
+  return hipGetLastError();
+}
 
 // -------------------------------------------------------------- launchers -
 

@@ -186,6 +186,16 @@ def test_pack_unpack_rejects(L):
     assert L.hyb_unpack(ctypes.byref(bad), ctypes.byref(P), FAKE, 256, None) == 5
 
 
+def test_stream_read_rejects(L):
+    assert L.hyb_stream_read(FAKE, -1, FAKE, 1, None) == 2
+    assert L.hyb_stream_read(FAKE, 1 << 31, FAKE, 1, None) == 2
+    assert L.hyb_stream_read(FAKE, 1024, FAKE, 0, None) == 1
+    assert L.hyb_stream_read(FAKE, 1024, FAKE, 65536, None) == 1
+    assert L.hyb_stream_read(FAKE, 1024, None, 1, None) == 1
+    assert L.hyb_stream_read(None, 1024, FAKE, 1, None) == 1
+    assert L.hyb_stream_read(FAKE + 4, 1024, FAKE, 1, None) == 1
+
+
 def test_product_path_has_no_cpu_fallback():
     """The binding imports nothing from the oracle and raises when the
     library is absent."""

@@ -397,3 +397,18 @@ def test_all_dense_matches_torch_matmul():
     yt = x.float() @ wt.t()
     s = x.float().abs() @ wt.abs().t()
     assert torch.all((y - yt).abs() <= 4e-3 * s + 1e-6)
+
+
+def test_stream_read_reads_every_byte_once():
+    """The streaming-read reference visits every 4-byte word exactly once:
+    the XOR of its per-thread sinks equals the XOR of the buffer."""
+    torch = _torch()
+    note("stream read")
+    rng = np.random.default_rng(21)
+    words = rng.integers(0, 1 << 32, size=(3 << 18) + 100, dtype=np.uint32)   # not a multiple of 4 KiB
+    buf = torch.from_numpy(words.view(np.int32)).to(dev())
+    for grid in (1, 7, 512):
+        sink = torch.zeros(grid * 256, dtype=torch.int32, device=dev())
+        hb.stream_read(buf, words.nbytes, sink, grid)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(words)
