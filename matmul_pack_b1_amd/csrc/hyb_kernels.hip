@@ -26,6 +26,24 @@
 #ifndef HYB_GEMV_STAGES
 #define HYB_GEMV_STAGES 2
 #endif
+// The GEMM re-reads each weight slab once per token block, so its weight
+// loads keep the default cache policy (the decode kernel's are
+// non-temporal: it reads each weight once).
+#ifndef HYB_GEMM_W_NT
+#define HYB_GEMM_W_NT 0
+#endif
+#ifndef HYB_GEMM_GROUP_N
+#define HYB_GEMM_GROUP_N 4
+#endif
+#ifndef HYB_GEMM_LDS_MB
+#define HYB_GEMM_LDS_MB 8
+#endif
+#ifndef HYB_GEMM_LDS_WAVES
+#define HYB_GEMM_LDS_WAVES 4
+#endif
+#ifndef HYB_GEMM_LDS_MIN_M
+#define HYB_GEMM_LDS_MIN_M 129
+#endif
 #ifndef HYB_W_AUX
 #define HYB_W_AUX 2  // non-temporal: the weights are read once per product
 #endif
@@ -565,9 +583,9 @@ __device__ __forceinline__ void gemm_load_a(GemmAStage& st, int32_t ti, int kb,
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl) {
     st.a[sl][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-        r, sl * slab_bytes + c0 + lane * 16, 0, HYB_W_AUX));
+        r, sl * slab_bytes + c0 + lane * 16, 0, HYB_GEMM_W_NT ? HYB_W_AUX : 0));
     st.a[sl][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-        r, sl * slab_bytes + c1 + lane * 16, 0, HYB_W_AUX));
+        r, sl * slab_bytes + c1 + lane * 16, 0, HYB_GEMM_W_NT ? HYB_W_AUX : 0));
   }
   const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs0) * B2) * 2;
   const __amdgpu_buffer_rsrc_t mr = make_rsrc(mbase, (ok && !is_dense) ? 4 * 2 * B2 : 0);
@@ -760,6 +778,307 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
   }
 }
 
+// ------------------------------------------------------------ GEMM (LDS) --
+//
+// Large-M variant: four wavefronts of 64 rows each share BM = 16 * MB
+// tokens.  Every K step (64 columns) the workgroup streams its weight pieces
+// (8 x 1 KiB per wavefront: two chunks per slab, the second an empty
+// out-of-range read for a sparse slab), the slabs' metadata words and the X
+// tile (BM rows x 128 B) straight into LDS with buffer-load-to-LDS
+// instructions, STAGES - 1 steps ahead, so the pipeline depth costs no
+// registers.  The loads are issued from inline assembly: the compiler then
+// does not tie every LDS read to every DMA in flight (which would drain the
+// pipeline each step), and the waits are explicit -- every wavefront issues
+// the same number of loads per step, so "at most (STAGES-2) steps of loads
+// outstanding" followed by a workgroup barrier marks a step's LDS data
+// complete and visible.  The X tile's 16-byte slots are XOR-swizzled by
+// (row >> 1) & 7 so the B-operand reads of 16 rows hit distinct banks.
+typedef __attribute__((ext_vector_type(4))) int srd_t;
+
+__device__ __forceinline__ srd_t make_srd(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return srd_t{__builtin_amdgcn_readfirstlane(int(a & 0xFFFFFFFFu)),
+               __builtin_amdgcn_readfirstlane(int((a >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane(int(bytes)), kBufDword3};
+}
+
+// 16 bytes per lane from srd + voffset into LDS at lds + 16 * lane.
+template <bool NT>
+__device__ __forceinline__ void dma16(srd_t srd, uint32_t lds, int voffset) {
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(lds), "v"(voffset), "s"(srd) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voffset), "s"(srd) : "memory", "m0");
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  // generic -> LDS address space, then the 32-bit LDS offset
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (linear id L runs
+// on XCD L % 8), each XCD with its own L2.  The launch is a 1-D grid; XCD x
+// takes a contiguous range of a grouped order in which kGroupN consecutive
+// row blocks are swept across all token blocks before the next group, so the
+// workgroups that run together on one XCD share both their weight rows and
+// their X tiles in that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupN = HYB_GEMM_GROUP_N;
+
+__device__ __forceinline__ void xcd_grouped_block(int32_t gx, int32_t& nb, int32_t& mb) {
+  const int32_t total = int32_t(gridDim.x);  // gx row blocks x gy token blocks
+  const int32_t gy = total / gx;
+  const int32_t L = int32_t(blockIdx.x);
+  const int32_t xcd = L % kXcds, j = L / kXcds;
+  const int32_t per = total / kXcds, extra = total % kXcds;
+  const int32_t g = xcd * per + (xcd < extra ? xcd : extra) + j;
+  const int32_t gn = g / (kGroupN * gy);
+  const int32_t first = gn * kGroupN;
+  const int32_t width = gx - first < kGroupN ? gx - first : kGroupN;
+  const int32_t r = g - first * gy;
+  mb = r / width;
+  nb = first + r % width;
+}
+
+// WAVES = 4: wavefront w owns rows 64w..64w+63 and all BM tokens.
+// WAVES = 8: wavefronts w and w+4 share rows 64(w%4).. and split the tokens,
+// giving two wavefronts per SIMD so one can multiply while the other waits
+// at the barrier or on LDS.  Loads are spread so every wavefront issues the
+// same number per step.
+template <int B2, int MB, int STAGES, int WAVES>
+struct GemmLdsCfg {
+  static constexpr int kABytes = 4 * 8 * 1024;               // weight pieces of 4 row groups
+  static constexpr int kXBytes = 16 * MB * 128;               // X tile
+  static constexpr int kMetaPerGroup = B2 * 8 < 1024 ? 1024 : B2 * 8;
+  static constexpr int kMetaBytes = 4 * kMetaPerGroup;
+  static constexpr int kStage = kABytes + kXBytes + kMetaBytes;
+  // An out-of-range DMA still writes (zeros) to LDS: loads issued only to
+  // keep the per-step count constant land in this sink, which nothing reads.
+  static constexpr int kSink = 1024;
+  static constexpr int kBytes = STAGES * kStage + kSink;
+  static constexpr int kSplit = WAVES / 4;                    // wavefronts per row group
+  static constexpr int kALoads = 8 / kSplit;                  // weight chunks per wavefront
+  static constexpr int kXLoads = kXBytes / 1024 / WAVES;      // X pieces per wavefront
+  static constexpr int kMetaLoads = (kMetaPerGroup / 1024 + kSplit - 1) / kSplit;
+  static constexpr int kLoadsPerStep = kALoads + kXLoads + kMetaLoads;
+  static constexpr int kMBW = MB / kSplit;                    // token blocks per wavefront
+};
+
+template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict__ dense,
+                                                  const uint4* __restrict__ val,
+                                                  const uint16_t* __restrict__ meta,
+                                                  const int32_t* __restrict__ tidx,
+                                                  const uint16_t* __restrict__ x,
+                                                  void* __restrict__ y, GemmDims d) {
+  using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
+  static_assert(Cfg::kXLoads >= 1 && Cfg::kXLoads * WAVES * 1024 == Cfg::kXBytes, "X tile split");
+  constexpr int MBW = Cfg::kMBW;
+  constexpr int BM = 16 * MB;
+  constexpr int kStepsPerTile = B2 / 64;
+  extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % 4;            // row group
+  const int wm = wave / 4;            // token half (WAVES = 8)
+  const int q = lane >> 4;
+  int32_t nb, mbk;
+  xcd_grouped_block((d.n + 255) / 256, nb, mbk);
+  const int32_t n0 = nb * 256 + wn * 64;
+  const int32_t m0 = mbk * BM;
+  const bool rows_ok = n0 < d.n;
+  const int32_t tn = n0 / d.b1;
+  const int rs0 = (n0 - tn * d.b1) / 16;
+  const int32_t steps = d.tiles_k * kStepsPerTile;
+  const int32_t* __restrict__ trow = tidx + int64_t(tn) * d.tiles_k;
+  const int32_t mrows = d.m - m0 < BM ? d.m - m0 : BM;
+  const int64_t tile = int64_t(d.b1) * B2;
+  const uint32_t smem_base = lds_addr(smem_dyn);
+
+  constexpr int32_t kNone = INT32_MIN;
+  auto tile_index = [&](int32_t st) -> int32_t {
+    if (!rows_ok || st >= steps) return kNone;
+    const int32_t ti = trow[st / kStepsPerTile];
+    const bool ok = ti >= 0 ? (ti < d.n_dense) : (~ti < d.n_sparse);
+    return ok ? ti : kNone;
+  };
+  int32_t tis[STAGES];
+
+  // Issue every load of step `st` into stage `sg` (a compile-time index).
+  auto issue = [&](int32_t st, int sg, int32_t ti) {
+    const uint32_t stage = smem_base + sg * Cfg::kStage;
+    const int kb = st % kStepsPerTile;
+    const bool live = ti != kNone;
+    const bool is_dense = ti >= 0;
+    const int32_t slot = is_dense ? ti : ~ti;
+    const int32_t slab_bytes = is_dense ? 32 * B2 : 16 * B2;
+    const char* base = is_dense
+        ? reinterpret_cast<const char*>(dense) + (int64_t(slot) * tile + int64_t(rs0) * 16 * B2) * 2
+        : reinterpret_cast<const char*>(val) + (int64_t(slot) * (tile / 2) + int64_t(rs0) * 8 * B2) * 2;
+    const srd_t ar = make_srd(live ? base : nullptr, live ? 4 * slab_bytes : 0);
+    const int32_t c0 = is_dense ? 2 * kb * 1024 : kb * 1024;
+    const int32_t c1 = is_dense ? c0 + 1024 : 0x40000000;
+    const uint32_t adst = stage + wn * 8192;
+#pragma unroll
+    for (int i = 0; i < Cfg::kALoads; ++i) {
+      const int c = wm * Cfg::kALoads + i;   // chunk 2*sl + h of this row group
+      const int sl = c >> 1;
+      const int32_t off = (c & 1) ? c1 : c0;
+      dma16<HYB_GEMM_W_NT != 0>(ar, adst + c * 1024, sl * slab_bytes + off + lane * 16);
+    }
+    // X tile: piece j (8 rows x 128 B); wavefront w loads pieces
+    // w * kXLoads ..; lane l -> row 8j + l/8, LDS slot l%8 holding global
+    // 16-byte column (l%8) ^ ((row >> 1) & 7).
+    const srd_t xr = make_srd(x + int64_t(m0) * d.ldx, st < steps ? uint32_t(mrows * d.ldx * 2) : 0u);
+    const uint32_t xdst = stage + Cfg::kABytes;
+#pragma unroll
+    for (int i = 0; i < Cfg::kXLoads; ++i) {
+      const int j = wave * Cfg::kXLoads + i;
+      const int row = 8 * j + (lane >> 3);
+      const int c8 = (lane & 7) ^ ((row >> 1) & 7);
+      dma16<false>(xr, xdst + j * 1024, int(row * d.ldx * 2) + st * 128 + c8 * 16);
+    }
+    // metadata words of the four slabs (sparse tiles only)
+    const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs0) * B2) * 2;
+    const srd_t mr = make_srd((live && !is_dense) ? mbase : nullptr, (live && !is_dense) ? 8 * B2 : 0);
+    const uint32_t mdst = stage + Cfg::kABytes + Cfg::kXBytes + wn * Cfg::kMetaPerGroup;
+#pragma unroll
+    for (int i = 0; i < Cfg::kMetaLoads; ++i) {
+      // piece wm * kMetaLoads + i of the group's metadata (past the end: an
+      // empty out-of-range load that keeps the per-step count constant)
+      const int piece = wm * Cfg::kMetaLoads + i;
+      const bool real = piece < Cfg::kMetaPerGroup / 1024;
+      dma16<false>(mr, real ? mdst + piece * 1024 : smem_base + STAGES * Cfg::kStage,
+                   real ? piece * 1024 + lane * 16 : 0x40000000);
+    }
+    tis[sg] = ti;
+  };
+
+  f32x4_t acc[4][MBW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Every step runs on v_smfmac with the accumulators updated in place.  A
+  // sparse slab is one A operand (its stored chunk) with its index word.  A
+  // dense 64-column slab is split into two 2:4 operands: positions 0,1 of
+  // every group of four (index word 0x4444) and positions 2,3 (0xEEEE).
+  // Lane L (row L%16, lane group g) needs the 16 columns 16g..16g+15, held
+  // by lane groups 2(g%2) and 2(g%2)+1 of dense chunk g/2; of the two 16-byte
+  // reads, dwords 0 and 2 form the first operand and dwords 1 and 3 the
+  // second.  Dense steps thus issue two sparse products per slab, the same
+  // matrix-core time as two 16x16x32 MFMAs.
+  auto compute = [&](int sg, int32_t st) {
+    const int32_t ti = tis[sg];
+    if (ti == kNone) return;
+    const char* stage = smem_dyn + sg * Cfg::kStage;
+    const char* xsrc = stage + Cfg::kABytes;
+    uint4 bq[MBW][2];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+      const int row = (wm * MBW + mb) * 16 + (lane & 15);
+      const int sw = (row >> 1) & 7;
+      bq[mb][0] = *reinterpret_cast<const uint4*>(xsrc + row * 128 + ((q ^ sw) * 16));
+      bq[mb][1] = *reinterpret_cast<const uint4*>(xsrc + row * 128 + (((q + 4) ^ sw) * 16));
+    }
+    const bool is_dense = ti >= 0;
+    uint4 a0[4], a1[4];
+    uint32_t i0[4];
+    const char* wbase = stage + wn * 8192;
+    if (is_dense) {
+      const int g = q;
+      const char* src = wbase + (g >> 1) * 1024 + ((2 * (g & 1)) * 16 + (lane & 15)) * 16;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const uint4 v0 = *reinterpret_cast<const uint4*>(src + (2 * sl) * 1024);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(src + (2 * sl) * 1024 + 256);
+        a0[sl] = make_uint4(v0.x, v0.z, v1.x, v1.z);
+        a1[sl] = make_uint4(v0.y, v0.w, v1.y, v1.w);
+        i0[sl] = 0x4444u;
+      }
+    } else {
+      const char* msrc = stage + Cfg::kABytes + Cfg::kXBytes + wn * Cfg::kMetaPerGroup +
+                         lane * (B2 / 32) + (st % kStepsPerTile) * 2;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        a0[sl] = *reinterpret_cast<const uint4*>(wbase + (2 * sl) * 1024 + lane * 16);
+        a1[sl] = make_uint4(0, 0, 0, 0);
+        i0[sl] = idx2_word<META>(*reinterpret_cast<const uint16_t*>(msrc + sl * 2 * B2));
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        acc[sl][mb] = smfmac16x16x64<DT>(a0[sl], bq[mb][0], bq[mb][1], i0[sl], acc[sl][mb]);
+    if (is_dense) {
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+          acc[sl][mb] = smfmac16x16x64<DT>(a1[sl], bq[mb][0], bq[mb][1], 0xEEEEu, acc[sl][mb]);
+    }
+  };
+
+  // Prologue: steps 0 .. STAGES-2.
+#pragma unroll
+  for (int sg = 0; sg < STAGES - 1; ++sg) issue(sg, sg, tile_index(sg));
+  for (int32_t s0 = 0; s0 < steps; s0 += STAGES) {
+#pragma unroll
+    for (int sg = 0; sg < STAGES; ++sg) {
+      const int32_t st = s0 + sg;
+      // Step st's loads are complete once at most the STAGES-2 later steps'
+      // loads are outstanding; the barrier makes every wavefront's DMA
+      // writes visible and frees the stage read in the previous step.
+      wait_vmcnt<(STAGES - 2) * Cfg::kLoadsPerStep>();
+      __syncthreads();
+      constexpr int kAhead = STAGES - 1;
+      issue(st + kAhead, (sg + kAhead) % STAGES, tile_index(st + kAhead));
+      if (st < steps) compute(sg, st);
+    }
+  }
+  wait_vmcnt<0>();
+
+  if (!rows_ok) return;
+  const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int64_t m = int64_t(m0) + (wm * MBW + mb) * 16 + (lane & 15);
+    if (m >= d.m) continue;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int64_t n = int64_t(n0) + sl * 16 + q * 4;
+      const f32x4_t v = acc[sl][mb];
+      const int64_t base = m * d.ldy + n;
+      if (d.ydt == HYB_F32) {
+        float* dst = static_cast<float*>(y) + base;
+        if (vec_ok) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = v[e];
+        }
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(y) + base;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------- stream read ----
 //
 // Practical read-rate reference: each wavefront reads four contiguous 1 KiB
@@ -920,11 +1239,28 @@ hipError_t gemm_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims
 // Workgroup shape by token count: few tokens -> the four wavefronts split
 // K (more workgroups, weights streamed once); many tokens -> they split n
 // and share each X tile.
+template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
+hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+  using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
+  static_assert(Cfg::kBytes <= 160 * 1024, "LDS budget");
+  const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
+  const int64_t gn = (L.n + 255) / 256;
+  if (gn * gm >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+  // 1-D launch of gn * gm workgroups, mapped to (row block, token block)
+  // inside the kernel.
+  hipLaunchKernelGGL((k_gemm_lds<B2, DT, META, MB, STAGES, WAVES>), dim3(unsigned(gn * gm)), dim3(64 * WAVES),
+                     size_t(Cfg::kBytes), s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+  return hipGetLastError();
+}
+
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   if (m <= 64) return gemm_go<B2, DT, META, 1, 4, 4>(L, q, m, d, s);
-  if (m <= 128) return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
-  return gemm_go<B2, DT, META, 4, 1, 8>(L, q, m, d, s);
+  if (m <= HYB_GEMM_LDS_MIN_M - 1) return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
+  constexpr int kMB = HYB_GEMM_LDS_MB;
+  constexpr int kW = HYB_GEMM_LDS_WAVES;
+  constexpr int kStages = GemmLdsCfg<B2, kMB, 3, kW>::kBytes <= 160 * 1024 ? 3 : 2;
+  return gemm_lds_go<B2, DT, META, kMB, kStages, kW>(L, q, m, d, s);
 }
 
 template <int DT, int META>
