@@ -35,15 +35,6 @@
 #ifndef HYB_GEMM_GROUP_N
 #define HYB_GEMM_GROUP_N 4
 #endif
-#ifndef HYB_GEMM_LDS_MB
-#define HYB_GEMM_LDS_MB 8
-#endif
-#ifndef HYB_GEMM_LDS_WAVES
-#define HYB_GEMM_LDS_WAVES 4
-#endif
-#ifndef HYB_GEMM_LDS_MIN_M
-#define HYB_GEMM_LDS_MIN_M 129
-#endif
 #ifndef HYB_W_AUX
 #define HYB_W_AUX 2  // non-temporal: the weights are read once per product
 #endif
@@ -58,6 +49,8 @@ typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
 typedef __attribute__((ext_vector_type(16))) __bf16 bf16x16_t;
 typedef __attribute__((ext_vector_type(16))) _Float16 half16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;  // an LDS-resident vector
 
 // ------------------------------------------------------------- helpers ----
 
@@ -814,6 +807,8 @@ __device__ __forceinline__ void dma16(srd_t srd, uint32_t lds, int voffset) {
   }
 }
 
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -980,11 +975,42 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
   // reads, dwords 0 and 2 form the first operand and dwords 1 and 3 the
   // second.  Dense steps thus issue two sparse products per slab, the same
   // matrix-core time as two 16x16x32 MFMAs.
+  //
+  // Both kinds share the first pass (one product per slab and token block)
+  // and its accumulator registers; dense steps add the second pass.  Every
+  // LDS read is a whole 16-byte read (the 64 lanes of a read cover 1 KiB
+  // without bank conflicts); the weight reads are volatile so the compiler
+  // cannot split one into dword reads of the shuffled halves (lanes 16 bytes
+  // apart reading single dwords conflict four ways).  A sparse step reads its chunk twice (the second read feeds
+  // nothing) so that both kinds run the same instructions up to the second
+  // pass.
   auto compute = [&](int sg, int32_t st) {
     const int32_t ti = tis[sg];
     if (ti == kNone) return;
     const char* stage = smem_dyn + sg * Cfg::kStage;
     const char* xsrc = stage + Cfg::kABytes;
+    const bool is_dense = ti >= 0;
+    const char* wbase = stage + wn * 8192;
+    const int r_off = is_dense ? (q >> 1) * 1024 + ((2 * (q & 1)) * 16 + (lane & 15)) * 16 : lane * 16;
+    const int r_off2 = is_dense ? r_off + 256 : r_off;
+    const char* msrc = stage + Cfg::kABytes + Cfg::kXBytes + wn * Cfg::kMetaPerGroup +
+                       lane * (B2 / 32) + (st % kStepsPerTile) * 2;
+    // all-ones for a dense step; opaque to the optimiser so the selects
+    // below stay bit-selects instead of becoming branches (each branch would
+    // wait for its slab's reads on its own)
+    uint32_t dm = is_dense ? ~0u : 0u;
+    asm("" : "+v"(dm));
+    uint4 a0[4], a1[4];
+    uint32_t i0[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const u32x4_t v0 = *(const volatile lds_u32x4_t*)(wbase + (2 * sl) * 1024 + r_off);
+      const u32x4_t v1 = *(const volatile lds_u32x4_t*)(wbase + (2 * sl) * 1024 + r_off2);
+      const uint32_t m = *reinterpret_cast<const uint16_t*>(msrc + sl * 2 * B2);
+      a0[sl] = make_uint4(v0[0], bitsel(dm, v0[2], v0[1]), bitsel(dm, v1[0], v0[2]), bitsel(dm, v1[2], v0[3]));
+      a1[sl] = make_uint4(v0[1], v0[3], v1[1], v1[3]);
+      i0[sl] = bitsel(dm, 0x4444u, idx2_word<META>(m));
+    }
     uint4 bq[MBW][2];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
@@ -992,31 +1018,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
       const int sw = (row >> 1) & 7;
       bq[mb][0] = *reinterpret_cast<const uint4*>(xsrc + row * 128 + ((q ^ sw) * 16));
       bq[mb][1] = *reinterpret_cast<const uint4*>(xsrc + row * 128 + (((q + 4) ^ sw) * 16));
-    }
-    const bool is_dense = ti >= 0;
-    uint4 a0[4], a1[4];
-    uint32_t i0[4];
-    const char* wbase = stage + wn * 8192;
-    if (is_dense) {
-      const int g = q;
-      const char* src = wbase + (g >> 1) * 1024 + ((2 * (g & 1)) * 16 + (lane & 15)) * 16;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const uint4 v0 = *reinterpret_cast<const uint4*>(src + (2 * sl) * 1024);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(src + (2 * sl) * 1024 + 256);
-        a0[sl] = make_uint4(v0.x, v0.z, v1.x, v1.z);
-        a1[sl] = make_uint4(v0.y, v0.w, v1.y, v1.w);
-        i0[sl] = 0x4444u;
-      }
-    } else {
-      const char* msrc = stage + Cfg::kABytes + Cfg::kXBytes + wn * Cfg::kMetaPerGroup +
-                         lane * (B2 / 32) + (st % kStepsPerTile) * 2;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        a0[sl] = *reinterpret_cast<const uint4*>(wbase + (2 * sl) * 1024 + lane * 16);
-        a1[sl] = make_uint4(0, 0, 0, 0);
-        i0[sl] = idx2_word<META>(*reinterpret_cast<const uint16_t*>(msrc + sl * 2 * B2));
-      }
     }
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb)
@@ -1236,9 +1237,6 @@ hipError_t gemm_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims
   return hipGetLastError();
 }
 
-// Workgroup shape by token count: few tokens -> the four wavefronts split
-// K (more workgroups, weights streamed once); many tokens -> they split n
-// and share each X tile.
 template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
 hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
@@ -1253,14 +1251,46 @@ hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const Gemm
   return hipGetLastError();
 }
 
+// Three LDS stages where they fit, else two.
+template <int B2, int MB, int WAVES>
+constexpr int lds_stages() {
+  return GemmLdsCfg<B2, MB, 3, WAVES>::kBytes <= 160 * 1024 ? 3 : 2;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Workgroup shape by token count.  Up to 128 tokens the register-fed kernel
+// runs (few tokens: the four wavefronts split K; more: they split n).  From
+// 129 tokens one of three LDS-fed shapes runs, 256 weight rows by BM = 256,
+// 128 or 64 tokens.  Every workgroup walks all of K, so the time is the
+// number of rounds of workgroups over the compute units times the time of
+// one workgroup; the relative step costs of the three shapes are measured
+// (a 256-token step costs 1, a 128-token step 0.64, a 64-token step 0.57),
+// and the shape with the smallest product runs.
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   if (m <= 64) return gemm_go<B2, DT, META, 1, 4, 4>(L, q, m, d, s);
-  if (m <= HYB_GEMM_LDS_MIN_M - 1) return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
-  constexpr int kMB = HYB_GEMM_LDS_MB;
-  constexpr int kW = HYB_GEMM_LDS_WAVES;
-  constexpr int kStages = GemmLdsCfg<B2, kMB, 3, kW>::kBytes <= 160 * 1024 ? 3 : 2;
-  return gemm_lds_go<B2, DT, META, kMB, kStages, kW>(L, q, m, d, s);
+  if (m <= 128) return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
+  const int64_t gn = (L.n + 255) / 256;
+  const int64_t cus = device_cus();
+  auto cost = [&](int64_t bm, double step) {
+    return double((gn * ((m + bm - 1) / bm) + cus - 1) / cus) * step;
+  };
+  const double c256 = cost(256, 1.0), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
+  if (c256 <= c128 && c256 <= c64) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8>(), 8>(L, q, m, d, s);
+  if (c128 <= c64) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8>(), 8>(L, q, m, d, s);
+  return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4>(), 4>(L, q, m, d, s);
 }
 
 template <int DT, int META>

@@ -227,6 +227,24 @@ def test_gemm_qwen14b_sampled(m):
     assert_close(y2[:, rows], yref, s, what=f"gemm_mfma m={m}")
 
 
+@pytest.mark.parametrize("m", [200, 256, 300, 512, 1024])
+def test_gemm_8b_up_shapes_sampled(m):
+    """14336x4096, 128x128 tiles, 70% sparse tiles.  From 129 tokens the
+    launcher picks one of three workgroup shapes (256, 128 or 64 tokens per
+    workgroup) by the number of workgroup rounds on the device; on a
+    256-CU device these token counts select the 64-token shape (200 with a
+    ragged last block, 256), the 128-token shape (300 ragged, 512) and the
+    256-token shape (1024)."""
+    torch = _torch()
+    mat, w, tmap = workload_matrix(2, 0)
+    note(f"gemm 8b up m={m}")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 4, m), x)
+    y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
+    assert_close(y[:, rows], yref, s, what=f"gemm m={m}")
+
+
 def test_gemm_output_16bit():
     torch = _torch()
     note("gemm fp16 output")
