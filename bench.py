@@ -20,6 +20,11 @@ reports (an event pair per launch adds the event packets' own latency).  Packed 
 kind (stepping by 3 copies) so the 256 MB last-level cache holds nothing
 from the previous use of a copy.
 
+After the timed steps, the prefill GEMM is measured on its own workload
+(Qwen3-14B-shaped 17408 x 5120, 64 x 64 tiles, M = 2048): hybrid, the same
+kernel all-dense, and the vendor BLAS dense product, with the matrix-core
+roofline (JSON key "prefill").
+
 Prints one JSON line.  `python bench.py --sweep` also measures the other
 workloads (stderr table plus --sweep-json file).
 """
@@ -141,6 +146,8 @@ def main():
     ap.add_argument("--meta", default="idx2", choices=["idx2", "mask4"])
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--gemm-m", type=int, default=64)
+    ap.add_argument("--prefill-m", type=int, default=2048,
+                    help="token count of the prefill GEMM measurement (0: skip)")
     ap.add_argument("--only", default="", help="comma list of rows to run (pack,gemv,dense,unpack,gemm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -381,12 +388,84 @@ def main():
     if stream_ref is not None and out.get("value"):
         stream_ref["gemv_frac_of_stream"] = round(out["value"] / stream_ref["GBps"], 4)
         out["stream_reference"] = stream_ref
+    if args.prefill_m > 0:
+        log(f"[bench] prefill GEMM M={args.prefill_m}")
+        out["prefill"] = prefill(hb, torch, wl, dev, args.prefill_m, args.meta)
+        log(f"[bench] prefill: {out['prefill']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(mat, w_bits, tmap, x_bits, L)
     if args.sweep:
         out["sweep_file"] = sweep(hb, torch, wl, dev, rotate, args)
     print(json.dumps(out), flush=True)
+
+
+def graph_us(torch, launch, count, reps=5):
+    """Per-launch time of `count` launches captured in one HIP graph and
+    replayed between one event pair (median of `reps` replays)."""
+    launch(count)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        g.capture_begin()
+        launch(count)
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        g.replay()
+        e_.record()
+        torch.cuda.synchronize()
+        times.append(1e3 * s_.elapsed_time(e_) / count)
+    del g
+    return statistics.median(times)
+
+
+def prefill(hb, torch, wl, dev, m, meta):
+    """Prefill product at the Qwen3-14B-shaped gate/up projection (17408 x
+    5120, 64 x 64 tiles, 60% of the tiles 2:4): the hybrid matrix-core GEMM,
+    the same kernel on the all-dense map, and torch's bf16 matmul (the
+    vendor BLAS) on the dense weights as the library reference."""
+    mat = wl.workload(5).matrices[0]
+    tmap = mat.tile_map()
+    w = hb.bits_to_tensor(mat.weight_bits(), mat.dtype, dev)
+    x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
+    y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+    hyb = [hb.pack(w, tmap, mat.b1, mat.b2, meta) for _ in range(2)]
+    den = [hb.pack(w, np.zeros_like(tmap), mat.b1, mat.b2, meta) for _ in range(2)]
+    torch.cuda.synchronize()
+    L, Ld = hyb[0].layout, den[0].layout
+    n_launch = 8
+    us_h = graph_us(torch, lambda c: [hb.gemm(hyb[i % 2], x, out=y) for i in range(c)], n_launch)
+    us_d = graph_us(torch, lambda c: [hb.gemm(den[i % 2], x, out=y) for i in range(c)], n_launch)
+    # vendor dense reference: bf16 X @ W^T with an fp32-accumulating bf16 output
+    wt = [w, w.clone()]
+    yb = torch.empty((m, mat.n), dtype=w.dtype, device=dev)
+    us_v = graph_us(torch, lambda c: [torch.matmul(x, wt[i % 2].t(), out=yb) for i in range(c)], n_launch)
+    fl = alg_flops(L, m)
+    fl_dense = 2 * m * mat.n * mat.k
+    tf = fl / (us_h * 1e-6) / 1e12
+    out = {"workload": f"Qwen3-14B gate/up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles, "
+                       f"{L.n_sparse}/{L.tiles_n * L.tiles_k} tiles 2:4 ({meta}), prefill M={m}",
+           "m": m, "hybrid_us": round(us_h, 2), "dense_same_kernel_us": round(us_d, 2),
+           "vendor_blas_dense_us": round(us_v, 2), "alg_flops": fl, "dense_flops": fl_dense,
+           "TFLOPs": round(tf, 1), "dense_same_kernel_TFLOPs": round(fl_dense / (us_d * 1e-6) / 1e12, 1),
+           "vendor_blas_TFLOPs": round(fl_dense / (us_v * 1e-6) / 1e12, 1),
+           "speedup_vs_dense_same_kernel": round(us_d / us_h, 4),
+           "speedup_vs_vendor_blas": round(us_v / us_h, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_BF16_TFLOPS, 4),
+                        "kernel": "k_gemm_lds (256x256 tile, 8 wavefronts)"},
+           "timing": f"graph burst of {n_launch} launches over 2 rotating copies, median of 5 replays"}
+    del hyb, den, wt, w, x, y, yb
+    torch.cuda.empty_cache()
+    return out
 
 
 def sweep(hb, torch, wl, dev, rotate, args):
