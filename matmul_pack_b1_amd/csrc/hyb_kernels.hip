@@ -773,9 +773,11 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
 
 // ------------------------------------------------------------ GEMM (LDS) --
 //
-// Large-M variant: four wavefronts of 64 rows each share BM = 16 * MB
+// Large-M variant: a workgroup covers 256 weight rows (four 64-row groups)
+// and BM = 16 * MB tokens.  With four wavefronts each owns a row group and
+// all BM tokens; with eight, two wavefronts share a row group and split the
 // tokens.  Every K step (64 columns) the workgroup streams its weight pieces
-// (8 x 1 KiB per wavefront: two chunks per slab, the second an empty
+// (8 x 1 KiB per row group: two chunks per slab, the second an empty
 // out-of-range read for a sparse slab), the slabs' metadata words and the X
 // tile (BM rows x 128 B) straight into LDS with buffer-load-to-LDS
 // instructions, STAGES - 1 steps ahead, so the pipeline depth costs no
