@@ -20,7 +20,9 @@ reports (an event pair per launch adds the event packets' own latency).  Packed 
 kind (stepping by 3 copies) so the 256 MB last-level cache holds nothing
 from the previous use of a copy.
 
-After the timed steps, the prefill GEMM is measured on its own workload
+After the timed steps, the grouped decode launch is compared with separate
+launches on one decoder layer (JSON key "grouped"), and the prefill GEMM is
+measured on its own workload
 (Qwen3-14B-shaped 17408 x 5120, 64 x 64 tiles, M = 2048): hybrid, the same
 kernel all-dense, and the vendor BLAS dense product, with the matrix-core
 roofline (JSON key "prefill").
@@ -150,6 +152,7 @@ def main():
                     help="token count of the prefill GEMM measurement (0: skip)")
     ap.add_argument("--only", default="", help="comma list of rows to run (pack,gemv,dense,unpack,gemm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-launch measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 128 MiB device copies (torch copy kernel) as a counter reference")
     ap.add_argument("--sweep", action="store_true")
@@ -388,6 +391,10 @@ def main():
     if stream_ref is not None and out.get("value"):
         stream_ref["gemv_frac_of_stream"] = round(out["value"] / stream_ref["GBps"], 4)
         out["stream_reference"] = stream_ref
+    if not args.no_grouped:
+        log("[bench] grouped decode launch on one decoder layer")
+        out["grouped"] = grouped(hb, torch, wl, dev, args.meta)
+        log(f"[bench] grouped: {out['grouped']}")
     if args.prefill_m > 0:
         log(f"[bench] prefill GEMM M={args.prefill_m}")
         out["prefill"] = prefill(hb, torch, wl, dev, args.prefill_m, args.meta)
@@ -464,6 +471,60 @@ def prefill(hb, torch, wl, dev, m, meta):
                         "kernel": "k_gemm_lds (256x256 tile, 8 wavefronts)"},
            "timing": f"graph burst of {n_launch} launches over 2 rotating copies, median of 5 replays"}
     del hyb, den, wt, w, x, y, yb
+    torch.cuda.empty_cache()
+    return out
+
+
+def grouped(hb, torch, wl, dev, meta):
+    """Grouped decode launch (hyb_gemv_grouped) against separate launches on
+    one Llama-3.1-8B decoder layer at M = 1: q, k, v (one x) and gate, up
+    (another), each matrix with its own tile map and fraction.  Weights
+    rotate over enough copies to leave the last-level cache cold."""
+    W = wl.workload(3)
+    groups = [[mt for mt in W.matrices if mt.name in names] for names in (("q", "k", "v"), ("gate", "up"))]
+    mats = [mt for g in groups for mt in g]
+    per_copy = 0
+    packed = {}
+    for mt in mats:
+        w = hb.bits_to_tensor(mt.weight_bits(), mt.dtype, dev)
+        packed[mt.name] = [hb.pack(w, mt.tile_map(), mt.b1, mt.b2, meta)]
+        per_copy += packed[mt.name][0].weight_bytes()
+        del w
+    n_copies = copies_for(per_copy, 1 << 30)
+    for mt in mats:
+        w = hb.bits_to_tensor(mt.weight_bits(), mt.dtype, dev)
+        packed[mt.name] += [hb.pack(w, mt.tile_map(), mt.b1, mt.b2, meta) for _ in range(n_copies - 1)]
+        del w
+    torch.cuda.synchronize()
+    x = hb.bits_to_tensor(mats[0].activation_bits(1), "bf16", dev)
+    outs = {mt.name: torch.empty((1, mt.n), dtype=torch.float32, device=dev) for mt in mats}
+
+    def separate(count):
+        for i in range(count):
+            c = (3 * i) % n_copies
+            for mt in mats:
+                hb.gemv(packed[mt.name][c], x, out=outs[mt.name])
+
+    def together(count):
+        for i in range(count):
+            c = (3 * i) % n_copies
+            for g in groups:
+                hb.gemv_grouped([packed[mt.name][c] for mt in g], x, outs=[outs[mt.name] for mt in g])
+
+    reps = 2 * n_copies
+    us_sep = graph_us(torch, separate, reps)
+    us_grp = graph_us(torch, together, reps)
+    alg = sum(alg_bytes(packed[mt.name][0].layout, 1) for mt in mats)
+    out = {"workload": "Llama-3.1-8B decoder layer q, k, v (one x) and gate, up (another), "
+                       "per-matrix tile fractions, M=1",
+           "matrices": {mt.name: [mt.n, mt.k, int(packed[mt.name][0].layout.n_sparse)] for mt in mats},
+           "launches": {"separate": len(mats), "grouped": len(groups)},
+           "separate_us": round(us_sep, 3), "grouped_us": round(us_grp, 3),
+           "speedup": round(us_sep / us_grp, 4), "alg_bytes": alg,
+           "GBps_separate": round(alg / (us_sep * 1e-6) / 1e9, 1),
+           "GBps_grouped": round(alg / (us_grp * 1e-6) / 1e9, 1),
+           "timing": f"graph burst of {reps} layer passes over {n_copies} rotating copies, median of 5 replays"}
+    del packed, outs
     torch.cuda.empty_cache()
     return out
 

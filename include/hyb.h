@@ -78,6 +78,7 @@ enum { HYB_META_IDX2 = 1, HYB_META_MASK4 = 2 };      /* metadata codes */
 #define HYB_MAGIC 0x31425948u /* "HYB1" little-endian */
 #define HYB_VERSION 1u
 #define HYB_ABI_VERSION 1
+#define HYB_MAX_GROUP 16 /* matrices per hyb_gemv_grouped call */
 
 /* Plain-old-data description of one packed matrix; filled by hyb_plan and
  * also usable as a serialised header (all fields fixed-width). */
@@ -144,6 +145,26 @@ hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_o
 hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x,
                     int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                     void* stream);
+
+/* Grouped decode product: one launch multiplies the same x (0 <= m <= 16
+ * tokens) by `count` packed matrices, Y_g[i, :] = W'_g X[i, :].  A layer's
+ * projections that read the same activations (q, k and v; gate and up) carry
+ * their own tile maps and sparsities (PATCH, gist.science, section 3
+ * "Contributi Chiave": attention stays denser, MLP matrices sparser), and the
+ * smaller ones are too short to fill the GPU alone.
+ *   count     0 <= count <= HYB_MAX_GROUP (0: no-op)
+ *   layouts   host array of count layouts; every matrix must have the same k,
+ *             b2, dtype and metadata kind (b1 and n may differ)
+ *   w         host array of count stream descriptors
+ *   x, m, ldx as for hyb_gemv (shared by all matrices)
+ *   y         host array of count device pointers, matrix g's output m x n_g
+ *   y_dtype   one output type for all (HYB_F32 or the weight dtype)
+ *   ldy       host array of count row strides (ldy[g] >= n_g)
+ * Every per-matrix check of hyb_gemv applies; outputs must not overlap each
+ * other or the inputs.  Results are bitwise those of count hyb_gemv calls. */
+hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_packed* w,
+                            const void* x, int32_t m, int64_t ldx, void* const* y,
+                            int32_t y_dtype, const int64_t* ldy, void* stream);
 
 /* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same

@@ -26,8 +26,9 @@ MAX_GEMV_M = 16
 META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4}
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
-EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemm", "hyb_gemm_mfma",
+EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_gemm", "hyb_gemm_mfma",
             "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+MAX_GROUP = 16
 
 
 class HybLayout(ctypes.Structure):
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I32, I64, P]
         f.restype = I32
+    L.hyb_gemv_grouped.argtypes = [I32, ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64,
+                                   ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I64), P]
+    L.hyb_gemv_grouped.restype = I32
     L.hyb_stream_read.argtypes = [P, I64, P, I32, P]
     L.hyb_stream_read.restype = I32
     L.hyb_status_str.argtypes = [I32]
@@ -249,6 +253,36 @@ def _product(fn_name: str, P: PackedWeight, x, out_dtype=None, out=None):
 def gemv(P: PackedWeight, x, out_dtype=None, out=None):
     """Decode product Y = X W'^T for 1..16 tokens (rows of x)."""
     return _product("hyb_gemv", P, x, out_dtype, out)
+
+
+def gemv_grouped(Ps, x, out_dtype=None, outs=None):
+    """Decode products of the same x with several packed matrices (same k,
+    b2, dtype and metadata kind) in one launch; returns one output per
+    matrix."""
+    torch = _torch()
+    Ps = list(Ps)
+    _check_rows(x, "x")
+    m = x.shape[0]
+    count = len(Ps)
+    codes = {_out_code(P, out_dtype) for P in Ps} or {HYB_F32}
+    if len(codes) != 1:
+        raise TypeError("all matrices must share one output type")
+    code = codes.pop()
+    tdt = {HYB_F32: torch.float32, HYB_BF16: torch.bfloat16, HYB_F16: torch.float16}[code]
+    if outs is None:
+        outs = [torch.empty((m, P.shape[0]), dtype=tdt, device=x.device) for P in Ps]
+    if len(outs) != count:
+        raise ValueError("one output per matrix")
+    layouts = (HybLayout * max(count, 1))(*[P.layout for P in Ps])
+    packed = (HybPacked * max(count, 1))(*[P.packed_struct() for P in Ps])
+    ys = (ctypes.c_void_p * max(count, 1))(*[_ptr(o) for o in outs])
+    ldys = (ctypes.c_int64 * max(count, 1))(*[int(o.stride(0)) if o.numel() else int(P.shape[0])
+                                               for o, P in zip(outs, Ps)])
+    k = Ps[0].shape[1] if Ps else x.shape[1]
+    st = lib().hyb_gemv_grouped(count, layouts, packed, _ptr(x), int(m),
+                                int(x.stride(0)) if x.numel() else int(k), ys, code, ldys, _stream(x.device))
+    check(st, "hyb_gemv_grouped")
+    return outs
 
 
 def gemm(P: PackedWeight, x, out_dtype=None, out=None):

@@ -228,6 +228,35 @@ hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x
                     "gemv launch");
 }
 
+hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_packed* w, const void* x,
+                            int32_t m, int64_t ldx, void* const* y, int32_t y_dtype, const int64_t* ldy,
+                            void* stream) {
+  if (count < 0 || count > hyb::kMaxGroup)
+    return fail(HYB_ERR_SHAPE, "count = %d outside [0, %d]", count, hyb::kMaxGroup);
+  if (count == 0) return ok();
+  if (!layouts || !w || !y || !ldy) return fail(HYB_ERR_INVALID_ARG, "layouts, w, y or ldy is NULL");
+  int64_t slabs = 0;
+  for (int32_t g = 0; g < count; ++g) {
+    hyb_status st = check_product(&layouts[g], &w[g], x, m, ldx, y[g], y_dtype, ldy[g], hyb::kMaxGemvM);
+    if (st != HYB_OK) {
+      const std::string detail = g_last_error;
+      return fail(st, "matrix %d: %s", g, detail.c_str());
+    }
+    const hyb_layout& L = layouts[g];
+    const hyb_layout& L0 = layouts[0];
+    if (L.k != L0.k || L.b2 != L0.b2 || L.dtype != L0.dtype || L.meta != L0.meta)
+      return fail(HYB_ERR_INVALID_ARG, "matrix %d differs from matrix 0 in k, b2, dtype or metadata kind", g);
+    slabs += L.n / 16;
+  }
+  if (m == 0 || slabs == 0) return ok();
+  if (slabs >= (int64_t(1) << 31)) return fail(HYB_ERR_UNSUPPORTED, "too many rows for one launch");
+  if (int64_t(m) * ldx * 2 >= (int64_t(1) << 31))
+    return fail(HYB_ERR_UNSUPPORTED, "decode kernel needs m * ldx * 2 < 2^31 bytes of x");
+  return hip_status(hyb::launch_gemv_grouped(count, layouts, w, x, m, ldx, y, y_dtype, ldy,
+                                             static_cast<hipStream_t>(stream)),
+                    "grouped gemv launch");
+}
+
 hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                          int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);

@@ -11,6 +11,8 @@ namespace hyb {
 
 // Decode kernel handles up to this many tokens per launch.
 constexpr int kMaxGemvM = 16;
+// Matrices per grouped decode launch (HYB_MAX_GROUP in hyb.h).
+constexpr int kMaxGroup = HYB_MAX_GROUP;
 
 hipError_t launch_pack(const hyb_layout& L, const void* w, int64_t ldw, const hyb_packed& P,
                        hipStream_t s);
@@ -18,6 +20,9 @@ hipError_t launch_unpack(const hyb_layout& L, const hyb_packed& P, void* w, int6
                          hipStream_t s);
 hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
                        int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
+// All matrices share k, b2, dtype and metadata kind (checked by the caller).
+hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
+                               int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s);
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
                        int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);

@@ -416,19 +416,17 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2>& st, int32_
   }
 }
 
+// The product of one 16-row slab (the whole work of one workgroup).
 template <int MT, int B2, int DT, int META, int WAVES, int STAGES>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ dense,
-                                                     const uint4* __restrict__ val,
-                                                     const uint16_t* __restrict__ meta,
-                                                     const int32_t* __restrict__ tidx,
-                                                     const uint16_t* __restrict__ x,
-                                                     void* __restrict__ y, GemvDims d) {
+__device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const uint4* __restrict__ val,
+                                          const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
+                                          const uint16_t* __restrict__ x, void* __restrict__ y,
+                                          const GemvDims& d, int64_t slab) {
   __shared__ __attribute__((aligned(16))) uint16_t xs_all[WAVES][MT * B2];
   __shared__ float red[WAVES][MT][16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t slab = blockIdx.x;
   const int slabs_per_tile = d.b1 / 16;
   const int64_t tn = slab / slabs_per_tile;
   const int rs = int(slab - tn * slabs_per_tile);
@@ -492,6 +490,48 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ d
       store_out(y, d.ydt, int64_t(m) * d.ldy + slab * 16 + r, v);
     }
   }
+}
+
+template <int MT, int B2, int DT, int META, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ dense,
+                                                     const uint4* __restrict__ val,
+                                                     const uint16_t* __restrict__ meta,
+                                                     const int32_t* __restrict__ tidx,
+                                                     const uint16_t* __restrict__ x,
+                                                     void* __restrict__ y, GemvDims d) {
+  gemv_slab<MT, B2, DT, META, WAVES, STAGES>(dense, val, meta, tidx, x, y, d, blockIdx.x);
+}
+
+// Grouped decode product: one launch multiplies the same x by up to
+// kMaxGroup matrices (for instance the q, k and v projections of a layer,
+// each with its own tile map and sparsity).  Matrix g owns workgroups
+// slab_start[g] .. slab_start[g+1]-1, one per 16-row slab as above, so every
+// slab runs exactly the single-matrix code and the results are bitwise those
+// of separate launches.
+struct GemvGroup {
+  const uint4* dense[kMaxGroup];
+  const uint4* val[kMaxGroup];
+  const uint16_t* meta[kMaxGroup];
+  const int32_t* tidx[kMaxGroup];
+  void* y[kMaxGroup];
+  int64_t ldy[kMaxGroup];
+  int32_t n_dense[kMaxGroup], n_sparse[kMaxGroup], b1[kMaxGroup];
+  int32_t slab_start[kMaxGroup + 1];
+  int32_t count;
+};
+
+template <int MT, int B2, int DT, int META, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_grouped(const uint16_t* __restrict__ x, GemvDims d,
+                                                             GemvGroup g) {
+  const int32_t b = blockIdx.x;
+  int gi = 0;
+  for (int i = 1; i < g.count; ++i) gi = b >= g.slab_start[i] ? i : gi;
+  d.ldy = g.ldy[gi];
+  d.n_dense = g.n_dense[gi];
+  d.n_sparse = g.n_sparse[gi];
+  d.b1 = g.b1[gi];
+  gemv_slab<MT, B2, DT, META, WAVES, STAGES>(g.dense[gi], g.val[gi], g.meta[gi], g.tidx[gi], x, g.y[gi], d,
+                                              b - g.slab_start[gi]);
 }
 
 // ---------------------------------------------------------------- GEMM ----
@@ -1223,6 +1263,73 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
   } else {
     if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2>(m, L.b2, grid, s, q, d);
     else gemv_mt<HYB_F16, HYB_META_MASK4>(m, L.b2, grid, s, q, d);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+
+template <int MT, int DT, int META>
+void gemv_grouped_b2(int b2, dim3 grid, hipStream_t s, const uint16_t* x, const GemvDims& d, const GemvGroup& g) {
+  const dim3 block(64 * kGemvWaves);
+  switch (b2) {
+    case 64:
+      hipLaunchKernelGGL((k_gemv_grouped<MT, 64, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, x, d, g);
+      break;
+    case 128:
+      hipLaunchKernelGGL((k_gemv_grouped<MT, 128, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, x, d, g);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemv_grouped<MT, 256, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, x, d, g);
+      break;
+  }
+}
+
+template <int DT, int META>
+void gemv_grouped_mt(int m, int b2, dim3 grid, hipStream_t s, const uint16_t* x, const GemvDims& d,
+                     const GemvGroup& g) {
+  if (m <= 1) gemv_grouped_b2<1, DT, META>(b2, grid, s, x, d, g);
+  else if (m <= 2) gemv_grouped_b2<2, DT, META>(b2, grid, s, x, d, g);
+  else if (m <= 4) gemv_grouped_b2<4, DT, META>(b2, grid, s, x, d, g);
+  else if (m <= 8) gemv_grouped_b2<8, DT, META>(b2, grid, s, x, d, g);
+  else gemv_grouped_b2<16, DT, META>(b2, grid, s, x, d, g);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
+                               int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s) {
+  GemvGroup g{};
+  g.count = count;
+  int64_t slabs = 0;
+  for (int i = 0; i < count; ++i) {
+    g.dense[i] = static_cast<const uint4*>(P[i].dense);
+    g.val[i] = static_cast<const uint4*>(P[i].val);
+    g.meta[i] = static_cast<const uint16_t*>(P[i].meta);
+    g.tidx[i] = P[i].tidx;
+    g.y[i] = y[i];
+    g.ldy[i] = ldy[i];
+    g.n_dense[i] = int32_t(L[i].n_dense);
+    g.n_sparse[i] = int32_t(L[i].n_sparse);
+    g.b1[i] = L[i].b1;
+    g.slab_start[i] = int32_t(slabs);
+    slabs += L[i].n / 16;
+  }
+  g.slab_start[count] = int32_t(slabs);
+  if (slabs == 0) return hipSuccess;
+  GemvDims d{};
+  d.ldx = ldx;
+  d.tiles_k = int32_t(L[0].tiles_k);
+  d.m = m;
+  d.ydt = y_dtype;
+  const dim3 grid(static_cast<unsigned>(slabs));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (L[0].dtype == HYB_BF16) {
+    if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_BF16, HYB_META_IDX2>(m, L[0].b2, grid, s, xp, d, g);
+    else gemv_grouped_mt<HYB_BF16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
+  } else {
+    if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_F16, HYB_META_IDX2>(m, L[0].b2, grid, s, xp, d, g);
+    else gemv_grouped_mt<HYB_F16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
   }
   return hipGetLastError();
 }

@@ -157,6 +157,37 @@ def test_product_rejects(L, fn):
     assert hb.last_error()
 
 
+def _grouped(L, count, lays, packs=None, x=FAKE, m=1, ldx=256, ys=None, ydt=3, ldys=None):
+    n = max(count, 1)
+    la = (hb.HybLayout * n)(*lays) if lays is not None else None
+    pk = (hb.HybPacked * n)(*(packs or [hb.HybPacked(FAKE, FAKE, FAKE, FAKE)] * len(lays or []))) \
+        if lays is not None else None
+    ya = (ctypes.c_void_p * n)(*(ys or [FAKE] * n))
+    la_y = (ctypes.c_int64 * n)(*(ldys or [256] * n))
+    return L.hyb_gemv_grouped(count, la, pk, x, m, ldx, ya, ydt, la_y, None)
+
+
+def test_gemv_grouped_rejects(L):
+    lay = _good_layout()
+    assert _grouped(L, 0, None) == 0                               # count 0: no-op, arrays unused
+    assert _grouped(L, -1, [lay]) == 2                             # count < 0
+    assert _grouped(L, hb.MAX_GROUP + 1, [lay] * (hb.MAX_GROUP + 1)) == 2
+    assert L.hyb_gemv_grouped(1, None, None, FAKE, 1, 256, None, 3, None, None) == 1
+    assert _grouped(L, 2, [lay, lay], m=17) == 2                   # decode kernel m <= 16
+    bad = hb.HybLayout.from_buffer_copy(lay)
+    bad.magic = 0
+    assert _grouped(L, 2, [lay, bad]) == 5
+    assert "matrix 1" in hb.last_error()
+    other_k = _good_layout(k=128, b2=128, n=256)                   # k = 128 instead of 256
+    assert _grouped(L, 2, [lay, other_k]) == 1
+    assert "differs" in hb.last_error()
+    other_b2, _ = hb.plan(256, 256, 128, 64, "bf16", "idx2", np.zeros((2, 4), np.uint8))
+    assert _grouped(L, 2, [lay, other_b2]) == 1
+    assert _grouped(L, 2, [lay, lay], ys=[FAKE, None]) == 1         # null output of matrix 1
+    assert _grouped(L, 2, [lay, lay], ldys=[256, 100]) == 1         # ldy < n
+    assert _grouped(L, 2, [lay, lay], m=0) == 0                    # m == 0: no-op
+
+
 def test_product_m_zero_is_noop(L):
     lay = _good_layout()
     assert _call(L, "hyb_gemv", lay, m=0, x=None, y=None) == 0

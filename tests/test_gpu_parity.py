@@ -178,6 +178,60 @@ def test_gemv_70b_endpoints_sampled(index):
     assert P.layout.n_sparse == expect
 
 
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_gemv_grouped_layer(m):
+    """One decoder layer's q, k, v and gate, up (same x, own tile maps and
+    fractions) in one grouped launch: bitwise equal to separate launches,
+    and within the bound of the oracle on sampled tile rows."""
+    torch = _torch()
+    W = wl.workload(3)
+    mats = [mt for mt in W.matrices if mt.name in ("q", "k", "v", "gate", "up")]
+    note(f"gemv grouped layer m={m}")
+    x_bits = mats[0].activation_bits(m)
+    xt = upload(x_bits, "bf16")
+    Ps, refs = [], []
+    for mt in mats:
+        w = mt.weight_bits()
+        tmap = mt.tile_map()
+        Ps.append(pack_gpu(w, tmap, mt.b1, mt.b2, mt.dtype, "idx2"))
+        refs.append((mt, w, tmap))
+    outs = hb.gemv_grouped(Ps, xt)
+    sep = [hb.gemv(P, xt) for P in Ps]
+    torch.cuda.synchronize()
+    for (mt, w, tmap), o, so in zip(refs, outs, sep):
+        assert torch.equal(o, so), mt.name
+        rows, yref, sref = oracle_rows(w, tmap, mt, sample_tile_rows(mt, 3, m), x_bits)
+        assert_close(o.cpu().numpy()[:, rows], yref, sref, what=f"grouped {mt.name}")
+
+
+def test_gemv_grouped_mixed_shapes():
+    """Matrices of different b1 and n (one of them empty) in one launch, f16
+    weights with mask4 codes and fp16 output, against separate launches and
+    the oracle."""
+    torch = _torch()
+    note("gemv grouped mixed shapes")
+    k, b2 = 384, 128
+    specs = [(128, 64), (0, 128), (512, 256), (256, 128), (64, 64)]
+    x_bits = wl.float32_to_bits(np.random.default_rng(9).standard_normal((3, k)).astype(np.float32), "f16")
+    xt = upload(x_bits, "f16")
+    Ps, refs = [], []
+    for i, (n, b1) in enumerate(specs):
+        w, tmap = random_case(40 + i, n, k, b1, b2, "f16")
+        Ps.append(pack_gpu(w, tmap, b1, b2, "f16", "mask4"))
+        refs.append((w, tmap, b1))
+    outs = hb.gemv_grouped(Ps, xt, out_dtype=torch.float16)
+    sep = [hb.gemv(P, xt, out_dtype=torch.float16) for P in Ps]
+    torch.cuda.synchronize()
+    for (w, tmap, b1), o, so in zip(refs, outs, sep):
+        assert torch.equal(o, so)
+        if w.shape[0] == 0:
+            assert o.shape == (3, 0)
+            continue
+        yref, sref = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x_bits, "f16")
+        yb = oracle.widen(hb.tensor_to_bits(o), "f16")
+        assert_close(yb, yref, sref, extra=np.abs(yref) * 2.0 ** -11 + 2.0 ** -25, what="grouped f16")
+
+
 def test_gemv_output_16bit():
     torch = _torch()
     mat, w, tmap = workload_matrix(2, 0)
