@@ -35,6 +35,9 @@
 #ifndef HYB_GEMM_GROUP_N
 #define HYB_GEMM_GROUP_N 4
 #endif
+#ifndef HYB_GEMM_C192
+#define HYB_GEMM_C192 0.8
+#endif
 #ifndef HYB_W_AUX
 #define HYB_W_AUX 2  // non-temporal: the weights are read once per product
 #endif
@@ -1381,12 +1384,12 @@ int device_cus() {
 
 // Workgroup shape by token count.  Up to 128 tokens the register-fed kernel
 // runs (few tokens: the four wavefronts split K; more: they split n).  From
-// 129 tokens one of three LDS-fed shapes runs, 256 weight rows by BM = 256,
-// 128 or 64 tokens.  Every workgroup walks all of K, so the time is the
-// number of rounds of workgroups over the compute units times the time of
-// one workgroup; the relative step costs of the three shapes are measured
-// (a 256-token step costs 1, a 128-token step 0.64, a 64-token step 0.57),
-// and the shape with the smallest product runs.
+// 129 tokens one of four LDS-fed shapes runs, 256 weight rows by BM = 256,
+// 192, 128 or 64 tokens.  Every workgroup walks all of K, so the time is
+// the number of rounds of workgroups over the compute units times the time
+// of one workgroup; the relative step costs of the shapes are measured (a
+// 256-token step costs 1, a 192-token step 0.8, a 128-token step 0.64, a
+// 64-token step 0.57), and the shape with the smallest product runs.
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   if (m <= 64) return gemm_go<B2, DT, META, 1, 4, 4>(L, q, m, d, s);
@@ -1396,9 +1399,12 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   auto cost = [&](int64_t bm, double step) {
     return double((gn * ((m + bm - 1) / bm) + cus - 1) / cus) * step;
   };
-  const double c256 = cost(256, 1.0), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
-  if (c256 <= c128 && c256 <= c64) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8>(), 8>(L, q, m, d, s);
-  if (c128 <= c64) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8>(), 8>(L, q, m, d, s);
+  const double c256 = cost(256, 1.0), c192 = cost(192, HYB_GEMM_C192), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
+  const double best = c256 < c192 ? (c256 < c128 ? (c256 < c64 ? c256 : c64) : (c128 < c64 ? c128 : c64))
+                                  : (c192 < c128 ? (c192 < c64 ? c192 : c64) : (c128 < c64 ? c128 : c64));
+  if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8>(), 8>(L, q, m, d, s);
+  if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8>(), 8>(L, q, m, d, s);
+  if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8>(), 8>(L, q, m, d, s);
   return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4>(), 4>(L, q, m, d, s);
 }
 

@@ -281,14 +281,16 @@ def test_gemm_qwen14b_sampled(m):
     assert_close(y2[:, rows], yref, s, what=f"gemm_mfma m={m}")
 
 
-@pytest.mark.parametrize("m", [200, 256, 300, 512, 1024])
+@pytest.mark.parametrize("m", [200, 256, 300, 512, 700, 1024])
 def test_gemm_8b_up_shapes_sampled(m):
     """14336x4096, 128x128 tiles, 70% sparse tiles.  From 129 tokens the
-    launcher picks one of three workgroup shapes (256, 128 or 64 tokens per
-    workgroup) by the number of workgroup rounds on the device; on a
+    launcher picks one of four workgroup shapes (256, 192, 128 or 64 tokens
+    per workgroup) by the number of workgroup rounds on the device; on a
     256-CU device these token counts select the 64-token shape (200 with a
-    ragged last block, 256), the 128-token shape (300 ragged, 512) and the
-    256-token shape (1024)."""
+    ragged last block, 256), the 128-token shape (300 ragged, 512), the
+    192-token shape (700 ragged) and the 256-token shape (1024).  The
+    17408-row matrix at 2048 tokens (test_gemm_qwen14b_sampled) also runs
+    the 192-token shape."""
     torch = _torch()
     mat, w, tmap = workload_matrix(2, 0)
     note(f"gemm 8b up m={m}")
