@@ -168,8 +168,8 @@ hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_
 
 /* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same
- * arguments as hyb_gemv; m <= 16 runs the decode kernel, larger m the
- * matrix-core kernel. */
+ * arguments as hyb_gemv; m <= 8 runs the decode kernel, larger m the
+ * matrix-core kernels. */
 hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x,
                     int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                     void* stream);

@@ -286,7 +286,7 @@ def gemv_grouped(Ps, x, out_dtype=None, outs=None):
 
 
 def gemm(P: PackedWeight, x, out_dtype=None, out=None):
-    """Y = X W'^T for any number of tokens (decode kernel for <= 16)."""
+    """Y = X W'^T for any number of tokens (decode kernel up to 8, matrix cores above)."""
     return _product("hyb_gemm", P, x, out_dtype, out)
 
 

@@ -273,7 +273,7 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
 
 hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                     int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
-  if (m >= 0 && m <= hyb::kMaxGemvM) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (m >= 0 && m <= hyb::kGemvCrossoverM) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 

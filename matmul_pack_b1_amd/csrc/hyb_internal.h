@@ -11,6 +11,11 @@ namespace hyb {
 
 // Decode kernel handles up to this many tokens per launch.
 constexpr int kMaxGemvM = 16;
+// hyb_gemm runs the decode kernel up to this many tokens and the
+// matrix-core kernels above (measured: from 9 tokens the register-fed
+// matrix-core kernel is 1.4-1.9x faster on every workload shape; up to 4
+// the decode kernel is faster; between they are even).
+constexpr int kGemvCrossoverM = 8;
 // Matrices per grouped decode launch (HYB_MAX_GROUP in hyb.h).
 constexpr int kMaxGroup = HYB_MAX_GROUP;
 

@@ -1618,9 +1618,11 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
     // Eight wavefronts (one workgroup per CU) when the row groups fit in one
     // round, else four (two workgroups per CU).
     if (groups <= cus) {
+      if (m <= 16) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
       return m <= 32 ? gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s)
                      : gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
     }
+    if (m <= 16) return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
     return m <= 32 ? gemm_rx_go<B2, DT, META, 2, 4, 2>(L, q, m, d, s)
                    : gemm_rx_go<B2, DT, META, 4, 4, 2>(L, q, m, d, s);
   }

@@ -264,10 +264,10 @@ def test_gemm_random(m, b1, b2, dtype, meta):
     assert_close(y.cpu().numpy(), yref, s, what="gemm")
 
 
-@pytest.mark.parametrize("m", [16, 64, 256, 2048])
+@pytest.mark.parametrize("m", [8, 16, 64, 256, 2048])
 def test_gemm_qwen14b_sampled(m):
     """17408x5120, 64x64 tiles, 60% sparse tiles; M from 16 to 2048 through
-    hyb_gemm (decode kernel at 16) and the matrix-core kernel for every M."""
+    hyb_gemm and through the matrix-core entry point for every M."""
     torch = _torch()
     mat, w, tmap = workload_matrix(5, 0)
     note(f"gemm qwen14b m={m}")
