@@ -836,42 +836,39 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
 // and the aligned dword holding the sparse metadata word (a 16-bit load is
 // zero-extended by the compiler where it lands, which waits for it and
 // drains the ring); the B operands of every token block; the tile index.
-template <int MB>
+template <int MB, int RG>
 struct GemmRxStage {
-  u32x4_t v0[4], v1[4];
-  uint32_t m[4];
+  u32x4_t v0[RG][4], v1[RG][4];
+  uint32_t m[RG][4];
   uint4 b[MB][2];
-  int32_t ti;
+  int32_t ti[RG];
 };
 
 // With four wavefronts and up to 64 tokens the launch bound asks for two
 // wavefronts per SIMD (at most 256 registers each), so that two workgroups
-// share a CU; 128 tokens need the whole register file of a SIMD.
-template <int B2, int DT, int META, int MB, int WAVES, int STAGES>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4) ? 2 : 1) void k_gemm_rx(const uint4* __restrict__ dense,
-                                                        const uint4* __restrict__ val,
-                                                        const uint16_t* __restrict__ meta,
-                                                        const int32_t* __restrict__ tidx,
-                                                        const uint16_t* __restrict__ x,
-                                                        void* __restrict__ y, GemmDims d) {
+// share a CU; 128 tokens, or two row groups per wavefront, need the whole
+// register file of a SIMD.  RG is the number of 64-row groups per
+// workgroup (each wavefront multiplies all of them over its K range: two
+// groups halve the X reads per weight byte).
+template <int B2, int DT, int META, int MB, int WAVES, int STAGES, int RG>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 : 1) void k_gemm_rx(
+    const uint4* __restrict__ dense, const uint4* __restrict__ val, const uint16_t* __restrict__ meta,
+    const int32_t* __restrict__ tidx, const uint16_t* __restrict__ x, void* __restrict__ y, GemmDims d) {
   static_assert(WAVES == 4 || WAVES == 8, "tree reduction over 4 or 8 wavefronts");
   constexpr int BM = 16 * MB;
   constexpr int kStepsPerTile = B2 / 64;
-  constexpr int kPart = 4 * MB * 64 * 4;  // floats of one wavefront's partial sums
+  constexpr int kPart = RG * 4 * MB * 64 * 4;  // floats of one wavefront's partial sums
   __shared__ __attribute__((aligned(16))) float red[WAVES / 2][kPart];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int r = lane & 15;
-  const int32_t n0 = int32_t(blockIdx.x) * 64;
+  const int32_t n0 = int32_t(blockIdx.x) * 64 * RG;
   const int32_t m0 = int32_t(blockIdx.y) * BM;
-  const int32_t tn = n0 / d.b1;
-  const int rs0 = (n0 - tn * d.b1) / 16;
   const int32_t steps = d.tiles_k * kStepsPerTile;
   const int32_t s0 = (wave * steps) / WAVES;
   const int32_t cnt = ((wave + 1) * steps) / WAVES - s0;
-  const int32_t* __restrict__ trow = tidx + int64_t(tn) * d.tiles_k;
   const int32_t mrows = d.m - m0 < BM ? d.m - m0 : BM;
   const int64_t tile = int64_t(d.b1) * B2;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + int64_t(m0) * d.ldx, mrows * int32_t(d.ldx) * 2);
@@ -880,29 +877,37 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4) ? 2 : 1) void k
   const int dense_off = (q >> 1) * 1024 + ((2 * (q & 1)) * 16 + r) * 16;
 
   constexpr int32_t kNone = INT32_MIN;
-  auto load = [&](GemmRxStage<MB>& st, int32_t it) {
+  auto load = [&](GemmRxStage<MB, RG>& st, int32_t it) {
     const bool live = it < cnt;
-    int32_t ti = live ? trow[(s0 + it) / kStepsPerTile] : kNone;
-    const bool is_dense = ti >= 0;
-    const int32_t slot = is_dense ? ti : ~ti;
-    if (is_dense ? (slot >= d.n_dense) : (slot >= d.n_sparse)) ti = kNone;
-    st.ti = ti;
-    const bool ok = ti != kNone;
     const int kb = (s0 + it) % kStepsPerTile;
-    const int32_t slab_bytes = is_dense ? 32 * B2 : 16 * B2;
-    const char* base = is_dense
-        ? reinterpret_cast<const char*>(dense) + (int64_t(slot) * tile + int64_t(rs0) * 16 * B2) * 2
-        : reinterpret_cast<const char*>(val) + (int64_t(slot) * (tile / 2) + int64_t(rs0) * 8 * B2) * 2;
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(ok ? base : nullptr, ok ? 4 * slab_bytes : 0);
-    const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs0) * B2) * 2;
-    const __amdgpu_buffer_rsrc_t mr = make_rsrc((ok && !is_dense) ? mbase : nullptr, (ok && !is_dense) ? 8 * B2 : 0);
-    const int32_t o0 = is_dense ? 2 * kb * 1024 + dense_off : kb * 1024 + lane * 16;
-    const int32_t o1 = is_dense ? o0 + 256 : 0x40000000;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      st.v0[sl] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, sl * slab_bytes + o0, 0, 0));
-      st.v1[sl] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, sl * slab_bytes + o1, 0, 0));
-      st.m[sl] = __builtin_amdgcn_raw_buffer_load_b32(mr, (sl * 2 * B2 + lane * (B2 / 32) + kb * 2) & ~3, 0, 0);
+    for (int g = 0; g < RG; ++g) {
+      const int32_t ng = n0 + 64 * g;
+      const bool rows = ng < d.n;
+      const int32_t tn = rows ? ng / d.b1 : 0;
+      const int rs0 = (ng - tn * d.b1) / 16;
+      int32_t ti = (live && rows) ? tidx[int64_t(tn) * d.tiles_k + (s0 + it) / kStepsPerTile] : kNone;
+      const bool is_dense = ti >= 0;
+      const int32_t slot = is_dense ? ti : ~ti;
+      if (is_dense ? (slot >= d.n_dense) : (slot >= d.n_sparse)) ti = kNone;
+      st.ti[g] = ti;
+      const bool ok = ti != kNone;
+      const int32_t slab_bytes = is_dense ? 32 * B2 : 16 * B2;
+      const char* base = is_dense
+          ? reinterpret_cast<const char*>(dense) + (int64_t(slot) * tile + int64_t(rs0) * 16 * B2) * 2
+          : reinterpret_cast<const char*>(val) + (int64_t(slot) * (tile / 2) + int64_t(rs0) * 8 * B2) * 2;
+      const __amdgpu_buffer_rsrc_t ar = make_rsrc(ok ? base : nullptr, ok ? 4 * slab_bytes : 0);
+      const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs0) * B2) * 2;
+      const __amdgpu_buffer_rsrc_t mr =
+          make_rsrc((ok && !is_dense) ? mbase : nullptr, (ok && !is_dense) ? 8 * B2 : 0);
+      const int32_t o0 = is_dense ? 2 * kb * 1024 + dense_off : kb * 1024 + lane * 16;
+      const int32_t o1 = is_dense ? o0 + 256 : 0x40000000;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        st.v0[g][sl] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, sl * slab_bytes + o0, 0, 0));
+        st.v1[g][sl] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, sl * slab_bytes + o1, 0, 0));
+        st.m[g][sl] = __builtin_amdgcn_raw_buffer_load_b32(mr, (sl * 2 * B2 + lane * (B2 / 32) + kb * 2) & ~3, 0, 0);
+      }
     }
     const int32_t col = live ? (s0 + it) * 128 + q * 16 : 0x40000000;
 #pragma unroll
@@ -913,53 +918,58 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4) ? 2 : 1) void k
     }
   };
 
-  f32x4_t acc[4][MB];
+  f32x4_t acc[RG][4][MB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j) acc[g][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Every slab runs on v_smfmac: the first pass for both kinds (a sparse
   // chunk with its index word, or positions 0,1 of every group of a dense
   // piece, index 0x4444), the second pass for dense slabs (positions 2,3,
   // index 0xEEEE).  The selects are bit-selects on an opaque mask so they
   // stay branch-free.
-  auto compute = [&](const GemmRxStage<MB>& st, int32_t it) {
-    const int32_t ti = st.ti;
-    if (ti == kNone) return;
-    const bool is_dense = ti >= 0;
-    uint32_t dm = is_dense ? ~0u : 0u;
-    asm("" : "+v"(dm));
+  auto compute = [&](const GemmRxStage<MB, RG>& st, int32_t it) {
     const int mshift = ((lane * (B2 / 32) + ((s0 + it) % kStepsPerTile) * 2) & 2) * 8;
-    uint4 a0[4], a1[4];
-    uint32_t i0[4];
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const u32x4_t v0 = st.v0[sl], v1 = st.v1[sl];
-      a0[sl] = make_uint4(v0[0], bitsel(dm, v0[2], v0[1]), bitsel(dm, v1[0], v0[2]), bitsel(dm, v1[2], v0[3]));
-      u32x4_t t = {v0[1], v0[3], v1[1], v1[3]};
-      asm("" : "+v"(t));
-      a1[sl] = __builtin_bit_cast(uint4, t);
-      i0[sl] = bitsel(dm, 0x4444u, idx2_word<META>((st.m[sl] >> mshift) & 0xFFFFu));
-    }
+    for (int g = 0; g < RG; ++g) {
+      const int32_t ti = st.ti[g];
+      if (ti == kNone) continue;
+      const bool is_dense = ti >= 0;
+      uint32_t dm = is_dense ? ~0u : 0u;
+      asm("" : "+v"(dm));
+      uint4 a0[4], a1[4];
+      uint32_t i0[4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-        acc[sl][mb] = smfmac16x16x64<DT>(a0[sl], st.b[mb][0], st.b[mb][1], i0[sl], acc[sl][mb]);
-    if (is_dense) {
+      for (int sl = 0; sl < 4; ++sl) {
+        const u32x4_t v0 = st.v0[g][sl], v1 = st.v1[g][sl];
+        a0[sl] = make_uint4(v0[0], bitsel(dm, v0[2], v0[1]), bitsel(dm, v1[0], v0[2]), bitsel(dm, v1[2], v0[3]));
+        u32x4_t t = {v0[1], v0[3], v1[1], v1[3]};
+        asm("" : "+v"(t));
+        a1[sl] = __builtin_bit_cast(uint4, t);
+        i0[sl] = bitsel(dm, 0x4444u, idx2_word<META>((st.m[g][sl] >> mshift) & 0xFFFFu));
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl)
-          acc[sl][mb] = smfmac16x16x64<DT>(a1[sl], st.b[mb][0], st.b[mb][1], 0xEEEEu, acc[sl][mb]);
+          acc[g][sl][mb] = smfmac16x16x64<DT>(a0[sl], st.b[mb][0], st.b[mb][1], i0[sl], acc[g][sl][mb]);
+      if (is_dense) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+            acc[g][sl][mb] = smfmac16x16x64<DT>(a1[sl], st.b[mb][0], st.b[mb][1], 0xEEEEu, acc[g][sl][mb]);
+      }
     }
   };
 
   // STAGES-deep ring, unrolled so every stage index is a compile-time
   // constant; loads of the next STAGES-1 steps are in flight while a step
   // is multiplied.
-  GemmRxStage<MB> st[STAGES];
+  GemmRxStage<MB, RG> st[STAGES];
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) load(st[s], s);
   for (int32_t i = 0; i < cnt; i += STAGES) {
@@ -977,48 +987,56 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4) ? 2 : 1) void k
     if (wave >= h && wave < 2 * h) {
       float* dst = red[wave - h];
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          *reinterpret_cast<f32x4_t*>(dst + ((sl * MB + mb) * 64 + lane) * 4) = acc[sl][mb];
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            *reinterpret_cast<f32x4_t*>(dst + (((g * 4 + sl) * MB + mb) * 64 + lane) * 4) = acc[g][sl][mb];
     }
     __syncthreads();
     if (wave < h) {
       const float* src = red[wave];
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[sl][mb] += *reinterpret_cast<const f32x4_t*>(src + ((sl * MB + mb) * 64 + lane) * 4);
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[g][sl][mb] += *reinterpret_cast<const f32x4_t*>(src + (((g * 4 + sl) * MB + mb) * 64 + lane) * 4);
     }
     __syncthreads();
   }
   if (wave != 0) return;
 
-  // acc[sl][mb] lane L holds rows n0 + 16 sl + 4 (L/16) + 0..3 of token
-  // m0 + 16 mb + L%16.
+  // acc[g][sl][mb] lane L holds rows n0 + 64 g + 16 sl + 4 (L/16) + 0..3 of
+  // token m0 + 16 mb + L%16.
   const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int64_t m = int64_t(m0) + mb * 16 + (lane & 15);
+    const int64_t m = int64_t(m0) + mb * 16 + r;
     if (m >= d.m) continue;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const int64_t n = int64_t(n0) + sl * 16 + q * 4;
-      const f32x4_t v = acc[sl][mb];
-      const int64_t base = m * d.ldy + n;
-      if (d.ydt == HYB_F32) {
-        float* dst = static_cast<float*>(y) + base;
-        if (vec_ok) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    for (int g = 0; g < RG; ++g) {
+      if (n0 + 64 * g >= d.n) continue;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int64_t n = int64_t(n0) + 64 * g + sl * 16 + q * 4;
+        const f32x4_t v = acc[g][sl][mb];
+        const int64_t base = m * d.ldy + n;
+        if (d.ydt == HYB_F32) {
+          float* dst = static_cast<float*>(y) + base;
+          if (vec_ok) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = v[e];
+          }
         } else {
+          uint16_t* dst = static_cast<uint16_t*>(y) + base;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = v[e];
+          for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
         }
-      } else {
-        uint16_t* dst = static_cast<uint16_t*>(y) + base;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
       }
     }
   }
@@ -1571,12 +1589,12 @@ hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const Gemm
   return hipGetLastError();
 }
 
-template <int B2, int DT, int META, int MB, int WAVES, int STAGES>
+template <int B2, int DT, int META, int MB, int WAVES, int STAGES, int RG = 1>
 hipError_t gemm_rx_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
   if (gm > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(unsigned(L.n / 64), unsigned(gm));
-  hipLaunchKernelGGL((k_gemm_rx<B2, DT, META, MB, WAVES, STAGES>), grid, dim3(64 * WAVES), 0, s, q.dense,
+  const dim3 grid(unsigned((L.n + 64 * RG - 1) / (64 * RG)), unsigned(gm));
+  hipLaunchKernelGGL((k_gemm_rx<B2, DT, META, MB, WAVES, STAGES, RG>), grid, dim3(64 * WAVES), 0, s, q.dense,
                      q.val, q.meta, q.tidx, q.x, q.y, d);
   return hipGetLastError();
 }
@@ -1615,16 +1633,19 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   const int64_t cus = device_cus();
   const int64_t groups = L.n / 64;  // 64-row workgroups of the register-fed kernel
   if (m <= 64) {
-    // Eight wavefronts (one workgroup per CU) when the row groups fit in one
-    // round, else four (two workgroups per CU).
+    // Eight wavefronts (one workgroup per CU) when the 64-row groups fit in
+    // one round.  Otherwise up to 16 tokens four wavefronts (two workgroups
+    // per CU), and from 17 tokens two row groups per workgroup on four
+    // wavefronts, which halves the reads of X (measured on 17408 x 5120:
+    // 1.0-1.34x at 17-64 tokens; with one round of row groups the loss of
+    // wavefronts costs more than the X reads save).
     if (groups <= cus) {
       if (m <= 16) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
       return m <= 32 ? gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s)
                      : gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
     }
     if (m <= 16) return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
-    return m <= 32 ? gemm_rx_go<B2, DT, META, 2, 4, 2>(L, q, m, d, s)
-                   : gemm_rx_go<B2, DT, META, 4, 4, 2>(L, q, m, d, s);
+    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
   }
   if (m <= 128) {
     // 128 tokens per wavefront need a SIMD to themselves: only when the row

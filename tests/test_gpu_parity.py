@@ -301,6 +301,23 @@ def test_gemm_8b_up_shapes_sampled(m):
     assert_close(y[:, rows], yref, s, what=f"gemm m={m}")
 
 
+@pytest.mark.parametrize("m", [20, 64])
+def test_gemm_two_row_groups_odd(m):
+    """16448 rows (257 row groups of 64, more than one round on a 256-CU
+    device): from 17 tokens the register-fed kernel takes two row groups per
+    workgroup, and the last workgroup's second group lies past the last row."""
+    torch = _torch()
+    note(f"gemm two row groups, odd count, m={m}")
+    n, k, b1, b2 = 64 * 257, 192, 64, 64
+    w, tmap = random_case(77 + m, n, k, b1, b2, "bf16", frac=0.6)
+    x = wl.float32_to_bits(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32), "bf16")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    y = hb.gemm(P, upload(x, "bf16"))
+    torch.cuda.synchronize()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x, "bf16")
+    assert_close(y.cpu().numpy(), yref, s, what="gemm two row groups")
+
+
 def test_gemm_output_16bit():
     torch = _torch()
     note("gemm fp16 output")
