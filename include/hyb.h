@@ -79,6 +79,7 @@ enum { HYB_META_IDX2 = 1, HYB_META_MASK4 = 2 };      /* metadata codes */
 #define HYB_VERSION 1u
 #define HYB_ABI_VERSION 1
 #define HYB_MAX_GROUP 16 /* matrices per hyb_gemv_grouped call */
+#define HYB_MAX_RANK 256 /* largest rank of hyb_gemv_lowrank */
 
 /* Plain-old-data description of one packed matrix; filled by hyb_plan and
  * also usable as a serialised header (all fields fixed-width). */
@@ -165,6 +166,27 @@ hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x
 hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_packed* w,
                             const void* x, int32_t m, int64_t ldx, void* const* y,
                             int32_t y_dtype, const int64_t* ldy, void* stream);
+
+/* Decode product of a sparse + low-rank weight, 0 <= m <= 16 tokens:
+ * Y[i, :] = W' X[i, :] + U T[i, :], i.e. Y = X W'^T + T U^T.  The weight
+ * is approximated as a sparse part plus a rank-r part, W ~ S + L (3BASiL,
+ * gist.science, section 1 "Il Problema"; section 4 "Risultati
+ * Sperimentali" uses 2:4 sparse + rank 64), with S packed here and
+ * L = U V^T kept as its two factors.  T = X V^T (m x rank) is computed
+ * beforehand, for instance with hyb_gemv on V (rank x k) packed with an
+ * all-dense tile map; this call adds T U^T inside the decode kernel.
+ *   layout, w, x, m, ldx, y, y_dtype, ldy  as for hyb_gemv
+ *   t      device fp32, m x rank, row stride ldt >= rank, ldt % 4 == 0,
+ *          16-byte aligned
+ *   u      device, n x rank of layout->dtype, row stride ldu >= rank,
+ *          ldu % 8 == 0, 16-byte aligned
+ *   rank   0 <= rank <= HYB_MAX_RANK, rank % 8 == 0 (0: plain hyb_gemv)
+ * The low-rank term is accumulated in fp32 (u widened, fp32 products), into
+ * the same per-row sums as the sparse product. */
+hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                            int32_t m, int64_t ldx, const float* t, int64_t ldt, const void* u,
+                            int64_t ldu, int32_t rank, void* y, int32_t y_dtype, int64_t ldy,
+                            void* stream);
 
 /* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same

@@ -26,9 +26,10 @@ MAX_GEMV_M = 16
 META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4}
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
-EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_gemm", "hyb_gemm_mfma",
-            "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_gemv_lowrank",
+            "hyb_gemm", "hyb_gemm_mfma", "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
 MAX_GROUP = 16
+MAX_RANK = 256
 
 
 class HybLayout(ctypes.Structure):
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.hyb_gemv_grouped.argtypes = [I32, ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64,
                                    ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I64), P]
     L.hyb_gemv_grouped.restype = I32
+    L.hyb_gemv_lowrank.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I64, P,
+                                   I64, I32, P, I32, I64, P]
+    L.hyb_gemv_lowrank.restype = I32
     L.hyb_stream_read.argtypes = [P, I64, P, I32, P]
     L.hyb_stream_read.restype = I32
     L.hyb_status_str.argtypes = [I32]
@@ -283,6 +287,41 @@ def gemv_grouped(Ps, x, out_dtype=None, outs=None):
                                 int(x.stride(0)) if x.numel() else int(k), ys, code, ldys, _stream(x.device))
     check(st, "hyb_gemv_grouped")
     return outs
+
+
+def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
+    """Decode product of a sparse + low-rank weight: Y = X W'^T + T U^T,
+    with t = X V^T (fp32, m x rank) given and u (n x rank, weight dtype)."""
+    torch = _torch()
+    _check_rows(x, "x")
+    _check_rows(t, "t")
+    _check_rows(u, "u")
+    m = x.shape[0]
+    n, k = P.shape
+    rank = t.shape[1]
+    if t.shape[0] != m or u.shape != (n, rank):
+        raise ValueError(f"t must be {m} x rank and u {n} x rank")
+    if t.dtype != torch.float32:
+        raise TypeError("t must be float32")
+    code = _out_code(P, out_dtype)
+    tdt = {HYB_F32: torch.float32, HYB_BF16: torch.bfloat16, HYB_F16: torch.float16}[code]
+    if out is None:
+        out = torch.empty((m, n), dtype=tdt, device=x.device)
+    st = lib().hyb_gemv_lowrank(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
+                                int(x.stride(0)) if x.numel() else int(k), _ptr(t),
+                                int(t.stride(0)) if t.numel() else int(rank), _ptr(u),
+                                int(u.stride(0)) if u.numel() else int(rank), int(rank), _ptr(out), code,
+                                int(out.stride(0)) if out.numel() else int(n), _stream(x.device))
+    check(st, "hyb_gemv_lowrank")
+    return out
+
+
+def sparse_lowrank_gemv(P: PackedWeight, V: PackedWeight, u, x, out_dtype=None, out=None):
+    """Y = X (W' + U V^T)^T in two launches: T = X V^T with the decode
+    kernel on V (rank x k, packed with an all-dense map), then the sparse
+    product with T U^T added in the same kernel."""
+    t = gemv(V, x)
+    return gemv_lowrank(P, x, t, u, out_dtype, out)
 
 
 def gemm(P: PackedWeight, x, out_dtype=None, out=None):

@@ -257,6 +257,28 @@ hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_
                     "grouped gemv launch");
 }
 
+hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                            int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, hyb::kMaxGemvM);
+  if (st != HYB_OK) return st;
+  if (rank < 0 || rank > hyb::kMaxRank || rank % 8 != 0)
+    return fail(HYB_ERR_SHAPE, "rank = %d must be a multiple of 8 in [0, %d]", rank, hyb::kMaxRank);
+  if (rank == 0) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (m == 0 || layout->n == 0) return ok();
+  if (!t || !aligned(t, 16)) return fail(HYB_ERR_INVALID_ARG, "t is NULL or not 16-byte aligned");
+  if (ldt < rank || ldt % 4 != 0)
+    return fail(HYB_ERR_INVALID_ARG, "t row stride %lld must be >= rank and a multiple of 4", (long long)ldt);
+  if (!u || !aligned(u, 16)) return fail(HYB_ERR_INVALID_ARG, "u is NULL or not 16-byte aligned");
+  if (ldu < rank || ldu % 8 != 0)
+    return fail(HYB_ERR_INVALID_ARG, "u row stride %lld must be >= rank and a multiple of 8", (long long)ldu);
+  if (int64_t(m) * ldx * 2 >= (int64_t(1) << 31))
+    return fail(HYB_ERR_UNSUPPORTED, "decode kernel needs m * ldx * 2 < 2^31 bytes of x");
+  return hip_status(hyb::launch_gemv_lowrank(*layout, *w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy,
+                                             static_cast<hipStream_t>(stream)),
+                    "low-rank gemv launch");
+}
+
 hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                          int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);

@@ -25,6 +25,12 @@ hipError_t launch_unpack(const hyb_layout& L, const hyb_packed& P, void* w, int6
                          hipStream_t s);
 hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
                        int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
+// Decode product plus the low-rank term T U^T (hyb_gemv_lowrank).
+hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
+                               const float* t, int64_t ldt, const void* u, int64_t ldu, int rank, void* y,
+                               int y_dtype, int64_t ldy, hipStream_t s);
+// Largest rank of hyb_gemv_lowrank (HYB_MAX_RANK in hyb.h).
+constexpr int kMaxRank = HYB_MAX_RANK;
 // All matrices share k, b2, dtype and metadata kind (checked by the caller).
 hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
                                int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s);

@@ -57,6 +57,16 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;  // an LDS-reside
 
 // ------------------------------------------------------------- helpers ----
 
+// fp32 value of a bf16 / fp16 bit pattern (low 16 bits of `bits`).
+template <int DT>
+__device__ __forceinline__ float widen16(uint32_t bits) {
+  if constexpr (DT == HYB_BF16) {
+    return __builtin_bit_cast(float, bits << 16);
+  } else {
+    return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
+  }
+}
+
 // Bits of a where m is set, of b elsewhere.
 __device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
 
@@ -296,6 +306,11 @@ struct GemvDims {
   int64_t ldx, ldy;
   int32_t tiles_k, n_dense, n_sparse;
   int b1, m, ydt;
+  // low-rank term T U^T (hyb_gemv_lowrank only): T m x rank fp32, U n x rank
+  const float* t;
+  const uint16_t* u;
+  int64_t ldt, ldu;
+  int32_t rank;
 };
 
 constexpr int kBufDword3 = 0x00020000;  // raw buffer resource word 3 on gfx9-family parts
@@ -422,8 +437,14 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2>& st, int32_
   }
 }
 
-// The product of one 16-row slab (the whole work of one workgroup).
-template <int MT, int B2, int DT, int META, int WAVES, int STAGES>
+// The product of one 16-row slab (the whole work of one workgroup).  With
+// LR the slab also adds the low-rank term sum_j T[m][j] U[row][j] (3BASiL,
+// gist.science, section 1: W ~ S + L with L of rank r, here L = U V^T and
+// T = X V^T given): wavefront 0's lanes take row L%16 and every fourth
+// 8-column chunk of the rank, and add their partial dot products into the
+// row sums before the lane and wavefront reduction, so the order of the
+// additions stays fixed.
+template <int MT, int B2, int DT, int META, int WAVES, int STAGES, bool LR = false>
 __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const uint4* __restrict__ val,
                                           const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
                                           const uint16_t* __restrict__ x, void* __restrict__ y,
@@ -473,6 +494,39 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
     }
   }
 
+  if constexpr (LR) {
+    if (wave == 0) {
+      const int64_t row = slab * 16 + (lane & 15);
+      for (int32_t j0 = (lane >> 4) * 8; j0 < d.rank; j0 += 32) {
+        const uint4 uv = *reinterpret_cast<const uint4*>(d.u + row * d.ldu + j0);
+        const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        float uf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uf[2 * i] = widen16<DT>(uw[i] & 0xFFFFu);
+          uf[2 * i + 1] = widen16<DT>(uw[i] >> 16);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < d.m) {
+            const float4 t0 = *reinterpret_cast<const float4*>(d.t + int64_t(m) * d.ldt + j0);
+            const float4 t1 = *reinterpret_cast<const float4*>(d.t + int64_t(m) * d.ldt + j0 + 4);
+            float a = acc[m];
+            a = fmaf(uf[0], t0.x, a);
+            a = fmaf(uf[1], t0.y, a);
+            a = fmaf(uf[2], t0.z, a);
+            a = fmaf(uf[3], t0.w, a);
+            a = fmaf(uf[4], t1.x, a);
+            a = fmaf(uf[5], t1.y, a);
+            a = fmaf(uf[6], t1.z, a);
+            a = fmaf(uf[7], t1.w, a);
+            acc[m] = a;
+          }
+        }
+      }
+    }
+  }
+
   // Lanes L, L^16, L^32, L^48 share row L%16: swizzle-add across the two
   // 16-lane halves of each 32-lane group, then across the 32-lane halves.
 #pragma unroll
@@ -498,14 +552,14 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
   }
 }
 
-template <int MT, int B2, int DT, int META, int WAVES, int STAGES>
+template <int MT, int B2, int DT, int META, int WAVES, int STAGES, bool LR>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ dense,
                                                      const uint4* __restrict__ val,
                                                      const uint16_t* __restrict__ meta,
                                                      const int32_t* __restrict__ tidx,
                                                      const uint16_t* __restrict__ x,
                                                      void* __restrict__ y, GemvDims d) {
-  gemv_slab<MT, B2, DT, META, WAVES, STAGES>(dense, val, meta, tidx, x, y, d, blockIdx.x);
+  gemv_slab<MT, B2, DT, META, WAVES, STAGES, LR>(dense, val, meta, tidx, x, y, d, blockIdx.x);
 }
 
 // Grouped decode product: one launch multiplies the same x by up to
@@ -1445,35 +1499,39 @@ struct GemvPtrs {
   void* y;
 };
 
-template <int MT, int DT, int META>
+template <int MT, int DT, int META, bool LR>
 void gemv_b2(int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
   const dim3 block(64 * kGemvWaves);
   switch (b2) {
     case 64:
-      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, kGemvWaves, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
       break;
     case 128:
-      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, kGemvWaves, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
       break;
     default:
-      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, kGemvWaves, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
       break;
   }
 }
 
-template <int DT, int META>
+template <int DT, int META, bool LR>
 void gemv_mt(int m, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
-  if (m <= 1) gemv_b2<1, DT, META>(b2, grid, s, q, d);
-  else if (m <= 2) gemv_b2<2, DT, META>(b2, grid, s, q, d);
-  else if (m <= 4) gemv_b2<4, DT, META>(b2, grid, s, q, d);
-  else if (m <= 8) gemv_b2<8, DT, META>(b2, grid, s, q, d);
-  else gemv_b2<16, DT, META>(b2, grid, s, q, d);
+  if (m <= 1) gemv_b2<1, DT, META, LR>(b2, grid, s, q, d);
+  else if (m <= 2) gemv_b2<2, DT, META, LR>(b2, grid, s, q, d);
+  else if (m <= 4) gemv_b2<4, DT, META, LR>(b2, grid, s, q, d);
+  else if (m <= 8) gemv_b2<8, DT, META, LR>(b2, grid, s, q, d);
+  else gemv_b2<16, DT, META, LR>(b2, grid, s, q, d);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
-                       void* y, int y_dtype, int64_t ldy, hipStream_t s) {
+namespace {
+
+template <bool LR>
+hipError_t launch_gemv_impl(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
+                            void* y, int y_dtype, int64_t ldy, const float* t, int64_t ldt, const void* u,
+                            int64_t ldu, int rank, hipStream_t s) {
   GemvPtrs q{static_cast<const uint4*>(P.dense), static_cast<const uint4*>(P.val),
              static_cast<const uint16_t*>(P.meta), P.tidx, static_cast<const uint16_t*>(x), y};
   GemvDims d{};
@@ -1485,15 +1543,33 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
   d.b1 = L.b1;
   d.m = m;
   d.ydt = y_dtype;
+  d.t = t;
+  d.ldt = ldt;
+  d.u = static_cast<const uint16_t*>(u);
+  d.ldu = ldu;
+  d.rank = rank;
   const dim3 grid(unsigned(L.n / 16));
   if (L.dtype == HYB_BF16) {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2>(m, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_BF16, HYB_META_MASK4>(m, L.b2, grid, s, q, d);
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, L.b2, grid, s, q, d);
+    else gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
   } else {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2>(m, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_F16, HYB_META_MASK4>(m, L.b2, grid, s, q, d);
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, L.b2, grid, s, q, d);
+    else gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
+                       void* y, int y_dtype, int64_t ldy, hipStream_t s) {
+  return launch_gemv_impl<false>(L, P, x, m, ldx, y, y_dtype, ldy, nullptr, 0, nullptr, 0, 0, s);
+}
+
+hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
+                               const float* t, int64_t ldt, const void* u, int64_t ldu, int rank, void* y,
+                               int y_dtype, int64_t ldy, hipStream_t s) {
+  return launch_gemv_impl<true>(L, P, x, m, ldx, y, y_dtype, ldy, t, ldt, u, ldu, rank, s);
 }
 
 namespace {

@@ -4,6 +4,6 @@ reference product.  Never imported by the product path."""
 from .hyb_oracle import (  # noqa: F401
     DTYPES, META_KINDS, PATTERNS, check_shape, dense_index, kept_positions,
     magnitude_key, meta_word_index, nibble, pack, plan, positions_from_nibble,
-    prune, ref_matmul, ref_rows, sparsity, unpack, value_index, widen,
+    prune, ref_lowrank, ref_matmul, ref_rows, sparsity, unpack, value_index, widen,
     within_bound,
 )

@@ -34,7 +34,9 @@ Readings where the pages are silent (each also listed in the design notes):
   R5 every group stores exactly two slots, zeros included;
   R6 dropped positions unpack to +0.0 (bit pattern 0x0000);
   R7 the stream layout below (format "HYB1");
-  R8 ragged shapes (n % b1 or k % b2 non-zero) are rejected.
+  R8 ragged shapes (n % b1 or k % b2 non-zero) are rejected;
+  R13 sparse + low-rank: L = U V^T is held as its two factors and T = X V^T
+      is computed before the product (ref_lowrank).
 
 Format HYB1 (all element indices count 16-bit words):
   tile t = tn * TK + tk, TN = n / b1, TK = k / b2, tile_map[tn, tk] in {0, 1};
@@ -291,6 +293,24 @@ def ref_matmul(wp_bits, x_bits, dtype: str) -> tuple[np.ndarray, np.ndarray]:
     w = widen(wp_bits, dtype)
     x = widen(np.atleast_2d(np.asarray(x_bits, dtype=np.uint16)), dtype)
     return x @ w.T, np.abs(x) @ np.abs(w).T
+
+
+def ref_lowrank(wp_bits, x_bits, t, u_bits, dtype: str) -> tuple[np.ndarray, np.ndarray]:
+    """Sparse + low-rank product (3BASiL, gist.science, section 1 "Il
+    Problema": W ~ S + L with L of rank r; section 4 "Risultati
+    Sperimentali": 2:4 sparse + rank 64).  With S = W' (the hybrid weight)
+    and L = U V^T held as its factors, and T = X V^T given (float32, m x r):
+
+        y_ref[m, n] = sum_k W'[n, k] X[m, k] + sum_j T[m, j] U[n, j]
+        s[m, n]     = sum_k |W'[n, k] X[m, k]| + sum_j |T[m, j] U[n, j]|
+
+    in float64 from exact widenings (T is taken as given, so the check does
+    not depend on how T was rounded).  R13: L enters through its factors and
+    T is computed before the product."""
+    y, s = ref_matmul(wp_bits, x_bits, dtype)
+    tt = np.atleast_2d(np.asarray(t, dtype=np.float64))
+    uu = widen(np.atleast_2d(np.asarray(u_bits, dtype=np.uint16)), dtype)
+    return y + tt @ uu.T, s + np.abs(tt) @ np.abs(uu).T
 
 
 def ref_rows(wp_bits, x_bits, dtype: str, rows) -> tuple[np.ndarray, np.ndarray]:

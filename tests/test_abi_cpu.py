@@ -188,6 +188,33 @@ def test_gemv_grouped_rejects(L):
     assert _grouped(L, 2, [lay, lay], m=0) == 0                    # m == 0: no-op
 
 
+def test_gemv_lowrank_rejects(L):
+    lay = _good_layout()
+    P = hb.HybPacked(FAKE, FAKE, FAKE, FAKE)
+
+    def call(m=1, t=FAKE, ldt=64, u=FAKE, ldu=64, rank=64, lay=lay):
+        return L.hyb_gemv_lowrank(ctypes.byref(lay), ctypes.byref(P), FAKE, m, 256, t, ldt, u, ldu, rank,
+                                  FAKE, 3, 256, None)
+    assert call(rank=-8) == 2
+    assert call(rank=7) == 2                        # rank % 8
+    assert call(rank=hb.MAX_RANK + 8) == 2
+    assert call(m=17) == 2                          # decode kernel m <= 16
+    assert call(t=None) == 1
+    assert call(t=FAKE + 4) == 1                    # t alignment
+    assert call(ldt=32) == 1                        # ldt < rank
+    assert call(ldt=66) == 1                        # ldt % 4
+    assert call(u=None) == 1
+    assert call(u=FAKE + 8) == 1                    # u alignment
+    assert call(ldu=60) == 1                        # ldu < rank
+    assert call(ldu=68) == 1                        # ldu % 8
+    assert call(m=0, rank=0) == 0                   # rank 0 and m 0: no-op
+    assert call(m=0) == 0                           # m 0: no-op
+    bad = hb.HybLayout.from_buffer_copy(lay)
+    bad.magic = 0
+    assert call(lay=bad) == 5
+    assert hb.last_error()
+
+
 def test_product_m_zero_is_noop(L):
     lay = _good_layout()
     assert _call(L, "hyb_gemv", lay, m=0, x=None, y=None) == 0

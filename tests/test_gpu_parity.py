@@ -232,6 +232,57 @@ def test_gemv_grouped_mixed_shapes():
         assert_close(yb, yref, sref, extra=np.abs(yref) * 2.0 ** -11 + 2.0 ** -25, what="grouped f16")
 
 
+@pytest.mark.parametrize("rank", [8, 64, 256])
+@pytest.mark.parametrize("m", [1, 3, 16])
+@pytest.mark.parametrize("b1,b2,dtype,meta", [(128, 128, "bf16", "idx2"), (64, 256, "f16", "mask4")])
+def test_gemv_lowrank(rank, m, b1, b2, dtype, meta):
+    """Y = X W'^T + T U^T with T given: against the oracle, and bitwise
+    equal to the plain decode product when U = 0."""
+    torch = _torch()
+    note(f"gemv lowrank r={rank} m={m} {b1}x{b2} {dtype} {meta}")
+    n, k = 2 * b1, 2 * b2
+    w, tmap = random_case(rank + m, n, k, b1, b2, dtype)
+    rng = np.random.default_rng(rank * 31 + m)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), dtype)
+    t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    xt = upload(x, dtype)
+    tt = torch.from_numpy(t).to(dev())
+    y = hb.gemv_lowrank(P, xt, tt, upload(u, dtype))
+    y0 = hb.gemv_lowrank(P, xt, tt, upload(np.zeros_like(u), dtype))
+    yg = hb.gemv(P, xt)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, yg)
+    yref, s = oracle.ref_lowrank(oracle.prune(w, tmap, b1, b2), x, t, u, dtype)
+    assert_close(y.cpu().numpy(), yref, s, what="gemv lowrank")
+
+
+def test_sparse_lowrank_end_to_end():
+    """Two launches on the 8B up projection shape: T = X V^T with the decode
+    kernel on V (64 x 4096, packed all-dense), then the hybrid product with
+    T U^T added (2:4 sparse + rank 64).  The oracle computes T itself; its
+    error bound adds T's own bound carried through |U|."""
+    torch = _torch()
+    note("sparse + low-rank end to end")
+    mat, w, tmap = workload_matrix(2, 0)
+    rank, m = 64, 4
+    rng = np.random.default_rng(64)
+    v = wl.float32_to_bits(rng.standard_normal((rank, mat.k)).astype(np.float32) * 0.02, "bf16")
+    u = wl.float32_to_bits(rng.standard_normal((mat.n, rank)).astype(np.float32) * 0.02, "bf16")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    V = pack_gpu(v, np.zeros((1, mat.k // 64), np.uint8), 64, 64, "bf16", "idx2")
+    y = hb.sparse_lowrank_gemv(P, V, upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
+    t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
+    tile_rows = sample_tile_rows(mat, 4, 7)
+    rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
+    sub = oracle.prune(w[rows], tmap[tile_rows], mat.b1, mat.b2)
+    yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
+    extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
+    assert_close(y[:, rows], yref, s, extra=extra, what="sparse + low-rank")
+
+
 def test_gemv_output_16bit():
     torch = _torch()
     mat, w, tmap = workload_matrix(2, 0)

@@ -120,3 +120,43 @@ def test_prune_mutation_caught(monkeypatch):
     monkeypatch.setattr(oracle, "prune", _prune_keeps_three)
     with pytest.raises(FAIL):
         pins.test_invariants(3, "idx2")
+
+
+def _lowrank_u_transposed(wp_bits, x_bits, t, u_bits, dtype):
+    y, s = ho.ref_matmul(wp_bits, x_bits, dtype)
+    tt = np.atleast_2d(np.asarray(t, dtype=np.float64))
+    uu = ho.widen(np.atleast_2d(np.asarray(u_bits, dtype=np.uint16)), dtype)
+    uu = uu.T.reshape(uu.shape) if uu.shape[0] != uu.shape[1] else uu.T
+    return y + tt @ uu.T, s + np.abs(tt) @ np.abs(uu).T
+
+
+def _lowrank_dropped(wp_bits, x_bits, t, u_bits, dtype):
+    return ho.ref_matmul(wp_bits, x_bits, dtype)
+
+
+def _lowrank_sign(wp_bits, x_bits, t, u_bits, dtype):
+    y, s = ho.ref_matmul(wp_bits, x_bits, dtype)
+    tt = np.atleast_2d(np.asarray(t, dtype=np.float64))
+    uu = ho.widen(np.atleast_2d(np.asarray(u_bits, dtype=np.uint16)), dtype)
+    return y - tt @ uu.T, s + np.abs(tt) @ np.abs(uu).T
+
+
+def _lowrank_last_rank_dropped(wp_bits, x_bits, t, u_bits, dtype):
+    y, s = ho.ref_matmul(wp_bits, x_bits, dtype)
+    tt = np.atleast_2d(np.asarray(t, dtype=np.float64))[:, :-1]
+    uu = ho.widen(np.atleast_2d(np.asarray(u_bits, dtype=np.uint16)), dtype)[:, :-1]
+    return y + tt @ uu.T, s + np.abs(tt) @ np.abs(uu).T
+
+
+@pytest.mark.parametrize("func", [_lowrank_u_transposed, _lowrank_dropped, _lowrank_sign,
+                                  _lowrank_last_rank_dropped])
+def test_lowrank_mutations_caught(monkeypatch, golden_dir, func):
+    monkeypatch.setattr(ho, "ref_lowrank", func)
+    monkeypatch.setattr(oracle, "ref_lowrank", func)
+    caught = 0
+    for pin in (lambda: pins.test_ref_lowrank_golden(golden_dir), pins.test_ref_lowrank_loops_and_special_cases):
+        try:
+            pin()
+        except FAIL:
+            caught += 1
+    assert caught >= 1

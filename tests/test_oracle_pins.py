@@ -355,3 +355,57 @@ def test_ref_matmul_orientation():
     assert y.shape == (1, 16)
     assert y[0, 3] == 2.0 * 3.0 - 4.0 and s[0, 3] == 10.0
     assert np.count_nonzero(y) == 1
+
+
+# ------------------------------------------------- sparse + low-rank -------
+
+def load_lowrank_golden(golden_dir):
+    rows = {}
+    with open(os.path.join(golden_dir, "lowrank_small.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key in ("W", "X", "U"):
+                rows.setdefault(key, []).append([int(v, 16) for v in vals])
+            else:
+                rows.setdefault(key, []).append([float(v) for v in vals])
+    return {k: np.array(v, dtype=np.uint16 if k in ("W", "X", "U") else np.float64) for k, v in rows.items()}
+
+
+def test_ref_lowrank_golden(golden_dir):
+    g = load_lowrank_golden(golden_dir)
+    y, s = oracle.ref_lowrank(g["W"], g["X"], g["T"], g["U"], "bf16")
+    np.testing.assert_array_equal(y, g["Y"])
+    np.testing.assert_array_equal(s, g["S"])
+
+
+def test_ref_lowrank_loops_and_special_cases():
+    """Brute-force loops on a small case with U not square (a transposed
+    operand or swapped index fails), and the two special cases: U = 0 gives
+    the plain hybrid product, W' = 0 gives T U^T alone."""
+    rng = np.random.default_rng(3)
+    n, k, r, m = 16, 64, 3, 2
+    w = wl.float32_to_bits(rng.standard_normal((n, k)).astype(np.float32), "f16")
+    tmap = np.ones((1, 1), np.uint8)
+    wp = oracle.prune(w, tmap, n, k)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), "f16")
+    t = rng.standard_normal((m, r)).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, r)).astype(np.float32), "f16")
+    y, s = oracle.ref_lowrank(wp, x, t, u, "f16")
+    wv, xv, uv = oracle.widen(wp, "f16"), oracle.widen(x, "f16"), oracle.widen(u, "f16")
+    for i in range(m):
+        for j in range(n):
+            terms = [wv[j, c] * xv[i, c] for c in range(k)] + [float(t[i, q]) * uv[j, q] for q in range(r)]
+            assert math.isclose(y[i, j], math.fsum(terms), rel_tol=0, abs_tol=1e-12)
+            assert math.isclose(s[i, j], math.fsum(abs(v) for v in terms), rel_tol=0, abs_tol=1e-12)
+    y0, s0 = oracle.ref_lowrank(wp, x, t, np.zeros_like(u), "f16")
+    yr, sr = oracle.ref_matmul(wp, x, "f16")
+    np.testing.assert_array_equal(y0, yr)
+    np.testing.assert_array_equal(s0, sr)
+    yz, _ = oracle.ref_lowrank(np.zeros_like(wp), x, t, u, "f16")
+    for i in range(m):
+        for j in range(n):
+            assert math.isclose(yz[i, j], math.fsum(float(t[i, q]) * uv[j, q] for q in range(r)),
+                                rel_tol=0, abs_tol=1e-12)
