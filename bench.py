@@ -21,7 +21,9 @@ kind (stepping by 3 copies) so the 256 MB last-level cache holds nothing
 from the previous use of a copy.
 
 After the timed steps, the grouped decode launch is compared with separate
-launches on one decoder layer (JSON key "grouped"), and the prefill GEMM is
+launches on one decoder layer (JSON key "grouped"), the sparse + low-rank
+decode product is compared with the plain one (JSON key "lowrank"), and the
+prefill GEMM is
 measured on its own workload
 (Qwen3-14B-shaped 17408 x 5120, 64 x 64 tiles, M = 2048): hybrid, the same
 kernel all-dense, and the vendor BLAS dense product, with the matrix-core
@@ -151,7 +153,7 @@ def main():
     ap.add_argument("--prefill-m", type=int, default=2048,
                     help="token count of the prefill GEMM measurement")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,prefill)")
+                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 128 MiB device copies (torch copy kernel) as a counter reference")
@@ -175,7 +177,7 @@ def main():
     dev = torch.device("cuda:0")
     rotate = int(args.rotate_gib * (1 << 30))
     rows = set(args.only.split(",")) if args.only else {"pack", "gemv", "dense", "unpack", "gemm", "grouped",
-                                                         "prefill"}
+                                                         "lowrank", "prefill"}
 
     if args.copy_calibration:
         # A plain copy of known size: 128 MiB read + 128 MiB written per
@@ -396,6 +398,10 @@ def main():
         log("[bench] grouped decode launch on one decoder layer")
         out["grouped"] = grouped(hb, torch, wl, dev, args.meta)
         log(f"[bench] grouped: {out['grouped']}")
+    if "lowrank" in rows:
+        log("[bench] sparse + low-rank decode")
+        out["lowrank"] = lowrank(hb, torch, wl, dev, args.meta)
+        log(f"[bench] lowrank: {out['lowrank']}")
     if "prefill" in rows and args.prefill_m > 0:
         log(f"[bench] prefill GEMM M={args.prefill_m}")
         out["prefill"] = prefill(hb, torch, wl, dev, args.prefill_m, args.meta)
@@ -526,6 +532,76 @@ def grouped(hb, torch, wl, dev, meta):
            "GBps_grouped": round(alg / (us_grp * 1e-6) / 1e9, 1),
            "timing": f"graph burst of {reps} layer passes over {n_copies} rotating copies, median of 5 replays"}
     del packed, outs
+    torch.cuda.empty_cache()
+    return out
+
+
+def lowrank(hb, torch, wl, dev, meta, rank=64):
+    """Sparse + low-rank decode (3BASiL, 2:4 sparse + rank 64) on the
+    Llama-3.1-8B up projection at M = 1: the plain hybrid product of S
+    against T = X V
+    followed by the hybrid product with T U^T added in the same kernel.
+    T comes from the projection kernel (V held transposed, 64 x 4096).
+    S, V and U rotate over enough copies to leave the last-level cache cold;
+    V and U are seeded normal draws scaled by 0.02."""
+    mat = wl.workload(2).matrices[0]
+    w = hb.bits_to_tensor(mat.weight_bits(), mat.dtype, dev)
+    tmap = mat.tile_map()
+    P0 = hb.pack(w, tmap, mat.b1, mat.b2, meta)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(64)
+    def factors():
+        v = (torch.randn((rank, mat.k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        u = (torch.randn((mat.n, rank), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        return v, u
+
+    V0, U0 = factors()
+    per_copy = P0.weight_bytes() + V0.numel() * 2 + U0.numel() * 2
+    n_copies = copies_for(per_copy, 1 << 30)
+    Ps, Vs, Us = [P0], [V0], [U0]
+    for _ in range(n_copies - 1):
+        Ps.append(hb.pack(w, tmap, mat.b1, mat.b2, meta))
+        v_, u_ = factors()
+        Vs.append(v_)
+        Us.append(u_)
+    del w
+    torch.cuda.synchronize()
+    x = hb.bits_to_tensor(mat.activation_bits(1), mat.dtype, dev)
+    t = torch.empty((1, rank), dtype=torch.float32, device=dev)
+    y = torch.empty((1, mat.n), dtype=torch.float32, device=dev)
+
+    def plain(count):
+        for i in range(count):
+            hb.gemv(Ps[(3 * i) % n_copies], x, out=y)
+
+    def two_launch(count):
+        for i in range(count):
+            c = (3 * i) % n_copies
+            hb.lowrank_project(Vs[c], x, out=t)
+            hb.gemv_lowrank(Ps[c], x, t, Us[c], out=y)
+
+    def fused_only(count):
+        for i in range(count):
+            c = (3 * i) % n_copies
+            hb.gemv_lowrank(Ps[c], x, t, Us[c], out=y)
+
+    reps = 2 * n_copies
+    us_plain = graph_us(torch, plain, reps)
+    us_two = graph_us(torch, two_launch, reps)
+    us_fused = graph_us(torch, fused_only, reps)
+    b_plain = alg_bytes(P0.layout, 1)
+    # projection: V + x read, T written; product: as plain plus U and T read
+    b_lr = b_plain + V0.numel() * 2 + 2 * mat.k + 4 * rank + U0.numel() * 2 + 4 * rank
+    out = {"workload": f"Llama-3.1-8B up projection {mat.n}x{mat.k} bf16 hybrid S ({P0.layout.n_sparse}/"
+                       f"{P0.layout.tiles_n * P0.layout.tiles_k} tiles 2:4) + rank {rank} U V^T, M=1",
+           "rank": rank, "plain_us": round(us_plain, 3), "sparse_lowrank_us": round(us_two, 3),
+           "lowrank_kernel_us": round(us_fused, 3), "t_kernel_us_by_difference": round(us_two - us_fused, 3),
+           "overhead_vs_plain": round(us_two / us_plain, 4),
+           "alg_bytes": {"plain": b_plain, "sparse_lowrank": b_lr},
+           "GBps_plain": round(b_plain / (us_plain * 1e-6) / 1e9, 1),
+           "GBps_sparse_lowrank": round(b_lr / (us_two * 1e-6) / 1e9, 1),
+           "timing": f"graph burst of {reps} products over {n_copies} rotating copies, median of 5 replays"}
+    del Ps, Vs, Us
     torch.cuda.empty_cache()
     return out
 

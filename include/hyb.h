@@ -167,14 +167,30 @@ hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_
                             const void* x, int32_t m, int64_t ldx, void* const* y,
                             int32_t y_dtype, const int64_t* ldy, void* stream);
 
+/* Low-rank projection T = X V for a sparse + low-rank weight W ~ S + U V^T
+ * (3BASiL, gist.science, section 1 "Il Problema": a sparse part plus a
+ * rank-r part), U n x r and V k x r: the first of the two products of the
+ * low-rank term X (U V^T)^T = (X V) U^T.  Any m >= 0.
+ *   v      device, V stored transposed: rank rows of k values of `dtype`,
+ *          row j (column j of V) at v + j * ldv; ldv >= k, ldv % 8 == 0,
+ *          16-byte aligned
+ *   rank   0 <= rank <= HYB_MAX_RANK (0: no-op)
+ *   k      k >= 0, k % 8 == 0 (0: T is set to zero)
+ *   dtype  HYB_BF16 or HYB_F16, the type of v and x
+ *   x      device m x k, row stride ldx >= k, ldx % 8 == 0, 16-byte aligned
+ *   t      device fp32 output m x rank, row stride ldt >= rank
+ * Products are exact and summed in fp32 in a fixed order (the result is
+ * deterministic).  0 <= m <= 16 * 65535 (one launch). */
+hyb_status hyb_lowrank_project(const void* v, int64_t ldv, int32_t rank, int64_t k, int32_t dtype,
+                               const void* x, int32_t m, int64_t ldx, float* t, int64_t ldt,
+                               void* stream);
+
 /* Decode product of a sparse + low-rank weight, 0 <= m <= 16 tokens:
- * Y[i, :] = W' X[i, :] + U T[i, :], i.e. Y = X W'^T + T U^T.  The weight
- * is approximated as a sparse part plus a rank-r part, W ~ S + L (3BASiL,
- * gist.science, section 1 "Il Problema"; section 4 "Risultati
- * Sperimentali" uses 2:4 sparse + rank 64), with S packed here and
- * L = U V^T kept as its two factors.  T = X V^T (m x rank) is computed
- * beforehand, for instance with hyb_gemv on V (rank x k) packed with an
- * all-dense tile map; this call adds T U^T inside the decode kernel.
+ * Y[i, :] = W' X[i, :] + U T[i, :], i.e. Y = X W'^T + T U^T, the second
+ * product of X (S + U V^T)^T with S = W' packed here (3BASiL section 4
+ * "Risultati Sperimentali" pairs 2:4 sparsity with rank 64).  T = X V
+ * (m x rank) comes from hyb_lowrank_project; this call adds T U^T inside the
+ * decode kernel, after each row's sparse sum.
  *   layout, w, x, m, ldx, y, y_dtype, ldy  as for hyb_gemv
  *   t      device fp32, m x rank, row stride ldt >= rank, ldt % 4 == 0,
  *          16-byte aligned

@@ -26,8 +26,8 @@ MAX_GEMV_M = 16
 META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4}
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
-EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_gemv_lowrank",
-            "hyb_gemm", "hyb_gemm_mfma", "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
+            "hyb_gemv_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
 MAX_GROUP = 16
 MAX_RANK = 256
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.hyb_gemv_lowrank.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I64, P,
                                    I64, I32, P, I32, I64, P]
     L.hyb_gemv_lowrank.restype = I32
+    L.hyb_lowrank_project.argtypes = [P, I64, I32, I64, I32, P, I32, I64, P, I64, P]
+    L.hyb_lowrank_project.restype = I32
     L.hyb_stream_read.argtypes = [P, I64, P, I32, P]
     L.hyb_stream_read.restype = I32
     L.hyb_status_str.argtypes = [I32]
@@ -289,9 +291,33 @@ def gemv_grouped(Ps, x, out_dtype=None, outs=None):
     return outs
 
 
+def lowrank_project(v, x, out=None):
+    """T = X V (fp32, m x rank) for a low-rank factor V (k x rank) held
+    transposed: `v` is rank x k with unit column stride, of x's dtype."""
+    torch = _torch()
+    _check_rows(v, "v")
+    _check_rows(x, "x")
+    if v.dtype != x.dtype or v.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("v and x must share one dtype, bfloat16 or float16")
+    rank, k = v.shape
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x must have {k} columns")
+    if out is None:
+        out = torch.empty((m, rank), dtype=torch.float32, device=x.device)
+    elif out.shape != (m, rank) or out.dtype != torch.float32:
+        raise ValueError(f"out must be float32 {m} x {rank}")
+    code = HYB_BF16 if v.dtype == torch.bfloat16 else HYB_F16
+    st = lib().hyb_lowrank_project(_ptr(v), int(v.stride(0)) if v.numel() else int(k), int(rank), int(k), code,
+                                   _ptr(x), int(m), int(x.stride(0)) if x.numel() else int(k), _ptr(out),
+                                   int(out.stride(0)) if out.numel() else int(rank), _stream(x.device))
+    check(st, "hyb_lowrank_project")
+    return out
+
+
 def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
     """Decode product of a sparse + low-rank weight: Y = X W'^T + T U^T,
-    with t = X V^T (fp32, m x rank) given and u (n x rank, weight dtype)."""
+    with t = X V (fp32, m x rank) given and u (n x rank, weight dtype)."""
     torch = _torch()
     _check_rows(x, "x")
     _check_rows(t, "t")
@@ -316,11 +342,11 @@ def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
     return out
 
 
-def sparse_lowrank_gemv(P: PackedWeight, V: PackedWeight, u, x, out_dtype=None, out=None):
-    """Y = X (W' + U V^T)^T in two launches: T = X V^T with the decode
-    kernel on V (rank x k, packed with an all-dense map), then the sparse
-    product with T U^T added in the same kernel."""
-    t = gemv(V, x)
+def sparse_lowrank_gemv(P: PackedWeight, v, u, x, out_dtype=None, out=None, t=None):
+    """Y = X (W' + U V^T)^T in two launches: T = X V (hyb_lowrank_project,
+    v = V^T, rank x k), then the sparse product with T U^T added in the
+    decode kernel.  `t` optionally gives the m x rank fp32 buffer for T."""
+    t = lowrank_project(v, x, out=t)
     return gemv_lowrank(P, x, t, u, out_dtype, out)
 
 

@@ -257,6 +257,28 @@ hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_
                     "grouped gemv launch");
 }
 
+hyb_status hyb_lowrank_project(const void* v, int64_t ldv, int32_t rank, int64_t k, int32_t dtype,
+                               const void* x, int32_t m, int64_t ldx, float* t, int64_t ldt, void* stream) {
+  if (dtype != HYB_BF16 && dtype != HYB_F16) return fail(HYB_ERR_DTYPE, "dtype %d must be bf16 or f16", dtype);
+  if (rank < 0 || rank > hyb::kMaxRank) return fail(HYB_ERR_SHAPE, "rank = %d must be in [0, %d]", rank, hyb::kMaxRank);
+  if (k < 0 || k % 8 != 0) return fail(HYB_ERR_SHAPE, "k = %lld must be a non-negative multiple of 8", (long long)k);
+  if (m < 0 || m > 16 * 65535) return fail(HYB_ERR_SHAPE, "m = %d must be in [0, %d]", m, 16 * 65535);
+  if (rank == 0 || m == 0) return ok();
+  if (!t || !aligned(t, 4)) return fail(HYB_ERR_INVALID_ARG, "t is NULL or misaligned");
+  if (ldt < rank) return fail(HYB_ERR_INVALID_ARG, "t row stride %lld must be >= rank", (long long)ldt);
+  if (k > 0) {
+    if (!v || !aligned(v, 16)) return fail(HYB_ERR_INVALID_ARG, "v is NULL or not 16-byte aligned");
+    if (ldv < k || ldv % 8 != 0)
+      return fail(HYB_ERR_INVALID_ARG, "v row stride %lld must be >= k and a multiple of 8", (long long)ldv);
+    if (!x || !aligned(x, 16)) return fail(HYB_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+    if (ldx < k || ldx % 8 != 0)
+      return fail(HYB_ERR_INVALID_ARG, "x row stride %lld must be >= k and a multiple of 8", (long long)ldx);
+  }
+  return hip_status(hyb::launch_lr_project(v, ldv, rank, k, dtype, x, m, ldx, t, ldt,
+                                           static_cast<hipStream_t>(stream)),
+                    "low-rank projection launch");
+}
+
 hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                             int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
                             void* y, int32_t y_dtype, int64_t ldy, void* stream) {

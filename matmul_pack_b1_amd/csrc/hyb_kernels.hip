@@ -1405,6 +1405,53 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
   }
 }
 
+// ---------------------------------------------------- low-rank project ----
+//
+// T = X V for the low-rank factor of a sparse + low-rank weight, V held as
+// rank rows of k values (row j is column j of V).  One workgroup per V row
+// and block of MT tokens: each thread takes 8-element slices of K at a
+// stride of 8 * 256, two products per v_dot2, then the 256 partial sums are
+// reduced across the wavefront and, in a fixed order, across the four
+// wavefronts.  V is read once per token block; the x rows come from L2.
+template <int DT, int MT>
+__global__ __launch_bounds__(256) void k_lr_project(const uint16_t* __restrict__ v, int64_t ldv, int64_t k,
+                                                    const uint16_t* __restrict__ x, int32_t m, int64_t ldx,
+                                                    float* __restrict__ t, int64_t ldt) {
+  __shared__ float part[4][MT];
+  const int tid = threadIdx.x;
+  const int64_t j = blockIdx.x;
+  const int32_t m0 = int32_t(blockIdx.y) * MT;
+  const int32_t mc = m - m0 < MT ? m - m0 : MT;
+  const uint16_t* vr = v + j * ldv;
+  float acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = 0.f;
+  for (int64_t kk = int64_t(tid) * 8; kk < k; kk += 256 * 8) {
+    const uint4 a = *reinterpret_cast<const uint4*>(vr + kk);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i < mc) {
+        const uint4 b = *reinterpret_cast<const uint4*>(x + int64_t(m0 + i) * ldx + kk);
+        acc[i] = dot2<DT>(a.x, b.x, acc[i]);
+        acc[i] = dot2<DT>(a.y, b.y, acc[i]);
+        acc[i] = dot2<DT>(a.z, b.z, acc[i]);
+        acc[i] = dot2<DT>(a.w, b.w, acc[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc[i] += __shfl_xor(acc[i], o, 64);
+  }
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) part[tid >> 6][i] = acc[i];
+  }
+  __syncthreads();
+  if (tid < mc) t[int64_t(m0 + tid) * ldt + j] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+}
+
 // --------------------------------------------------------- stream read ----
 //
 // Practical read-rate reference: each wavefront reads four contiguous 1 KiB
@@ -1431,6 +1478,31 @@ __global__ __launch_bounds__(256) void k_stream_read(const char* __restrict__ p,
 }
 
 }  // namespace
+
+namespace {
+
+template <int DT>
+void lr_project_mt(int m, dim3 grid, hipStream_t s, const uint16_t* v, int64_t ldv, int64_t k,
+                   const uint16_t* x, int64_t ldx, float* t, int64_t ldt) {
+  if (m <= 1) hipLaunchKernelGGL((k_lr_project<DT, 1>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else if (m <= 2) hipLaunchKernelGGL((k_lr_project<DT, 2>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else if (m <= 4) hipLaunchKernelGGL((k_lr_project<DT, 4>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else if (m <= 8) hipLaunchKernelGGL((k_lr_project<DT, 8>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else hipLaunchKernelGGL((k_lr_project<DT, 16>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
+}
+
+}  // namespace
+
+hipError_t launch_lr_project(const void* v, int64_t ldv, int rank, int64_t k, int dtype, const void* x, int m,
+                             int64_t ldx, float* t, int64_t ldt, hipStream_t s) {
+  const int mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
+  const dim3 grid(static_cast<unsigned>(rank), static_cast<unsigned>((m + mt - 1) / mt));
+  const auto* vv = static_cast<const uint16_t*>(v);
+  const auto* xx = static_cast<const uint16_t*>(x);
+  if (dtype == HYB_BF16) lr_project_mt<HYB_BF16>(m, grid, s, vv, ldv, k, xx, ldx, t, ldt);
+  else lr_project_mt<HYB_F16>(m, grid, s, vv, ldv, k, xx, ldx, t, ldt);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
   hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, s, static_cast<const char*>(p), bytes, sink);

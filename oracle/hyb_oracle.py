@@ -35,8 +35,9 @@ Readings where the pages are silent (each also listed in the design notes):
   R6 dropped positions unpack to +0.0 (bit pattern 0x0000);
   R7 the stream layout below (format "HYB1");
   R8 ragged shapes (n % b1 or k % b2 non-zero) are rejected;
-  R13 sparse + low-rank: L = U V^T is held as its two factors and T = X V^T
-      is computed before the product (ref_lowrank).
+  R13 sparse + low-rank: L = U V^T (U n x r, V k x r) is held as its two
+      factors and T = X V is computed before the product (ref_lowrank; T
+      itself is ref_matmul of V^T and X).
 
 Format HYB1 (all element indices count 16-bit words):
   tile t = tn * TK + tk, TN = n / b1, TK = k / b2, tile_map[tn, tk] in {0, 1};
@@ -299,7 +300,8 @@ def ref_lowrank(wp_bits, x_bits, t, u_bits, dtype: str) -> tuple[np.ndarray, np.
     """Sparse + low-rank product (3BASiL, gist.science, section 1 "Il
     Problema": W ~ S + L with L of rank r; section 4 "Risultati
     Sperimentali": 2:4 sparse + rank 64).  With S = W' (the hybrid weight)
-    and L = U V^T held as its factors, and T = X V^T given (float32, m x r):
+    and L = U V^T held as its factors (U n x r, V k x r), and T = X V
+    given (float32, m x r):
 
         y_ref[m, n] = sum_k W'[n, k] X[m, k] + sum_j T[m, j] U[n, j]
         s[m, n]     = sum_k |W'[n, k] X[m, k]| + sum_j |T[m, j] U[n, j]|

@@ -188,6 +188,30 @@ def test_gemv_grouped_rejects(L):
     assert _grouped(L, 2, [lay, lay], m=0) == 0                    # m == 0: no-op
 
 
+def test_lowrank_project_rejects(L):
+    def call(v=FAKE, ldv=4096, rank=64, k=4096, dtype=hb.HYB_BF16, x=FAKE, m=1, ldx=4096, t=FAKE, ldt=64):
+        return L.hyb_lowrank_project(v, ldv, rank, k, dtype, x, m, ldx, t, ldt, None)
+    assert call(dtype=hb.HYB_F32) == 3
+    assert call(rank=-1) == 2
+    assert call(rank=hb.MAX_RANK + 1) == 2
+    assert call(k=-8) == 2
+    assert call(k=4100) == 2                        # k % 8
+    assert call(m=-1) == 2
+    assert call(m=16 * 65535 + 1) == 2
+    assert call(t=None) == 1
+    assert call(ldt=63) == 1
+    assert call(v=None) == 1
+    assert call(v=FAKE + 8) == 1                    # v alignment
+    assert call(ldv=4088) == 1                      # ldv < k
+    assert call(ldv=4100) == 1                      # ldv % 8
+    assert call(x=None) == 1
+    assert call(x=FAKE + 2) == 1
+    assert call(ldx=4092) == 1
+    assert call(rank=0) == 0                        # no-op
+    assert call(m=0) == 0                           # no-op
+    assert call(rank=0, t=None, v=None, x=None) == 0
+
+
 def test_gemv_lowrank_rejects(L):
     lay = _good_layout()
     P = hb.HybPacked(FAKE, FAKE, FAKE, FAKE)

@@ -258,11 +258,50 @@ def test_gemv_lowrank(rank, m, b1, b2, dtype, meta):
     assert_close(y.cpu().numpy(), yref, s, what="gemv lowrank")
 
 
+@pytest.mark.parametrize("rank,k,m,dtype", [(64, 4096, 1, "bf16"), (64, 4096, 16, "bf16"), (1, 72, 3, "f16"),
+                                             (256, 5120, 40, "bf16"), (8, 2056, 17, "f16")])
+def test_lowrank_project(rank, k, m, dtype):
+    """T = X V (V held transposed, rank x k) against the oracle's product,
+    over token blocks of 16 with a ragged last block and K tails that do
+    not fill a stride of 2048; bitwise repeatable."""
+    torch = _torch()
+    note(f"lowrank project r={rank} k={k} m={m} {dtype}")
+    rng = np.random.default_rng(rank + k + m)
+    v = wl.float32_to_bits(rng.standard_normal((rank, k)).astype(np.float32) * 0.05, dtype)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), dtype)
+    vt, xt = upload(v, dtype), upload(x, dtype)
+    t = hb.lowrank_project(vt, xt)
+    t2 = hb.lowrank_project(vt, xt)
+    torch.cuda.synchronize()
+    assert torch.equal(t, t2)
+    tref, s = oracle.ref_matmul(v, x, dtype)
+    assert_close(t.cpu().numpy(), tref, s, what="lowrank project")
+
+
+def test_lowrank_project_strided_and_empty():
+    """Row strides above k for v, x and t; k = 0 gives T = 0."""
+    torch = _torch()
+    note("lowrank project strided / k = 0")
+    rng = np.random.default_rng(5)
+    rank, k, m = 24, 256, 5
+    v = wl.float32_to_bits(rng.standard_normal((rank, k + 40)).astype(np.float32), "bf16")
+    x = wl.float32_to_bits(rng.standard_normal((m, k + 16)).astype(np.float32), "bf16")
+    tbuf = torch.full((m, rank + 8), 7.0, dtype=torch.float32, device=dev())
+    hb.lowrank_project(upload(v, "bf16")[:, :k], upload(x, "bf16")[:, :k], out=tbuf[:, :rank])
+    got = tbuf.cpu().numpy()
+    tref, s = oracle.ref_matmul(v[:, :k], x[:, :k], "bf16")
+    assert_close(got[:, :rank], tref, s, what="strided project")
+    assert (got[:, rank:] == 7.0).all()
+    z = hb.lowrank_project(torch.empty((rank, 0), dtype=torch.bfloat16, device=dev()),
+                           torch.empty((m, 0), dtype=torch.bfloat16, device=dev()))
+    assert z.shape == (m, rank) and (z.cpu() == 0).all()
+
+
 def test_sparse_lowrank_end_to_end():
-    """Two launches on the 8B up projection shape: T = X V^T with the decode
-    kernel on V (64 x 4096, packed all-dense), then the hybrid product with
-    T U^T added (2:4 sparse + rank 64).  The oracle computes T itself; its
-    error bound adds T's own bound carried through |U|."""
+    """Two launches on the 8B up projection shape: T = X V with the
+    projection kernel, then the hybrid product with T U^T added (2:4 sparse +
+    rank 64).  The oracle computes T itself; its error bound adds T's own
+    bound carried through |U|."""
     torch = _torch()
     note("sparse + low-rank end to end")
     mat, w, tmap = workload_matrix(2, 0)
@@ -272,8 +311,7 @@ def test_sparse_lowrank_end_to_end():
     u = wl.float32_to_bits(rng.standard_normal((mat.n, rank)).astype(np.float32) * 0.02, "bf16")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    V = pack_gpu(v, np.zeros((1, mat.k // 64), np.uint8), 64, 64, "bf16", "idx2")
-    y = hb.sparse_lowrank_gemv(P, V, upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
+    y = hb.sparse_lowrank_gemv(P, upload(v, "bf16"), upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
     t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
     tile_rows = sample_tile_rows(mat, 4, 7)
     rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
