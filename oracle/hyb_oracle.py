@@ -35,6 +35,12 @@ Readings where the pages are silent (each also listed in the design notes):
   R6 dropped positions unpack to +0.0 (bit pattern 0x0000);
   R7 the stream layout below (format "HYB1");
   R8 ragged shapes (n % b1 or k % b2 non-zero) are rejected;
+  R14 4:8 tiles (metadata kind "mask8"): PATCH section 5 "Significato"
+      names 4:8 as the next N:M pattern and SparseDecoding's kernel serves
+      N:M with bitmask indices.  Groups of eight aligned columns keep their
+      four largest keys (R2's key and tie rule), stored in ascending
+      position order, with an 8-bit mask (bit p set = position p kept).  A
+      4:8 tile has the same byte counts as a 2:4 tile;
   R13 sparse + low-rank: L = U V^T (U n x r, V k x r) is held as its two
       factors and T = X V is computed before the product (ref_lowrank; T
       itself is ref_matmul of V^T and X).
@@ -51,13 +57,19 @@ Format HYB1 (all element indices count 16-bit words):
   Metadata (16-bit little-endian words), nibble of (s, r, g) sits in word
       s*b1*b2/16 + (r//16)*b2 + (((g%16)//4)*16 + r%16)*(b2//64) + g//16
   at bits 4*(g%4) .. 4*(g%4)+3.
+  4:8 (mask8) sparse slot s, row r, group h (columns 8h..8h+7), kept value
+  j in {0, 1, 2, 3}:
+      s*b1*b2/2 + (r//16)*8*b2 + (h//8)*512 + ((h%8)//2)*128 + (r%16)*8
+      + (h%2)*4 + j
+  and its mask byte sits in the word of the 2:4 group g = 2h, at bits
+  8*(h%2) .. 8*(h%2)+7 (the same 16 columns per lane and word as 2:4).
   Requires b1 % 16 == 0 and b2 % 64 == 0.
 """
 from __future__ import annotations
 
 import numpy as np
 
-META_KINDS = ("idx2", "mask4")
+META_KINDS = ("idx2", "mask4", "mask8")
 DTYPES = ("bf16", "f16")
 
 # The six two-of-four patterns (PATCH section 2, "Distribuzioni Apprendibili"),
@@ -100,6 +112,48 @@ def kept_positions(group_bits) -> tuple[np.ndarray, np.ndarray]:
     order = np.argsort(-rank_score, axis=-1, kind="stable")
     first, second = order[..., 0], order[..., 1]
     return np.minimum(first, second), np.maximum(first, second)
+
+
+def group_shape(meta: str) -> tuple[int, int]:
+    """(kept, group size) of a sparse tile's groups: 2:4 for idx2 and mask4,
+    4:8 for mask8 (R14)."""
+    if meta in ("idx2", "mask4"):
+        return 2, 4
+    if meta == "mask8":
+        return 4, 8
+    raise ValueError(f"unknown metadata kind {meta!r}")
+
+
+def kept_positions_nm(group_bits, keep: int) -> np.ndarray:
+    """Ascending positions of the `keep` entries kept in each group.
+
+    group_bits: uint16 array of shape (..., size).  The same rule as the
+    2:4 case (R2): rank by magnitude key, larger first, equal keys by lower
+    position; the first `keep` of the ranking are kept.  Returns int64
+    (..., keep)."""
+    g = np.asarray(group_bits, dtype=np.uint16)
+    size = g.shape[-1]
+    key = magnitude_key(g).astype(np.int64)
+    pos = np.arange(size, dtype=np.int64)
+    rank_score = key * size + (size - 1 - pos)
+    order = np.argsort(-rank_score, axis=-1, kind="stable")
+    return np.sort(order[..., :keep], axis=-1)
+
+
+def mask8(positions) -> np.ndarray:
+    """R14: 8-bit mask of a 4:8 group with kept positions (..., 4)."""
+    p = np.asarray(positions, dtype=np.int64)
+    return np.bitwise_or.reduce(np.left_shift(1, p), axis=-1).astype(np.uint8)
+
+
+def positions_from_mask8(mask) -> np.ndarray:
+    """Inverse of `mask8`; raises ValueError unless exactly four bits are set."""
+    m = np.asarray(mask, dtype=np.int64)
+    bits = (m[..., None] >> np.arange(8)) & 1
+    if np.any(bits.sum(axis=-1) != 4):
+        bad = np.unique(m[bits.sum(axis=-1) != 4])
+        raise ValueError(f"invalid mask8 bytes: {bad.tolist()}")
+    return np.argsort(1 - bits, axis=-1, kind="stable")[..., :4]
 
 
 def nibble(i0, i1, meta: str) -> np.ndarray:
@@ -169,14 +223,16 @@ def _tile(w, tn, tk, b1, b2):
     return w[tn * b1:(tn + 1) * b1, tk * b2:(tk + 1) * b2]
 
 
-def prune(w_bits, tile_map, b1: int, b2: int) -> np.ndarray:
+def prune(w_bits, tile_map, b1: int, b2: int, meta: str = "idx2") -> np.ndarray:
     """W' = the tile-hybrid pruned weight, as uint16 bit patterns.
 
     Dense tiles are copied unchanged; in a sparse tile every row's aligned
     groups of four columns keep their two largest-magnitude entries and the
     other two become +0.0 (PATCH section 2 "Meccanismo Principale" and
-    "Distribuzioni Apprendibili"; readings R1, R2, R6).
+    "Distribuzioni Apprendibili"; readings R1, R2, R6).  With meta "mask8"
+    the groups are eight columns and keep four (R14).
     """
+    keep, size = group_shape(meta)
     w = np.asarray(w_bits, dtype=np.uint16)
     n, k = w.shape
     tn_count, tk_count = check_shape(n, k, b1, b2)
@@ -186,11 +242,11 @@ def prune(w_bits, tile_map, b1: int, b2: int) -> np.ndarray:
         for tk in range(tk_count):
             if not tmap[tn, tk]:
                 continue
-            groups = _tile(w, tn, tk, b1, b2).reshape(b1, b2 // 4, 4)
-            i0, i1 = kept_positions(groups)
-            pos = np.arange(4)
-            keep = (pos == i0[..., None]) | (pos == i1[..., None])
-            pruned = np.where(keep, groups, np.uint16(0)).reshape(b1, b2)
+            groups = _tile(w, tn, tk, b1, b2).reshape(b1, b2 // size, size)
+            kept = kept_positions_nm(groups, keep)
+            pos = np.arange(size)
+            keepm = (pos[None, None, :, None] == kept[..., None, :]).any(axis=-1)
+            pruned = np.where(keepm, groups, np.uint16(0)).reshape(b1, b2)
             _tile(out, tn, tk, b1, b2)[...] = pruned
     return out
 
@@ -207,6 +263,11 @@ def value_index(s, r, g, j, b1: int, b2: int):
             + ((g % 16) // 4) * 128 + (r % 16) * 8 + (g % 4) * 2 + j)
 
 
+def value_index8(s, r, h, j, b1: int, b2: int):
+    return (s * (b1 * b2 // 2) + (r // 16) * 8 * b2 + (h // 8) * 512
+            + ((h % 8) // 2) * 128 + (r % 16) * 8 + (h % 2) * 4 + j)
+
+
 def meta_word_index(s, r, g, b1: int, b2: int):
     return (s * (b1 * b2 // 16) + (r // 16) * b2
             + (((g % 16) // 4) * 16 + r % 16) * (b2 // 64) + g // 16)
@@ -219,7 +280,8 @@ def pack(w_bits, tile_map, b1: int, b2: int, meta: str) -> dict:
     16-bit words), tidx=int32[], plan=...).  Dense tiles are copied; for each
     sparse group the two kept values are stored in ascending position order
     with their nibble (SparseDecoding abstract: bitmask indexing, fixed
-    stride; readings R3-R5, R7).
+    stride; readings R3-R5, R7).  With meta "mask8" each group of eight
+    stores its four kept values and a mask byte (R14).
     """
     if meta not in META_KINDS:
         raise ValueError(f"unknown metadata kind {meta!r}")
@@ -240,6 +302,15 @@ def pack(w_bits, tile_map, b1: int, b2: int, meta: str) -> dict:
             dense[dense_index(int(ti), r, c, b1, b2)] = tile
             continue
         s = int(~ti)
+        if meta == "mask8":
+            groups8 = tile.reshape(b1, b2 // 8, 8)
+            kept = kept_positions_nm(groups8, 4)
+            h = np.arange(b2 // 8)[None, :]
+            for j in range(4):
+                val[value_index8(s, r, h, j, b1, b2)] = np.take_along_axis(groups8, kept[..., j:j + 1], axis=-1)[..., 0]
+            byte = mask8(kept).astype(np.uint16) << (8 * (h % 2)).astype(np.uint16)
+            np.bitwise_or.at(words, meta_word_index(s, r, 2 * h, b1, b2), byte)
+            continue
         groups = tile.reshape(b1, b2 // 4, 4)
         i0, i1 = kept_positions(groups)
         v0 = np.take_along_axis(groups, i0[..., None], axis=-1)[..., 0]
@@ -254,7 +325,8 @@ def pack(w_bits, tile_map, b1: int, b2: int, meta: str) -> dict:
 
 def unpack(dense, val, meta_bytes, tidx, n: int, k: int, b1: int, b2: int, meta: str) -> np.ndarray:
     """W' from the compressed streams: dense tiles gathered back, sparse
-    groups rebuilt from their two values and nibble, +0.0 elsewhere (R6)."""
+    groups rebuilt from their two values and nibble (four values and mask
+    byte for mask8), +0.0 elsewhere (R6)."""
     tn_count, tk_count = check_shape(n, k, b1, b2)
     tidx = np.asarray(tidx, dtype=np.int32).reshape(-1)
     if tidx.size != tn_count * tk_count:
@@ -273,6 +345,16 @@ def unpack(dense, val, meta_bytes, tidx, n: int, k: int, b1: int, b2: int, meta:
             dst[...] = dense[dense_index(int(ti), r, c, b1, b2)]
             continue
         s = int(~ti)
+        if meta == "mask8":
+            h = np.arange(b2 // 8)[None, :]
+            byte = (words[meta_word_index(s, r, 2 * h, b1, b2)] >> (8 * (h % 2)).astype(np.uint16)) & 0xFF
+            kept = positions_from_mask8(byte)
+            groups8 = np.zeros((b1, b2 // 8, 8), dtype=np.uint16)
+            for j in range(4):
+                np.put_along_axis(groups8, kept[..., j:j + 1], val[value_index8(s, r, h, j, b1, b2)][..., None],
+                                  axis=-1)
+            dst[...] = groups8.reshape(b1, b2)
+            continue
         nib = (words[meta_word_index(s, r, g, b1, b2)] >> (4 * (g % 4)).astype(np.uint16)) & 0xF
         i0, i1 = positions_from_nibble(nib, meta)
         v0 = val[value_index(s, r, g, 0, b1, b2)]

@@ -72,7 +72,7 @@ def _ref_signed_bound(wp_bits, x_bits, dtype):
     return x @ w.T, np.abs(x @ w.T)
 
 
-def _prune_keeps_three(w_bits, tile_map, b1, b2):
+def _prune_keeps_three(w_bits, tile_map, b1, b2, meta="idx2"):
     w = np.asarray(w_bits, dtype=np.uint16)
     n, k = w.shape
     tn_count, tk_count = ho.check_shape(n, k, b1, b2)
@@ -120,6 +120,8 @@ def test_prune_mutation_caught(monkeypatch):
     monkeypatch.setattr(oracle, "prune", _prune_keeps_three)
     with pytest.raises(FAIL):
         pins.test_invariants(3, "idx2")
+    with pytest.raises(FAIL):
+        pins.test_invariants(3, "mask8")
 
 
 def _lowrank_u_transposed(wp_bits, x_bits, t, u_bits, dtype):
@@ -160,3 +162,66 @@ def test_lowrank_mutations_caught(monkeypatch, golden_dir, func):
         except FAIL:
             caught += 1
     assert caught >= 1
+
+
+# ------------------------------------------------------------------ 4:8 ----
+
+def _kept_nm_ties_high(group_bits, keep):
+    g = np.asarray(group_bits, dtype=np.uint16)
+    size = g.shape[-1]
+    key = (g & 0x7FFF).astype(np.int64)
+    order = np.argsort(-(key * size + np.arange(size)), axis=-1, kind="stable")
+    return np.sort(order[..., :keep], axis=-1)
+
+
+def _kept_nm_per_half(group_bits, keep):
+    """Top keep/2 of each half instead of top keep of the whole group."""
+    g = np.asarray(group_bits, dtype=np.uint16)
+    size = g.shape[-1]
+    h = size // 2
+    key = (g & 0x7FFF).astype(np.int64)
+    out = []
+    for lo in (0, h):
+        k = key[..., lo:lo + h]
+        order = np.argsort(-(k * h + (h - 1 - np.arange(h))), axis=-1, kind="stable")
+        out.append(order[..., :keep // 2] + lo)
+    return np.sort(np.concatenate(out, axis=-1), axis=-1)
+
+
+def _mask8_reversed(positions):
+    p = np.asarray(positions, dtype=np.int64)
+    return np.bitwise_or.reduce(np.left_shift(1, 7 - p), axis=-1).astype(np.uint8)
+
+
+def _value_index8_reversed(s, r, h, j, b1, b2):
+    return (s * (b1 * b2 // 2) + (r // 16) * 8 * b2 + (h // 8) * 512
+            + ((h % 8) // 2) * 128 + (r % 16) * 8 + (h % 2) * 4 + (3 - j))
+
+
+def _value_index8_groups_swapped(s, r, h, j, b1, b2):
+    return (s * (b1 * b2 // 2) + (r // 16) * 8 * b2 + (h // 8) * 512
+            + ((h % 8) // 2) * 128 + (r % 16) * 8 + (1 - h % 2) * 4 + j)
+
+
+@pytest.mark.parametrize("name,func", [("kept_positions_nm", _kept_nm_ties_high),
+                                       ("kept_positions_nm", _kept_nm_per_half),
+                                       ("mask8", _mask8_reversed)])
+def test_4of8_rule_mutations_caught(monkeypatch, golden_dir, name, func):
+    monkeypatch.setattr(ho, name, func)
+    monkeypatch.setattr(oracle, name, func)
+    with pytest.raises(FAIL):
+        pins.test_golden_groups_4of8(golden_dir)
+
+
+@pytest.mark.parametrize("func", [_value_index8_reversed, _value_index8_groups_swapped])
+def test_4of8_layout_mutations_caught(monkeypatch, func):
+    monkeypatch.setattr(ho, "value_index8", func)
+    with pytest.raises(FAIL):
+        pins.test_layout_restatement(32, 128, "mask8")
+
+
+def test_4of8_per_half_rule_caught_by_magnitude_pin(monkeypatch):
+    monkeypatch.setattr(ho, "kept_positions_nm", _kept_nm_per_half)
+    monkeypatch.setattr(oracle, "kept_positions_nm", _kept_nm_per_half)
+    with pytest.raises(FAIL):
+        pins.test_4of8_keeps_at_least_the_2of4_magnitude()

@@ -1,7 +1,8 @@
 """Pins of the CPU oracle against facts fixed outside the oracle itself:
 hand-derived group cases (tests/golden), an exhaustive brute force of the
 kept-pair rule, a restatement of the HYB1 stream layout in lane/chunk terms,
-exact matmul closed forms, math.fsum brute force, and the invariants the pages
+exact matmul closed forms, math.fsum brute force, the same for the 4:8 groups
+(PATCH section 5 "Significato"), and the invariants the pages
 state (PATCH section 2: dense tiles untouched, sparse tiles exactly half kept,
 six patterns; SparseDecoding abstract: fixed stride, bitmask metadata)."""
 import itertools
@@ -78,7 +79,7 @@ def test_six_patterns_and_bijection():
     assert mask4 == {0x3, 0x5, 0x9, 0x6, 0xA, 0xC}
     for m in mask4:
         assert bin(m).count("1") == 2
-    for kind in oracle.META_KINDS:
+    for kind in ("idx2", "mask4"):
         for nib in range(16):
             valid = nib in (idx2 if kind == "idx2" else mask4)
             if valid:
@@ -87,6 +88,92 @@ def test_six_patterns_and_bijection():
             else:
                 with pytest.raises(ValueError):
                     oracle.positions_from_nibble(np.array([nib]), kind)
+
+
+def load_golden_groups8(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "groups_4of8.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            bits = [int(h, 16) for h in parts[1:9]]
+            kept = [int(v) for v in parts[9:13]]
+            mask = int(parts[13], 16)
+            stored = [int(h, 16) for h in parts[14:18]]
+            rows.append((parts[0], bits, kept, mask, stored))
+    return rows
+
+
+def test_golden_groups_4of8(golden_dir):
+    """Kept positions, mask byte and stored values of hand-derived 4:8 groups,
+    the stored values read back through a one-row pack (row 0, group 0 of a
+    16 x 64 tile whose other entries are zero)."""
+    rows = load_golden_groups8(golden_dir)
+    assert len(rows) >= 20
+    for dtype, bits, kept, mask, stored in rows:
+        got = oracle.kept_positions_nm(np.array(bits, dtype=np.uint16), 4)
+        assert got.tolist() == kept, (dtype, [hex(x) for x in bits])
+        assert int(oracle.mask8(got)) == mask
+        assert oracle.positions_from_mask8(np.array([mask]))[0].tolist() == kept
+        w = np.zeros((16, 64), dtype=np.uint16)
+        w[0, :8] = bits
+        P = oracle.pack(w, np.ones((1, 1), np.uint8), 16, 64, "mask8")
+        vals = [int(P["val"][oracle.value_index8(0, 0, 0, j, 16, 64)]) for j in range(4)]
+        assert vals == stored, (dtype, [hex(x) for x in bits])
+        assert int(P["meta"].view("<u2")[oracle.meta_word_index(0, 0, 0, 16, 64)]) & 0xFF == mask
+        wp = oracle.prune(w, np.ones((1, 1), np.uint8), 16, 64, "mask8")
+        expect = [b if p in kept else 0 for p, b in enumerate(bits)]
+        assert wp[0, :8].tolist() == expect
+
+
+def test_kept_four_rule_brute_force():
+    """All 4^8 groups over alphabets with ties, +-0, subnormals, +-Inf and
+    NaN: the four kept positions equal a float-magnitude sort (lower position
+    first among equals), computed from widened values."""
+    for dtype, alphabet in (
+        ("bf16", [0x8000, 0x0001, 0xBF80, 0x7F80]),
+        ("f16", [0x0000, 0x03FF, 0x3C00, 0x7E00]),
+    ):
+        groups = np.array(list(itertools.product(alphabet, repeat=8)), dtype=np.uint16)
+        kept = oracle.kept_positions_nm(groups, 4)
+        ranks = {x: _float_magnitude_rank(x, dtype) for x in alphabet}
+        for g, kk in zip(groups.tolist(), kept.tolist()):
+            order = sorted(range(8), key=lambda p: (tuple(-v for v in ranks[g[p]]), p))
+            assert kk == sorted(order[:4]), (dtype, [hex(x) for x in g])
+
+
+def test_mask8_bytes():
+    """70 valid mask bytes (four of eight bits set), each the inverse of its
+    positions; every other byte is rejected."""
+    valid = {int(oracle.mask8(np.array(c))) for c in itertools.combinations(range(8), 4)}
+    assert len(valid) == 70
+    for b in range(256):
+        if bin(b).count("1") == 4:
+            p = oracle.positions_from_mask8(np.array([b]))[0]
+            assert int(oracle.mask8(p)) == b and b in valid
+        else:
+            with pytest.raises(ValueError):
+                oracle.positions_from_mask8(np.array([b]))
+
+
+def test_4of8_keeps_at_least_the_2of4_magnitude():
+    """The kept four maximise the summed magnitude over all 4-subsets of the
+    group (brute force over the 70 subsets), hence never keep less than the
+    two 2:4 halves do."""
+    rng = np.random.default_rng(48)
+    w = wl.float32_to_bits(rng.standard_normal((400, 8)).astype(np.float32), "bf16")
+    mag = np.abs(oracle.widen(w, "bf16"))
+    k48 = oracle.kept_positions_nm(w, 4)
+    s48 = np.take_along_axis(mag, k48, axis=-1).sum(axis=-1)
+    best = np.max([mag[:, list(c)].sum(axis=-1) for c in itertools.combinations(range(8), 4)], axis=0)
+    np.testing.assert_array_equal(s48, best)
+    a0, a1 = oracle.kept_positions(w[:, :4])
+    b0, b1 = oracle.kept_positions(w[:, 4:])
+    r = np.arange(len(w))
+    s24 = mag[r, a0] + mag[r, a1] + mag[r, 4 + b0] + mag[r, 4 + b1]
+    assert np.all(s48 >= s24)
 
 
 # ------------------------------------------------------ layout restatement --
@@ -103,7 +190,9 @@ def _layout_by_lanes(w, tile_map, b1, b2, meta):
       4*(L//16) .. +3 of the block, row L % 16, each group's pair in position
       order; the slab's metadata is 64 lanes x (b2/64) 16-bit words, lane L's
       words for blocks 0, 1, ... back to back, nibble q of a word for the
-      lane's q-th group."""
+      lane's q-th group.  With mask8 a lane holds the four kept values of
+      each of its two groups of eight, and byte hq of its word is the mask
+      of its hq-th group."""
     n, k = w.shape
     tn_count, tk_count = n // b1, k // b2
     dense, val, words, tidx = [], [], [], []
@@ -125,6 +214,17 @@ def _layout_by_lanes(w, tile_map, b1, b2, meta):
                 for blk in range(b2 // 64):
                     for lane in range(64):
                         row = slab * 16 + lane % 16
+                        if meta == "mask8":
+                            # two groups of eight: four values each, mask byte
+                            # hq of the word for the lane's group hq
+                            for hq in range(2):
+                                col = blk * 64 + 16 * (lane // 16) + 8 * hq
+                                grp = [int(v) for v in tile[row, col:col + 8]]
+                                order = sorted(range(8), key=lambda p: (-(grp[p] & 0x7FFF), p))
+                                top = sorted(order[:4])
+                                val.extend(grp[p] for p in top)
+                                lane_words[lane][blk] |= sum(1 << p for p in top) << (8 * hq)
+                            continue
                         for q in range(4):
                             col = blk * 64 + 16 * (lane // 16) + 4 * q
                             grp = [int(v) for v in tile[row, col:col + 4]]
@@ -140,7 +240,7 @@ def _layout_by_lanes(w, tile_map, b1, b2, meta):
 
 
 @pytest.mark.parametrize("b1,b2", [(16, 64), (32, 128), (16, 256)])
-@pytest.mark.parametrize("meta", ["idx2", "mask4"])
+@pytest.mark.parametrize("meta", ["idx2", "mask4", "mask8"])
 def test_layout_restatement(b1, b2, meta):
     rng = np.random.default_rng([b1, b2, len(meta)])
     n, k = 2 * b1, 2 * b2
@@ -187,11 +287,12 @@ def _random_case(seed, dtype="bf16"):
 
 
 @pytest.mark.parametrize("seed", range(12))
-@pytest.mark.parametrize("meta", ["idx2", "mask4"])
+@pytest.mark.parametrize("meta", ["idx2", "mask4", "mask8"])
 def test_invariants(seed, meta):
     w, tmap, b1, b2 = _random_case(seed, "bf16" if seed % 2 else "f16")
     n, k = w.shape
-    wp = oracle.prune(w, tmap, b1, b2)
+    keep, size = (4, 8) if meta == "mask8" else (2, 4)
+    wp = oracle.prune(w, tmap, b1, b2, meta)
     P = oracle.pack(w, tmap, b1, b2, meta)
     dropped = 0
     for tn in range(tmap.shape[0]):
@@ -201,16 +302,21 @@ def test_invariants(seed, meta):
             if not tmap[tn, tk]:
                 np.testing.assert_array_equal(src, dst)       # dense untouched
                 continue
-            gs = src.reshape(b1, b2 // 4, 4).astype(np.int64)
-            gd = dst.reshape(b1, b2 // 4, 4).astype(np.int64)
-            i0, i1 = oracle.kept_positions(gs.astype(np.uint16))
-            pos = np.arange(4)
-            kept = (pos == i0[..., None]) | (pos == i1[..., None])
+            gs = src.reshape(b1, b2 // size, size).astype(np.int64)
+            gd = dst.reshape(b1, b2 // size, size).astype(np.int64)
+            # kept = positions where the pruned group still holds the source
+            # bits and that are not among the dropped; dropped entries are +0
+            ks = gs & 0x7FFF
+            # rank each entry: number of entries that beat it (larger key, or
+            # equal key at a lower position)
+            beats = (ks[..., None, :] > ks[..., :, None]) | (
+                (ks[..., None, :] == ks[..., :, None]) & (np.arange(size)[None, :] < np.arange(size)[:, None]))
+            kept = beats.sum(axis=-1) < keep
+            assert np.all(kept.sum(axis=-1) == keep)
             assert np.all(gd[~kept] == 0)
             assert np.all(gd[kept] == gs[kept])
-            assert np.all(np.count_nonzero(gd & 0x7FFF, axis=-1) <= 2)
+            assert np.all(np.count_nonzero(gd & 0x7FFF, axis=-1) <= keep)
             # kept keys dominate dropped keys
-            ks = gs & 0x7FFF
             kmin_kept = np.where(kept, ks, 1 << 20).min(axis=-1)
             kmax_drop = np.where(~kept, ks, -1).max(axis=-1)
             assert np.all(kmin_kept >= kmax_drop)
@@ -218,7 +324,7 @@ def test_invariants(seed, meta):
     # overall sparsity counts dropped positions: half of each sparse tile
     assert dropped == int(tmap.sum()) * b1 * b2 // 2
     assert dropped / (n * k) == oracle.sparsity(tmap, b1, b2, n, k)
-    # byte totals
+    # byte totals (the same for 2:4 and 4:8)
     p = P["plan"]
     assert P["dense"].nbytes == p["n_dense"] * b1 * b2 * 2
     assert P["val"].nbytes == p["n_sparse"] * b1 * b2
@@ -229,11 +335,15 @@ def test_invariants(seed, meta):
     P2 = oracle.pack(u, tmap, b1, b2, meta)
     for key in ("dense", "val", "meta", "tidx"):
         np.testing.assert_array_equal(P2[key], P[key])
-    # all nibbles valid
+    # all metadata valid
     words = P["meta"].view("<u2")
-    for q in range(4):
-        nib = (words >> (4 * q)) & 0xF
-        oracle.positions_from_nibble(nib, meta)
+    if meta == "mask8":
+        for hq in range(2):
+            oracle.positions_from_mask8((words >> (8 * hq)) & 0xFF)
+    else:
+        for q in range(4):
+            nib = (words >> (4 * q)) & 0xF
+            oracle.positions_from_nibble(nib, meta)
 
 
 def test_idx2_mask4_same_values():
