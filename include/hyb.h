@@ -33,6 +33,16 @@
  *       s*b1*b2/16 + (r/16)*b2 + (((g%16)/4)*16 + r%16)*(b2/64) + g/16
  *       at bits 4*(g%4)..4*(g%4)+3;  HYB_META_IDX2: i0 | i1<<2,
  *       HYB_META_MASK4: 1<<i0 | 1<<i1  (i0 < i1 the kept columns).
+ *   4:8 tiles (HYB_META_MASK8).  PATCH section 5 "Significato" names 4:8
+ *   as the next N:M pattern for the same scheme, and SparseDecoding's kernel
+ *   reads N:M with bitmask indices.  Each aligned group of eight columns
+ *   keeps its four largest |w| (same key and tie rule); a sparse tile has
+ *   the same byte counts as a 2:4 one.
+ *   values slot s, row r, group h (columns 8h..8h+7), kept j = 0..3
+ *       (ascending column):  s*b1*b2/2 + (r/16)*8*b2 + (h/8)*512
+ *                 + ((h%8)/2)*128 + (r%16)*8 + (h%2)*4 + j
+ *   meta   the mask byte (bit p set = column 8h+p kept) sits in the word of
+ *       the 2:4 group g = 2h above, at bits 8*(h%2)..8*(h%2)+7.
  *   Every 1 KiB of the dense or value stream is one 16-row slab piece that a
  *   64-lane wavefront loads with one 16-byte load per lane.
  *
@@ -49,8 +59,9 @@
  *   - Entries of tidx that name a slot outside [0, n_dense) or
  *     [0, n_sparse) are not reported; the kernels skip such tiles (they add
  *     nothing and write nothing) so they never read outside the streams.
- *     Metadata nibbles outside the six valid codes give unspecified values
- *     for that group (never an out-of-bounds access).
+ *     Metadata nibbles outside the six valid codes (mask bytes without
+ *     exactly four bits set) give unspecified values for that group (never
+ *     an out-of-bounds access).
  */
 #ifndef HYB_H_
 #define HYB_H_
@@ -73,7 +84,8 @@ enum {
 };
 
 enum { HYB_F16 = 1, HYB_BF16 = 2, HYB_F32 = 3 };    /* element types */
-enum { HYB_META_IDX2 = 1, HYB_META_MASK4 = 2 };      /* metadata codes */
+enum { HYB_META_IDX2 = 1, HYB_META_MASK4 = 2,       /* metadata codes (2:4 tiles) */
+       HYB_META_MASK8 = 3 };                         /* 4:8 tiles, see above */
 
 #define HYB_MAGIC 0x31425948u /* "HYB1" little-endian */
 #define HYB_VERSION 1u
@@ -87,7 +99,7 @@ typedef struct {
   uint32_t magic, version; /* HYB_MAGIC, HYB_VERSION */
   int64_t n, k;            /* W is n x k (out_features x in_features) */
   int32_t b1, b2;          /* tile rows x tile columns */
-  int32_t dtype, meta;     /* HYB_F16 | HYB_BF16; HYB_META_IDX2 | HYB_META_MASK4 */
+  int32_t dtype, meta;     /* HYB_F16 | HYB_BF16; HYB_META_IDX2 | HYB_META_MASK4 | HYB_META_MASK8 */
   int64_t tiles_n, tiles_k, n_dense, n_sparse;
   int64_t dense_bytes, val_bytes, meta_bytes, tidx_bytes;
 } hyb_layout;

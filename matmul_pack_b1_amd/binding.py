@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(PKG_DIR, "libhyb.so")
 
 HYB_OK = 0
 HYB_F16, HYB_BF16, HYB_F32 = 1, 2, 3
-HYB_META_IDX2, HYB_META_MASK4 = 1, 2
+HYB_META_IDX2, HYB_META_MASK4, HYB_META_MASK8 = 1, 2, 3
 HYB_MAGIC = 0x31425948
 HYB_VERSION = 1
 MAX_GEMV_M = 16
 
-META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4}
+META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_MASK8}
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",

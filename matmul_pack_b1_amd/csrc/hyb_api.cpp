@@ -38,8 +38,8 @@ hyb_status check_geometry(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t 
                           int32_t meta) {
   if (dtype != HYB_F16 && dtype != HYB_BF16)
     return fail(HYB_ERR_DTYPE, "dtype %d is not HYB_F16 or HYB_BF16", dtype);
-  if (meta != HYB_META_IDX2 && meta != HYB_META_MASK4)
-    return fail(HYB_ERR_INVALID_ARG, "meta %d is not HYB_META_IDX2 or HYB_META_MASK4", meta);
+  if (meta != HYB_META_IDX2 && meta != HYB_META_MASK4 && meta != HYB_META_MASK8)
+    return fail(HYB_ERR_INVALID_ARG, "meta %d is not HYB_META_IDX2, HYB_META_MASK4 or HYB_META_MASK8", meta);
   if (b1 <= 0 || b2 <= 0 || b1 % 16 != 0 || b2 % 64 != 0)
     return fail(HYB_ERR_SHAPE, "tile %dx%d: need b1 %% 16 == 0 and b2 %% 64 == 0", b1, b2);
   if (n < 0 || k < 0) return fail(HYB_ERR_SHAPE, "negative shape %lldx%lld", (long long)n, (long long)k);

@@ -168,6 +168,67 @@ __device__ __forceinline__ uint32_t scatter_selector(uint32_t e, uint32_t i0, ui
   return s0 | (s1 << 16);
 }
 
+// 4:8 groups (metadata kind HYB_META_MASK8): eight aligned columns keep
+// four values, stored in ascending position as the 64-bit pair
+// {v3 v2 : v1 v0}, with a mask byte (bit p = position p kept).
+// Kept mask of eight 16-bit values: the same ranking as kept_mask (key
+// bits & 0x7FFF, larger first, ties to the lower position), first four kept.
+__device__ __forceinline__ uint32_t kept_mask8(const uint32_t (&e)[8]) {
+  uint32_t sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sc[i] = ((e[i] & 0x7FFFu) << 3) | uint32_t(7 - i);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r += (j != i && sc[j] > sc[i]) ? 1u : 0u;
+    mask |= (r < 4 ? 1u : 0u) << i;
+  }
+  return mask;
+}
+
+// v_perm selector that writes positions 2j and 2j+1 of a 4:8 group from its
+// stored pair: the value of rank r (number of kept positions below) for a
+// kept position, zero otherwise.  A mask without exactly four bits gives
+// unspecified values, never an out-of-range access.
+__device__ __forceinline__ uint32_t expand8_selector(uint32_t mask, int j) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = 2 * j + h;
+    const uint32_t r = __builtin_popcount(mask & ((1u << p) - 1u));
+    const uint32_t sel = ((mask >> p) & 1u) ? (0x0100u + 0x0202u * r) : 0x0C0Cu;
+    out |= sel << (16 * h);
+  }
+  return out;
+}
+
+// Selector table of every mask byte, one 16-byte entry (j = 0..3) per mask,
+// filled once per workgroup into LDS by its threads.
+__device__ __forceinline__ void fill_expand8_lut(uint4* lut) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x)
+    lut[i] = make_uint4(expand8_selector(i, 0), expand8_selector(i, 1), expand8_selector(i, 2),
+                        expand8_selector(i, 3));
+}
+
+// The sixteen columns of one lane's two 4:8 groups as eight dwords
+// (positions 2j, 2j+1 in dword j; group 1 in dwords 4..7), from the lane's
+// 16-byte value piece and its 16-bit metadata word.
+__device__ __forceinline__ void expand8_lane(const uint4* lut, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                             uint32_t word, uint32_t (&e)[8]) {
+  const uint4 s0 = lut[word & 0xFFu];
+  const uint4 s1 = lut[(word >> 8) & 0xFFu];
+  e[0] = __builtin_amdgcn_perm(v1, v0, s0.x);
+  e[1] = __builtin_amdgcn_perm(v1, v0, s0.y);
+  e[2] = __builtin_amdgcn_perm(v1, v0, s0.z);
+  e[3] = __builtin_amdgcn_perm(v1, v0, s0.w);
+  e[4] = __builtin_amdgcn_perm(v3, v2, s1.x);
+  e[5] = __builtin_amdgcn_perm(v3, v2, s1.y);
+  e[6] = __builtin_amdgcn_perm(v3, v2, s1.z);
+  e[7] = __builtin_amdgcn_perm(v3, v2, s1.w);
+}
+
 // ---------------------------------------------------------------- pack ----
 
 struct PackParams {
@@ -215,6 +276,32 @@ __global__ __launch_bounds__(256) void k_pack(PackParams p) {
     const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t outv[4];
     uint32_t word = 0;
+    if (p.meta_kind == HYB_META_MASK8) {
+      // two groups of eight: four kept values each, in ascending position
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t e[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          e[2 * i] = d[4 * h + i] & 0xFFFFu;
+          e[2 * i + 1] = d[4 * h + i] >> 16;
+        }
+        const uint32_t mask = kept_mask8(e);
+        uint32_t kv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t r = __builtin_popcount(mask & ((1u << i) - 1u));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) kv[t] = (((mask >> i) & 1u) && r == uint32_t(t)) ? e[i] : kv[t];
+        }
+        outv[2 * h] = kv[0] | (kv[1] << 16);
+        outv[2 * h + 1] = kv[2] | (kv[3] << 16);
+        word |= mask << (8 * h);
+      }
+      *reinterpret_cast<uint4*>(vdst + c * 512) = make_uint4(outv[0], outv[1], outv[2], outv[3]);
+      words[c] = word;
+      continue;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t lo = d[2 * q], hi = d[2 * q + 1];
@@ -274,6 +361,17 @@ __global__ __launch_bounds__(256) void k_unpack(PackParams p) {
     const uint32_t word = msrc[c];
     const uint32_t pv[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[8];
+    if (p.meta_kind == HYB_META_MASK8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[j] = __builtin_amdgcn_perm(v.y, v.x, expand8_selector(word & 0xFFu, j));
+        o[4 + j] = __builtin_amdgcn_perm(v.w, v.z, expand8_selector(word >> 8, j));
+      }
+      uint16_t* dst = wrow + c * 64 + (lane >> 4) * 16;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+      continue;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t i0, i1;
@@ -295,8 +393,9 @@ __global__ __launch_bounds__(256) void k_unpack(PackParams p) {
 // wavefront loads the slab piece (dense: b2/32 x 16 B per lane; sparse: b2/64
 // x 16 B of values plus b2/64 16-bit metadata words per lane) and this tile's
 // x columns (MT x b2), stages x in its own LDS region, and accumulates in
-// fp32 with v_dot2.  Sparse groups gather their two x values with one v_perm
-// each.  Loads run one tile ahead through a two-stage register ring (the
+// fp32 with v_dot2.  Sparse 2:4 groups gather their two x values with one
+// v_perm each; 4:8 groups are expanded to their eight columns with v_perm
+// selectors from a per-workgroup LDS table of all 256 mask bytes.  Loads run one tile ahead through a two-stage register ring (the
 // loop is unrolled by two so no in-flight register is ever copied).  Lanes
 // L, L^16, L^32, L^48 hold the same row and are combined with cross-lane
 // swizzles; the wavefronts are then summed in a fixed order through LDS, so
@@ -380,7 +479,8 @@ __device__ __forceinline__ void gemv_load(GemvStage<MT, B2>& st, int32_t ti, int
 
 template <int MT, int B2, int DT, int META>
 __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2>& st, int32_t ti, uint16_t* xs,
-                                             const GemvDims& d, int lane, float (&acc)[MT]) {
+                                             const uint4* lut8, const GemvDims& d, int lane,
+                                             float (&acc)[MT]) {
   const int q = lane >> 4;  // column group of the lane inside a chunk
   // Stage this tile's x columns in the wavefront's LDS region.  LDS
   // accesses of one wavefront complete in order, so no barrier is needed;
@@ -410,6 +510,34 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2>& st, int32_
     }
   } else {
     if (~ti >= d.n_sparse) return;
+    if constexpr (META == HYB_META_MASK8) {
+      // 4:8: expand the lane's two groups to their sixteen columns with the
+      // selector table, then the dense dot products
+#pragma unroll
+      for (int c = 0; c < B2 / 64; ++c) {
+        const uint4 w = st.w[c];
+        const uint32_t word = (st.mw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+        uint32_t e[8];
+        expand8_lane(lut8, w.x, w.y, w.z, w.w, word, e);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const uint16_t* xrow = xs + m * B2 + c * 64 + q * 16;
+          const uint4 xa = *reinterpret_cast<const uint4*>(xrow);
+          const uint4 xb = *reinterpret_cast<const uint4*>(xrow + 8);
+          float a = acc[m];
+          a = dot2<DT>(e[0], xa.x, a);
+          a = dot2<DT>(e[1], xa.y, a);
+          a = dot2<DT>(e[2], xa.z, a);
+          a = dot2<DT>(e[3], xa.w, a);
+          a = dot2<DT>(e[4], xb.x, a);
+          a = dot2<DT>(e[5], xb.y, a);
+          a = dot2<DT>(e[6], xb.z, a);
+          a = dot2<DT>(e[7], xb.w, a);
+          acc[m] = a;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < B2 / 64; ++c) {
       const uint4 w = st.w[c];
@@ -440,7 +568,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2>& st, int32_
 // The product of one 16-row slab (the whole work of one workgroup).  With
 // LR the slab also adds the low-rank term sum_j T[m][j] U[row][j] (3BASiL,
 // gist.science, section 1: W ~ S + L with L of rank r, here L = U V^T and
-// T = X V^T given): wavefront 0's lanes take row L%16 and every fourth
+// T = X V given): wavefront 0's lanes take row L%16 and every fourth
 // 8-column chunk of the rank, and add their partial dot products into the
 // row sums before the lane and wavefront reduction, so the order of the
 // additions stays fixed.
@@ -451,6 +579,11 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
                                           const GemvDims& d, int64_t slab) {
   __shared__ __attribute__((aligned(16))) uint16_t xs_all[WAVES][MT * B2];
   __shared__ float red[WAVES][MT][16];
+  __shared__ uint4 lut8[META == HYB_META_MASK8 ? 256 : 1];
+  if constexpr (META == HYB_META_MASK8) {
+    fill_expand8_lut(lut8);
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -490,7 +623,7 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
       ti[ld] = tiN;
       gemv_load<MT, B2>(st[ld], tiN, tk0 + i + s + kLast, dense, val, meta, x, d, rs, lane);
       tiN = tile_index(i + s + STAGES);
-      if (i + s < cnt) gemv_compute<MT, B2, DT, META>(st[s], ti[s], xs, d, lane, acc);
+      if (i + s < cnt) gemv_compute<MT, B2, DT, META>(st[s], ti[s], xs, lut8, d, lane, acc);
     }
   }
 
@@ -638,7 +771,9 @@ __device__ __forceinline__ f32x4_t smfmac16x16x64(uint4 a, uint4 b0, uint4 b1, u
 // 2-bit index word (i0 | i1 << 2 per group) from a metadata word.
 template <int META>
 __device__ __forceinline__ uint32_t idx2_word(uint32_t word) {
-  if constexpr (META == HYB_META_IDX2) {
+  if constexpr (META == HYB_META_MASK8) {
+    return 0u;  // 4:8 groups have no 2-bit index word; their paths never ask
+  } else if constexpr (META == HYB_META_IDX2) {
     return word & 0xFFFFu;
   } else {
     uint32_t out = 0;
@@ -913,6 +1048,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
   constexpr int kStepsPerTile = B2 / 64;
   constexpr int kPart = RG * 4 * MB * 64 * 4;  // floats of one wavefront's partial sums
   __shared__ __attribute__((aligned(16))) float red[WAVES / 2][kPart];
+  __shared__ uint4 lut8[META == HYB_META_MASK8 ? 256 : 1];
+  if constexpr (META == HYB_META_MASK8) {
+    fill_expand8_lut(lut8);
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -996,6 +1136,34 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
       asm("" : "+v"(dm));
       uint4 a0[4], a1[4];
       uint32_t i0[4];
+      if constexpr (META == HYB_META_MASK8) {
+        // 4:8: a sparse slab's sixteen columns per lane, expanded, take the
+        // place of the dense slab's two chunk pieces; both kinds run both
+        // passes.
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const u32x4_t v0 = st.v0[g][sl], v1 = st.v1[g][sl];
+          uint32_t e[8];
+          expand8_lane(lut8, v0[0], v0[1], v0[2], v0[3], (st.m[g][sl] >> mshift) & 0xFFFFu, e);
+          const uint32_t l0 = bitsel(dm, v0[0], e[0]), l1 = bitsel(dm, v0[1], e[1]);
+          const uint32_t l2 = bitsel(dm, v0[2], e[2]), l3 = bitsel(dm, v0[3], e[3]);
+          const uint32_t h0 = bitsel(dm, v1[0], e[4]), h1 = bitsel(dm, v1[1], e[5]);
+          const uint32_t h2 = bitsel(dm, v1[2], e[6]), h3 = bitsel(dm, v1[3], e[7]);
+          a0[sl] = make_uint4(l0, l2, h0, h2);
+          a1[sl] = make_uint4(l1, l3, h1, h3);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+            acc[g][sl][mb] = smfmac16x16x64<DT>(a0[sl], st.b[mb][0], st.b[mb][1], 0x4444u, acc[g][sl][mb]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+            acc[g][sl][mb] = smfmac16x16x64<DT>(a1[sl], st.b[mb][0], st.b[mb][1], 0xEEEEu, acc[g][sl][mb]);
+        continue;
+      }
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         const u32x4_t v0 = st.v0[g][sl], v1 = st.v1[g][sl];
@@ -1206,6 +1374,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
   constexpr int BM = 16 * MB;
   constexpr int kStepsPerTile = B2 / 64;
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
+  __shared__ uint4 lut8[META == HYB_META_MASK8 ? 256 : 1];
+  // (4:8 only; the first barrier of the main loop precedes every read)
+  if constexpr (META == HYB_META_MASK8) fill_expand8_lut(lut8);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1327,6 +1498,43 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
     asm("" : "+v"(dm));
     uint4 a0[4], a1[4];
     uint32_t i0[4];
+    if constexpr (META == HYB_META_MASK8) {
+      // 4:8: the sparse chunk's two groups per lane, expanded, stand in for
+      // the dense slab's two pieces; every step runs both passes.
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const u32x4_t v0 = *(const volatile lds_u32x4_t*)(wbase + (2 * sl) * 1024 + r_off);
+        const u32x4_t v1 = *(const volatile lds_u32x4_t*)(wbase + (2 * sl) * 1024 + r_off2);
+        const uint32_t m = *reinterpret_cast<const uint16_t*>(msrc + sl * 2 * B2);
+        uint32_t e[8];
+        expand8_lane(lut8, v0[0], v0[1], v0[2], v0[3], m, e);
+        const uint32_t l0 = bitsel(dm, v0[0], e[0]), l1 = bitsel(dm, v0[1], e[1]);
+        const uint32_t l2 = bitsel(dm, v0[2], e[2]), l3 = bitsel(dm, v0[3], e[3]);
+        const uint32_t h0 = bitsel(dm, v1[0], e[4]), h1 = bitsel(dm, v1[1], e[5]);
+        const uint32_t h2 = bitsel(dm, v1[2], e[6]), h3 = bitsel(dm, v1[3], e[7]);
+        a0[sl] = make_uint4(l0, l2, h0, h2);
+        a1[sl] = make_uint4(l1, l3, h1, h3);
+      }
+      uint4 bq[MBW][2];
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) {
+        const int row = (wm * MBW + mb) * 16 + (lane & 15);
+        const int sw = (row >> 1) & 7;
+        bq[mb][0] = *reinterpret_cast<const uint4*>(xsrc + row * 128 + ((q ^ sw) * 16));
+        bq[mb][1] = *reinterpret_cast<const uint4*>(xsrc + row * 128 + (((q + 4) ^ sw) * 16));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+          acc[sl][mb] = smfmac16x16x64<DT>(a0[sl], bq[mb][0], bq[mb][1], 0x4444u, acc[sl][mb]);
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+          acc[sl][mb] = smfmac16x16x64<DT>(a1[sl], bq[mb][0], bq[mb][1], 0xEEEEu, acc[sl][mb]);
+      return;
+    }
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
       const u32x4_t v0 = *(const volatile lds_u32x4_t*)(wbase + (2 * sl) * 1024 + r_off);
@@ -1623,10 +1831,12 @@ hipError_t launch_gemv_impl(const hyb_layout& L, const hyb_packed& P, const void
   const dim3 grid(unsigned(L.n / 16));
   if (L.dtype == HYB_BF16) {
     if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
+    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, L.b2, grid, s, q, d);
   } else {
     if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
+    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, L.b2, grid, s, q, d);
   }
   return hipGetLastError();
 }
@@ -1703,10 +1913,12 @@ hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed*
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   if (L[0].dtype == HYB_BF16) {
     if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_BF16, HYB_META_IDX2>(m, L[0].b2, grid, s, xp, d, g);
-    else gemv_grouped_mt<HYB_BF16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
+    else if (L[0].meta == HYB_META_MASK4) gemv_grouped_mt<HYB_BF16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
+    else gemv_grouped_mt<HYB_BF16, HYB_META_MASK8>(m, L[0].b2, grid, s, xp, d, g);
   } else {
     if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_F16, HYB_META_IDX2>(m, L[0].b2, grid, s, xp, d, g);
-    else gemv_grouped_mt<HYB_F16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
+    else if (L[0].meta == HYB_META_MASK4) gemv_grouped_mt<HYB_F16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
+    else gemv_grouped_mt<HYB_F16, HYB_META_MASK8>(m, L[0].b2, grid, s, xp, d, g);
   }
   return hipGetLastError();
 }
@@ -1747,10 +1959,11 @@ hipError_t gemm_rx_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   return hipGetLastError();
 }
 
-// Three LDS stages where they fit, else two.
-template <int B2, int MB, int WAVES>
+// Three LDS stages where they fit (with the 4 KiB selector table of 4:8
+// tiles), else two.
+template <int B2, int MB, int WAVES, int META>
 constexpr int lds_stages() {
-  return GemmLdsCfg<B2, MB, 3, WAVES>::kBytes <= 160 * 1024 ? 3 : 2;
+  return GemmLdsCfg<B2, MB, 3, WAVES>::kBytes + (META == HYB_META_MASK8 ? 4096 : 0) <= 160 * 1024 ? 3 : 2;
 }
 
 // Compute units of the current device (cached per device).
@@ -1799,7 +2012,9 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
     // 128 tokens per wavefront need a SIMD to themselves: only when the row
     // groups fit in one round.
     if (groups <= cus) return gemm_rx_go<B2, DT, META, 8, 4, 2>(L, q, m, d, s);
-    return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
+    // (k_gemm has no 4:8 path: 4:8 weights stay on the register-fed kernel)
+    if constexpr (META == HYB_META_MASK8) return gemm_rx_go<B2, DT, META, 8, 4, 2>(L, q, m, d, s);
+    else return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
   }
   const int64_t gn = (L.n + 255) / 256;
   auto cost = [&](int64_t bm, double step) {
@@ -1808,10 +2023,10 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   const double c256 = cost(256, 1.0), c192 = cost(192, HYB_GEMM_C192), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
   const double best = c256 < c192 ? (c256 < c128 ? (c256 < c64 ? c256 : c64) : (c128 < c64 ? c128 : c64))
                                   : (c192 < c128 ? (c192 < c64 ? c192 : c64) : (c128 < c64 ? c128 : c64));
-  if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8>(), 8>(L, q, m, d, s);
-  if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8>(), 8>(L, q, m, d, s);
-  if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8>(), 8>(L, q, m, d, s);
-  return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4>(), 4>(L, q, m, d, s);
+  if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
+  if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
+  if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);
+  return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4, META>(), 4>(L, q, m, d, s);
 }
 
 template <int DT, int META>
@@ -1840,11 +2055,13 @@ hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, 
   d.b1 = L.b1;
   d.ydt = y_dtype;
   if (L.dtype == HYB_BF16) {
-    return L.meta == HYB_META_IDX2 ? gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, s)
-                                   : gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, s);
+    if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, s);
+    if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, s);
+    return gemm_b2<HYB_BF16, HYB_META_MASK8>(L, q, m, d, s);
   }
-  return L.meta == HYB_META_IDX2 ? gemm_b2<HYB_F16, HYB_META_IDX2>(L, q, m, d, s)
-                                 : gemm_b2<HYB_F16, HYB_META_MASK4>(L, q, m, d, s);
+  if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_F16, HYB_META_IDX2>(L, q, m, d, s);
+  if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_F16, HYB_META_MASK4>(L, q, m, d, s);
+  return gemm_b2<HYB_F16, HYB_META_MASK8>(L, q, m, d, s);
 }
 
 }  // namespace hyb

@@ -52,7 +52,7 @@ def test_layout_struct_size():
 
 
 @pytest.mark.parametrize("seed", range(6))
-@pytest.mark.parametrize("meta", ["idx2", "mask4"])
+@pytest.mark.parametrize("meta", ["idx2", "mask4", "mask8"])
 def test_plan_matches_oracle(seed, meta):
     rng = np.random.default_rng(seed)
     b1 = int(rng.choice([64, 128, 256]))
