@@ -22,8 +22,8 @@ from the previous use of a copy.
 
 After the timed steps, the grouped decode launch is compared with separate
 launches on one decoder layer (JSON key "grouped"), the sparse + low-rank
-decode product is compared with the plain one (JSON key "lowrank"), and the
-prefill GEMM is
+decode product is compared with the plain one (JSON key "lowrank"), 4:8
+tiles with 2:4 ones (JSON key "nm48"), and the prefill GEMM is
 measured on its own workload
 (Qwen3-14B-shaped 17408 x 5120, 64 x 64 tiles, M = 2048): hybrid, the same
 kernel all-dense, and the vendor BLAS dense product, with the matrix-core
@@ -153,7 +153,7 @@ def main():
     ap.add_argument("--prefill-m", type=int, default=2048,
                     help="token count of the prefill GEMM measurement")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,prefill)")
+                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 128 MiB device copies (torch copy kernel) as a counter reference")
@@ -177,7 +177,7 @@ def main():
     dev = torch.device("cuda:0")
     rotate = int(args.rotate_gib * (1 << 30))
     rows = set(args.only.split(",")) if args.only else {"pack", "gemv", "dense", "unpack", "gemm", "grouped",
-                                                         "lowrank", "prefill"}
+                                                         "lowrank", "nm48", "prefill"}
 
     if args.copy_calibration:
         # A plain copy of known size: 128 MiB read + 128 MiB written per
@@ -398,6 +398,10 @@ def main():
         log("[bench] grouped decode launch on one decoder layer")
         out["grouped"] = grouped(hb, torch, wl, dev, args.meta)
         log(f"[bench] grouped: {out['grouped']}")
+    if "nm48" in rows:
+        log("[bench] 4:8 against 2:4")
+        out["nm48"] = nm48(hb, torch, wl, dev)
+        log(f"[bench] nm48: {out['nm48']}")
     if "lowrank" in rows:
         log("[bench] sparse + low-rank decode")
         out["lowrank"] = lowrank(hb, torch, wl, dev, args.meta)
@@ -478,6 +482,57 @@ def prefill(hb, torch, wl, dev, m, meta):
                         "kernel": "k_gemm_lds (256-row x 192-token workgroups on 8 wavefronts at this M on 256 CUs)"},
            "timing": f"graph burst of {n_launch} launches over 2 rotating copies, median of 5 replays"}
     del hyb, den, wt, w, x, y, yb
+    torch.cuda.empty_cache()
+    return out
+
+
+def nm48(hb, torch, wl, dev):
+    """4:8 sparse tiles (metadata kind mask8) against 2:4 (idx2) on the same
+    tile maps: the decode product on the Llama-3.1-8B up projection at M = 1
+    and 16 (rotating cold copies; both kinds store the same bytes), and the
+    prefill product on the Qwen3-14B gate/up projection at M = 2048 (4:8
+    tiles expand to dense matrix-core work, so the all-dense map of the same
+    kernel is the comparison there)."""
+    out = {}
+    mat = wl.workload(2).matrices[0]
+    w = hb.bits_to_tensor(mat.weight_bits(), mat.dtype, dev)
+    tmap = mat.tile_map()
+    for m in (1, 16):
+        x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
+        y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+        row = {}
+        for meta in ("idx2", "mask8"):
+            P0 = hb.pack(w, tmap, mat.b1, mat.b2, meta)
+            n_copies = copies_for(P0.weight_bytes(), 1 << 30)
+            Ps = [P0] + [hb.pack(w, tmap, mat.b1, mat.b2, meta) for _ in range(n_copies - 1)]
+            torch.cuda.synchronize()
+            us = graph_us(torch, lambda c: [hb.gemv(Ps[(3 * i) % n_copies], x, out=y) for i in range(c)],
+                          2 * n_copies)
+            row[meta] = {"us": round(us, 3), "GBps": round(alg_bytes(P0.layout, m) / (us * 1e-6) / 1e9, 1)}
+            del Ps, P0
+            torch.cuda.empty_cache()
+        row["mask8_over_idx2"] = round(row["mask8"]["us"] / row["idx2"]["us"], 4)
+        out[f"gemv_m{m}"] = row
+    del w
+    mat = wl.workload(5).matrices[0]
+    tmap = mat.tile_map()
+    w = hb.bits_to_tensor(mat.weight_bits(), mat.dtype, dev)
+    m = 2048
+    x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
+    y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+    row = {}
+    for name, meta, tm in (("idx2", "idx2", tmap), ("mask8", "mask8", tmap),
+                           ("all_dense", "idx2", np.zeros_like(tmap))):
+        Ps = [hb.pack(w, tm, mat.b1, mat.b2, meta) for _ in range(2)]
+        torch.cuda.synchronize()
+        us = graph_us(torch, lambda c: [hb.gemm(Ps[i % 2], x, out=y) for i in range(c)], 8)
+        row[name] = {"us": round(us, 2), "dense_flops_TFLOPs": round(2 * m * mat.n * mat.k / (us * 1e-6) / 1e12, 1)}
+        del Ps
+        torch.cuda.empty_cache()
+    out["gemm_m2048"] = row
+    out["workloads"] = {"gemv": "Llama-3.1-8B up projection 14336x4096 bf16, 128x128 tiles, 2509/3584 sparse",
+                        "gemm": "Qwen3-14B gate/up projection 17408x5120 bf16, 64x64 tiles, 13056/21760 sparse"}
+    del w, x, y
     torch.cuda.empty_cache()
     return out
 
