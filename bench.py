@@ -658,6 +658,32 @@ def lowrank(hb, torch, wl, dev, meta, rank=64):
            "timing": f"graph burst of {reps} products over {n_copies} rotating copies, median of 5 replays"}
     del Ps, Vs, Us
     torch.cuda.empty_cache()
+    # prefill: the Qwen3-14B gate/up projection at M = 2048 with rank 64
+    mat = wl.workload(5).matrices[0]
+    m = 2048
+    w = hb.bits_to_tensor(mat.weight_bits(), mat.dtype, dev)
+    Ps = [hb.pack(w, mat.tile_map(), mat.b1, mat.b2, meta) for _ in range(2)]
+    del w
+    Vs, Us = [], []
+    for _ in range(2):
+        Vs.append((torch.randn((rank, mat.k), generator=gen, device=dev) * 0.02).to(torch.bfloat16))
+        Us.append((torch.randn((mat.n, rank), generator=gen, device=dev) * 0.02).to(torch.bfloat16))
+    x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
+    t = torch.empty((m, rank), dtype=torch.float32, device=dev)
+    y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    n_launch = 8
+    us_g = graph_us(torch, lambda c: [hb.gemm(Ps[i % 2], x, out=y) for i in range(c)], n_launch)
+    us_p = graph_us(torch, lambda c: [hb.lowrank_project(Vs[i % 2], x, out=t) for i in range(c)], n_launch)
+    us_l = graph_us(torch, lambda c: [hb.gemm_lowrank(Ps[i % 2], x, t, Us[i % 2], out=y) for i in range(c)], n_launch)
+    out["prefill"] = {"workload": f"Qwen3-14B gate/up projection {mat.n}x{mat.k} bf16 hybrid + rank {rank}, M={m}",
+                      "gemm_us": round(us_g, 2), "project_us": round(us_p, 2), "gemm_lowrank_us": round(us_l, 2),
+                      "update_us_by_difference": round(us_l - us_g, 2),
+                      "sparse_lowrank_total_us": round(us_p + us_l, 2),
+                      "overhead_vs_gemm": round((us_p + us_l) / us_g, 4),
+                      "timing": f"graph burst of {n_launch} launches over 2 copies, median of 5 replays"}
+    del Ps, Vs, Us, x, t, y
+    torch.cuda.empty_cache()
     return out
 
 

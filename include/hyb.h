@@ -192,7 +192,10 @@ hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_
  *   x      device m x k, row stride ldx >= k, ldx % 8 == 0, 16-byte aligned
  *   t      device fp32 output m x rank, row stride ldt >= rank
  * Products are exact and summed in fp32 in a fixed order (the result is
- * deterministic).  0 <= m <= 16 * 65535 (one launch). */
+ * deterministic).  0 <= m <= 16 * 65535 (one launch).  Decode sizes
+ * (m <= 16) take one workgroup per row of V on the vector ALUs; larger m
+ * runs on the matrix cores (exact products, fp32 sums), one workgroup per
+ * 16 tokens. */
 hyb_status hyb_lowrank_project(const void* v, int64_t ldv, int32_t rank, int64_t k, int32_t dtype,
                                const void* x, int32_t m, int64_t ldx, float* t, int64_t ldt,
                                void* stream);
@@ -212,6 +215,17 @@ hyb_status hyb_lowrank_project(const void* v, int64_t ldv, int32_t rank, int64_t
  * The low-rank term is accumulated in fp32 (u widened, fp32 products), into
  * the same per-row sums as the sparse product. */
 hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                            int32_t m, int64_t ldx, const float* t, int64_t ldt, const void* u,
+                            int64_t ldu, int32_t rank, void* y, int32_t y_dtype, int64_t ldy,
+                            void* stream);
+
+/* Sparse + low-rank product for any m >= 0: Y = X W'^T + T U^T as for
+ * hyb_gemv_lowrank (3BASiL sections 1 and 4), with the same arguments and
+ * checks.  m <= 8 runs the fused decode kernel; larger m the matrix-core
+ * kernels, which add T U^T to each output tile before it is stored (fp32
+ * products and sums, rank walked in order), so 16-bit outputs are rounded
+ * once.  rank 0 is plain hyb_gemm. */
+hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x,
                             int32_t m, int64_t ldx, const float* t, int64_t ldt, const void* u,
                             int64_t ldu, int32_t rank, void* y, int32_t y_dtype, int64_t ldy,
                             void* stream);

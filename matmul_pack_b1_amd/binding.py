@@ -27,7 +27,7 @@ META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
-            "hyb_gemv_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
 MAX_GROUP = 16
 MAX_RANK = 256
 
@@ -84,9 +84,10 @@ def lib() -> ctypes.CDLL:
     L.hyb_gemv_grouped.argtypes = [I32, ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64,
                                    ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I64), P]
     L.hyb_gemv_grouped.restype = I32
-    L.hyb_gemv_lowrank.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I64, P,
-                                   I64, I32, P, I32, I64, P]
-    L.hyb_gemv_lowrank.restype = I32
+    for f in (L.hyb_gemv_lowrank, L.hyb_gemm_lowrank):
+        f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I64, P, I64, I32, P,
+                      I32, I64, P]
+        f.restype = I32
     L.hyb_lowrank_project.argtypes = [P, I64, I32, I64, I32, P, I32, I64, P, I64, P]
     L.hyb_lowrank_project.restype = I32
     L.hyb_stream_read.argtypes = [P, I64, P, I32, P]
@@ -315,9 +316,7 @@ def lowrank_project(v, x, out=None):
     return out
 
 
-def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
-    """Decode product of a sparse + low-rank weight: Y = X W'^T + T U^T,
-    with t = X V (fp32, m x rank) given and u (n x rank, weight dtype)."""
+def _lowrank(fn_name: str, P: PackedWeight, x, t, u, out_dtype, out):
     torch = _torch()
     _check_rows(x, "x")
     _check_rows(t, "t")
@@ -333,13 +332,25 @@ def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
     tdt = {HYB_F32: torch.float32, HYB_BF16: torch.bfloat16, HYB_F16: torch.float16}[code]
     if out is None:
         out = torch.empty((m, n), dtype=tdt, device=x.device)
-    st = lib().hyb_gemv_lowrank(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
-                                int(x.stride(0)) if x.numel() else int(k), _ptr(t),
-                                int(t.stride(0)) if t.numel() else int(rank), _ptr(u),
-                                int(u.stride(0)) if u.numel() else int(rank), int(rank), _ptr(out), code,
-                                int(out.stride(0)) if out.numel() else int(n), _stream(x.device))
-    check(st, "hyb_gemv_lowrank")
+    st = getattr(lib(), fn_name)(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
+                                 int(x.stride(0)) if x.numel() else int(k), _ptr(t),
+                                 int(t.stride(0)) if t.numel() else int(rank), _ptr(u),
+                                 int(u.stride(0)) if u.numel() else int(rank), int(rank), _ptr(out), code,
+                                 int(out.stride(0)) if out.numel() else int(n), _stream(x.device))
+    check(st, fn_name)
     return out
+
+
+def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
+    """Decode product of a sparse + low-rank weight (1..16 tokens): Y = X W'^T
+    + T U^T, with t = X V (fp32, m x rank) given and u (n x rank, weight
+    dtype)."""
+    return _lowrank("hyb_gemv_lowrank", P, x, t, u, out_dtype, out)
+
+
+def gemm_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
+    """Sparse + low-rank product for any number of tokens."""
+    return _lowrank("hyb_gemm_lowrank", P, x, t, u, out_dtype, out)
 
 
 def sparse_lowrank_gemv(P: PackedWeight, v, u, x, out_dtype=None, out=None, t=None):
@@ -348,6 +359,12 @@ def sparse_lowrank_gemv(P: PackedWeight, v, u, x, out_dtype=None, out=None, t=No
     decode kernel.  `t` optionally gives the m x rank fp32 buffer for T."""
     t = lowrank_project(v, x, out=t)
     return gemv_lowrank(P, x, t, u, out_dtype, out)
+
+
+def sparse_lowrank_gemm(P: PackedWeight, v, u, x, out_dtype=None, out=None, t=None):
+    """As sparse_lowrank_gemv for any number of tokens (hyb_gemm_lowrank)."""
+    t = lowrank_project(v, x, out=t)
+    return gemm_lowrank(P, x, t, u, out_dtype, out)
 
 
 def gemm(P: PackedWeight, x, out_dtype=None, out=None):

@@ -279,21 +279,37 @@ hyb_status hyb_lowrank_project(const void* v, int64_t ldv, int32_t rank, int64_t
                     "low-rank projection launch");
 }
 
-hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
-                            int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
-                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
-  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, hyb::kMaxGemvM);
-  if (st != HYB_OK) return st;
-  if (rank < 0 || rank > hyb::kMaxRank || rank % 8 != 0)
-    return fail(HYB_ERR_SHAPE, "rank = %d must be a multiple of 8 in [0, %d]", rank, hyb::kMaxRank);
-  if (rank == 0) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
-  if (m == 0 || layout->n == 0) return ok();
+namespace {
+
+// Checks of the low-rank operands shared by the decode and prefill entry
+// points (rank > 0, m > 0).
+hyb_status check_lowrank(const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank) {
   if (!t || !aligned(t, 16)) return fail(HYB_ERR_INVALID_ARG, "t is NULL or not 16-byte aligned");
   if (ldt < rank || ldt % 4 != 0)
     return fail(HYB_ERR_INVALID_ARG, "t row stride %lld must be >= rank and a multiple of 4", (long long)ldt);
   if (!u || !aligned(u, 16)) return fail(HYB_ERR_INVALID_ARG, "u is NULL or not 16-byte aligned");
   if (ldu < rank || ldu % 8 != 0)
     return fail(HYB_ERR_INVALID_ARG, "u row stride %lld must be >= rank and a multiple of 8", (long long)ldu);
+  return HYB_OK;
+}
+
+hyb_status check_rank(int32_t rank) {
+  if (rank < 0 || rank > hyb::kMaxRank || rank % 8 != 0)
+    return fail(HYB_ERR_SHAPE, "rank = %d must be a multiple of 8 in [0, %d]", rank, hyb::kMaxRank);
+  return HYB_OK;
+}
+
+}  // namespace
+
+hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                            int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, hyb::kMaxGemvM);
+  if (st != HYB_OK) return st;
+  if ((st = check_rank(rank)) != HYB_OK) return st;
+  if (rank == 0) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (m == 0 || layout->n == 0) return ok();
+  if ((st = check_lowrank(t, ldt, u, ldu, rank)) != HYB_OK) return st;
   if (int64_t(m) * ldx * 2 >= (int64_t(1) << 31))
     return fail(HYB_ERR_UNSUPPORTED, "decode kernel needs m * ldx * 2 < 2^31 bytes of x");
   return hip_status(hyb::launch_gemv_lowrank(*layout, *w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy,
@@ -301,15 +317,41 @@ hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const
                     "low-rank gemv launch");
 }
 
+namespace {
+
+// Launch limits of the matrix-core kernels (m > 0, n > 0).
+hyb_status check_mfma_limits(int32_t m, int64_t ldx) {
+  if (ldx * 2 * 256 >= (int64_t(1) << 31))
+    return fail(HYB_ERR_UNSUPPORTED, "matrix-core kernel needs ldx < 4194304 elements");
+  if ((int64_t(m) + 15) / 16 > 65535 * 8) return fail(HYB_ERR_UNSUPPORTED, "m = %d too large for one launch", m);
+  return HYB_OK;
+}
+
+}  // namespace
+
+hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                            int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  if (m >= 0 && m <= hyb::kGemvCrossoverM)
+    return hyb_gemv_lowrank(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
+  if (st != HYB_OK) return st;
+  if ((st = check_rank(rank)) != HYB_OK) return st;
+  if (rank == 0) return hyb_gemm(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (layout->n == 0) return ok();
+  if ((st = check_lowrank(t, ldt, u, ldu, rank)) != HYB_OK) return st;
+  if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream), t,
+                                     ldt, u, ldu, rank),
+                    "low-rank gemm launch");
+}
+
 hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                          int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
   if (st != HYB_OK) return st;
   if (m == 0 || layout->n == 0) return ok();
-  if (ldx * 2 * 256 >= (int64_t(1) << 31))
-    return fail(HYB_ERR_UNSUPPORTED, "matrix-core kernel needs ldx < 4194304 elements");
-  if ((int64_t(m) + 15) / 16 > 65535 * 8)
-    return fail(HYB_ERR_UNSUPPORTED, "m = %d too large for one launch", m);
+  if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
   return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy,
                                      static_cast<hipStream_t>(stream)),
                     "gemm launch");

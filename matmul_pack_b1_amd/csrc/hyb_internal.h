@@ -37,7 +37,11 @@ constexpr int kMaxRank = HYB_MAX_RANK;
 hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
                                int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s);
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+// With rank > 0 the kernels add T U^T (t: m x rank fp32, u: n x rank) to
+// every output before it is stored.
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
-                       int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s);
+                       int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s,
+                       const float* t = nullptr, int64_t ldt = 0, const void* u = nullptr, int64_t ldu = 0,
+                       int rank = 0);
 
 }  // namespace hyb

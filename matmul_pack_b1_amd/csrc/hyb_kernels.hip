@@ -749,7 +749,75 @@ struct GemmDims {
   int64_t ldx, ldy;
   int32_t n, m, tiles_k, n_dense, n_sparse;
   int b1, ydt;
+  // low-rank term T U^T (hyb_gemm_lowrank; rank 0 otherwise): T m x rank
+  // fp32, U n x rank of the weight dtype
+  const float* t;
+  const uint16_t* u;
+  int64_t ldt, ldu;
+  int32_t rank;
 };
+
+// Adds the low-rank term sum_j U[row][j] T[tok][j] (3BASiL, gist.science,
+// section 1: W ~ S + L with L = U V^T, and T = X V) to a block of 16 x 16
+// accumulator tiles: slab s holds rows row0 + 16 s, token block b tokens
+// tok0 + 16 b (lane L: rows 4 (L/16) + 0..3 of the slab, token L%16), the
+// layout of the products above.  Per 32-wide slice of the rank each slab's
+// U piece and each token block's T piece is loaded once.  With bf16
+// weights T is split into bf16 hi + lo (|T - hi - lo| <= 2^-16 |T|) and
+// each tile takes two exact 16x16x32 products; with fp16 weights (where a
+// 16-bit T could overflow) the fp32 16x16x4 instruction takes the products,
+// lane group q supplying j = j0 + 8q + e to step e of both operands.  Rows
+// are whole (n is a multiple of 64); tokens >= m and j >= rank read as zero.
+template <int DT, int NS, int NT>
+__device__ __forceinline__ void lr_block(f32x4_t (&c)[NS][NT], const GemmDims& d, int64_t row0, int64_t tok0,
+                                         int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  for (int32_t j0 = 0; j0 < d.rank; j0 += 32) {
+    const int32_t j = j0 + 8 * q;
+    const bool j_ok = j < d.rank;
+    uint4 uw[NS];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+      uw[sl] = j_ok ? *reinterpret_cast<const uint4*>(d.u + (row0 + 16 * sl + r) * d.ldu + j)
+                    : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const int64_t tok = tok0 + 16 * b + r;
+      float4 t0 = make_float4(0.f, 0.f, 0.f, 0.f), t1 = t0;
+      if (j_ok && tok < d.m) {
+        t0 = *reinterpret_cast<const float4*>(d.t + tok * d.ldt + j);
+        t1 = *reinterpret_cast<const float4*>(d.t + tok * d.ldt + j + 4);
+      }
+      const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+      if constexpr (DT == HYB_BF16) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t h0 = round16<HYB_BF16>(tv[2 * e]), h1 = round16<HYB_BF16>(tv[2 * e + 1]);
+          const uint32_t l0 = round16<HYB_BF16>(tv[2 * e] - widen16<HYB_BF16>(h0));
+          const uint32_t l1 = round16<HYB_BF16>(tv[2 * e + 1] - widen16<HYB_BF16>(h1));
+          hi[e] = h0 | (h1 << 16);
+          lo[e] = l0 | (l1 << 16);
+        }
+        const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+          c[sl][b] = mfma16x16x32<HYB_BF16>(uw[sl], bh, c[sl][b]);
+          c[sl][b] = mfma16x16x32<HYB_BF16>(uw[sl], bl, c[sl][b]);
+        }
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+          const uint32_t w4[4] = {uw[sl].x, uw[sl].y, uw[sl].z, uw[sl].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            c[sl][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(widen16<DT>(e & 1 ? w4[e >> 1] >> 16 : w4[e >> 1] & 0xFFFFu),
+                                                            tv[e], c[sl][b], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
 
 struct GemmAStage {
   uint4 a[4][2];     // per slab: dense chunks 2kb, 2kb+1, or the sparse value chunk in a[.][0]
@@ -977,6 +1045,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
   }
 
   if (!rows_ok) return;
+  if (d.rank > 0) lr_block<DT, 4, MB>(acc, d, n0, m0, lane);
   // acc[sl][mb] lane L holds rows n0 + 16 sl + 4 (L/16) + 0..3 of token
   // m0 + 16 mb + L%16.
   const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
@@ -1199,6 +1268,23 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
     for (int s = 0; s < STAGES; ++s) {
       load(st[(s + STAGES - 1) % STAGES], i + s + STAGES - 1);
       if (i + s < cnt) compute(st[s], i + s);
+    }
+  }
+
+  // Low-rank term: token block mb by wavefront mb % WAVES, into that
+  // wavefront's partial sums (the tree below keeps a fixed order).
+  if (d.rank > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb % WAVES != wave) continue;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        if (n0 + 64 * g >= d.n) continue;
+        f32x4_t c[4][1] = {{acc[g][0][mb]}, {acc[g][1][mb]}, {acc[g][2][mb]}, {acc[g][3][mb]}};
+        lr_block<DT, 4, 1>(c, d, n0 + 64 * g, m0 + 16 * mb, lane);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) acc[g][sl][mb] = c[sl][0];
+      }
     }
   }
 
@@ -1586,6 +1672,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
   wait_vmcnt<0>();
 
   if (!rows_ok) return;
+  if (d.rank > 0) lr_block<DT, 4, MBW>(acc, d, n0, m0 + wm * MBW * 16, lane);
   const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
@@ -1616,11 +1703,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
 // ---------------------------------------------------- low-rank project ----
 //
 // T = X V for the low-rank factor of a sparse + low-rank weight, V held as
-// rank rows of k values (row j is column j of V).  One workgroup per V row
-// and block of MT tokens: each thread takes 8-element slices of K at a
-// stride of 8 * 256, two products per v_dot2, then the 256 partial sums are
-// reduced across the wavefront and, in a fixed order, across the four
-// wavefronts.  V is read once per token block; the x rows come from L2.
+// rank rows of k values (row j is column j of V).
+//
+// Decode sizes (m <= 16): one workgroup per V row and block of MT tokens;
+// each thread takes 8-element slices of K at a stride of 8 * 256, two
+// products per v_dot2, then the 256 partial sums are reduced across the
+// wavefront and, in a fixed order, across the four wavefronts.
 template <int DT, int MT>
 __global__ __launch_bounds__(256) void k_lr_project(const uint16_t* __restrict__ v, int64_t ldv, int64_t k,
                                                     const uint16_t* __restrict__ x, int32_t m, int64_t ldx,
@@ -1660,6 +1748,66 @@ __global__ __launch_bounds__(256) void k_lr_project(const uint16_t* __restrict__
   if (tid < mc) t[int64_t(m0 + tid) * ldt + j] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
 }
 
+// Prefill sizes (m > 16): the matrix cores, loading operands straight from
+// memory.  One workgroup per 16 tokens and 16 NB ranks (the ranks split
+// over at most four workgroups); its eight wavefronts take the 32-column K
+// steps round-robin, each holding NB accumulator tiles of 16 ranks.  A operand: V rows (lane L: rank 16 nb + L%16, columns 8 (L/16)
+// of the step), B operand: X rows (token L%16), so a tile holds T^T.  The
+// wavefronts' sums are added in a fixed tree through LDS.  X is read once
+// per workgroup, V once per 16 tokens.
+template <int DT, int NB>
+__global__ __launch_bounds__(512) void k_lr_project_mfma(const uint16_t* __restrict__ v, int64_t ldv, int32_t rank,
+                                                         int64_t k, const uint16_t* __restrict__ x, int32_t m,
+                                                         int64_t ldx, float* __restrict__ t, int64_t ldt) {
+  constexpr int kWaves = 8;
+  __shared__ __attribute__((aligned(16))) float red[kWaves / 2][NB * 4 * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4, r = lane & 15;
+  const int64_t tok = int64_t(blockIdx.x) * 16 + r;
+  const bool tok_ok = tok < m;
+  const int32_t jb = int32_t(blockIdx.y) * NB * 16;  // first rank of the workgroup
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t ksteps = (k + 31) / 32;
+#pragma unroll 4
+  for (int64_t st = wave; st < ksteps; st += kWaves) {
+    const int64_t kk = st * 32 + 8 * q;
+    const bool k_ok = kk < k;
+    const uint4 bx = (tok_ok && k_ok) ? *reinterpret_cast<const uint4*>(x + tok * ldx + kk) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int32_t j = jb + nb * 16 + r;
+      const uint4 av = (j < rank && k_ok) ? *reinterpret_cast<const uint4*>(v + int64_t(j) * ldv + kk)
+                                          : make_uint4(0u, 0u, 0u, 0u);
+      acc[nb] = mfma16x16x32<DT>(av, bx, acc[nb]);
+    }
+  }
+#pragma unroll
+  for (int h = kWaves / 2; h >= 1; h /= 2) {
+    if (wave >= h && wave < 2 * h) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4_t*>(&red[wave - h][(nb * 64 + lane) * 4]) = acc[nb];
+    }
+    __syncthreads();
+    if (wave < h) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] += *reinterpret_cast<const f32x4_t*>(&red[wave][(nb * 64 + lane) * 4]);
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || !tok_ok) return;
+  // acc[nb] lane L: ranks 16 nb + 4 (L/16) + 0..3 of token L%16
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int32_t j = jb + nb * 16 + 4 * q + e;
+      if (j < rank) t[tok * ldt + j] = acc[nb][e];
+    }
+}
+
 // --------------------------------------------------------- stream read ----
 //
 // Practical read-rate reference: each wavefront reads four contiguous 1 KiB
@@ -1690,25 +1838,43 @@ __global__ __launch_bounds__(256) void k_stream_read(const char* __restrict__ p,
 namespace {
 
 template <int DT>
-void lr_project_mt(int m, dim3 grid, hipStream_t s, const uint16_t* v, int64_t ldv, int64_t k,
-                   const uint16_t* x, int64_t ldx, float* t, int64_t ldt) {
-  if (m <= 1) hipLaunchKernelGGL((k_lr_project<DT, 1>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
-  else if (m <= 2) hipLaunchKernelGGL((k_lr_project<DT, 2>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
-  else if (m <= 4) hipLaunchKernelGGL((k_lr_project<DT, 4>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
-  else if (m <= 8) hipLaunchKernelGGL((k_lr_project<DT, 8>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
-  else hipLaunchKernelGGL((k_lr_project<DT, 16>), grid, dim3(256), 0, s, v, ldv, k, x, m, ldx, t, ldt);
+void lr_project_mt(int m, dim3 grid, hipStream_t s, const uint16_t* v, int64_t ldv, int64_t k, const uint16_t* x,
+                   int64_t ldx, float* t, int64_t ldt) {
+  const dim3 b(256);
+  if (m <= 1) hipLaunchKernelGGL((k_lr_project<DT, 1>), grid, b, 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else if (m <= 2) hipLaunchKernelGGL((k_lr_project<DT, 2>), grid, b, 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else if (m <= 4) hipLaunchKernelGGL((k_lr_project<DT, 4>), grid, b, 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else if (m <= 8) hipLaunchKernelGGL((k_lr_project<DT, 8>), grid, b, 0, s, v, ldv, k, x, m, ldx, t, ldt);
+  else hipLaunchKernelGGL((k_lr_project<DT, 16>), grid, b, 0, s, v, ldv, k, x, m, ldx, t, ldt);
+}
+
+template <int DT>
+void lr_project_nb(int nb, dim3 grid, hipStream_t s, const uint16_t* v, int64_t ldv, int rank, int64_t k,
+                   const uint16_t* x, int m, int64_t ldx, float* t, int64_t ldt) {
+  const dim3 b(512);
+  if (nb == 1) hipLaunchKernelGGL((k_lr_project_mfma<DT, 1>), grid, b, 0, s, v, ldv, rank, k, x, m, ldx, t, ldt);
+  else if (nb == 2) hipLaunchKernelGGL((k_lr_project_mfma<DT, 2>), grid, b, 0, s, v, ldv, rank, k, x, m, ldx, t, ldt);
+  else hipLaunchKernelGGL((k_lr_project_mfma<DT, 4>), grid, b, 0, s, v, ldv, rank, k, x, m, ldx, t, ldt);
 }
 
 }  // namespace
 
 hipError_t launch_lr_project(const void* v, int64_t ldv, int rank, int64_t k, int dtype, const void* x, int m,
                              int64_t ldx, float* t, int64_t ldt, hipStream_t s) {
-  const int mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
-  const dim3 grid(static_cast<unsigned>(rank), static_cast<unsigned>((m + mt - 1) / mt));
   const auto* vv = static_cast<const uint16_t*>(v);
   const auto* xx = static_cast<const uint16_t*>(x);
-  if (dtype == HYB_BF16) lr_project_mt<HYB_BF16>(m, grid, s, vv, ldv, k, xx, ldx, t, ldt);
-  else lr_project_mt<HYB_F16>(m, grid, s, vv, ldv, k, xx, ldx, t, ldt);
+  if (m <= 16) {
+    const int mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
+    const dim3 grid(static_cast<unsigned>(rank), static_cast<unsigned>((m + mt - 1) / mt));
+    if (dtype == HYB_BF16) lr_project_mt<HYB_BF16>(m, grid, s, vv, ldv, k, xx, ldx, t, ldt);
+    else lr_project_mt<HYB_F16>(m, grid, s, vv, ldv, k, xx, ldx, t, ldt);
+  } else {
+    const int blocks = (rank + 15) / 16;  // 16-rank tiles, split over up to four workgroups
+    const int nb = blocks <= 4 ? 1 : blocks <= 8 ? 2 : 4;  // tiles per workgroup (a template instance)
+    const dim3 grid(static_cast<unsigned>((m + 15) / 16), static_cast<unsigned>((blocks + nb - 1) / nb));
+    if (dtype == HYB_BF16) lr_project_nb<HYB_BF16>(nb, grid, s, vv, ldv, rank, k, xx, m, ldx, t, ldt);
+    else lr_project_nb<HYB_F16>(nb, grid, s, vv, ldv, rank, k, xx, m, ldx, t, ldt);
+  }
   return hipGetLastError();
 }
 
@@ -2041,7 +2207,8 @@ hipError_t gemm_b2(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims
 }  // namespace
 
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
-                       void* y, int y_dtype, int64_t ldy, hipStream_t s) {
+                       void* y, int y_dtype, int64_t ldy, hipStream_t s, const float* t, int64_t ldt,
+                       const void* u, int64_t ldu, int rank) {
   GemvPtrs q{static_cast<const uint4*>(P.dense), static_cast<const uint4*>(P.val),
              static_cast<const uint16_t*>(P.meta), P.tidx, static_cast<const uint16_t*>(x), y};
   GemmDims d{};
@@ -2054,6 +2221,11 @@ hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, 
   d.n_sparse = int32_t(L.n_sparse);
   d.b1 = L.b1;
   d.ydt = y_dtype;
+  d.t = t;
+  d.u = static_cast<const uint16_t*>(u);
+  d.ldt = ldt;
+  d.ldu = ldu;
+  d.rank = rank;
   if (L.dtype == HYB_BF16) {
     if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, s);
     if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, s);

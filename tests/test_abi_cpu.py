@@ -239,6 +239,27 @@ def test_gemv_lowrank_rejects(L):
     assert hb.last_error()
 
 
+def test_gemm_lowrank_rejects(L):
+    lay = _good_layout()
+    P = hb.HybPacked(FAKE, FAKE, FAKE, FAKE)
+
+    def call(m=40, t=FAKE, ldt=64, u=FAKE, ldu=64, rank=64, ydt=3):
+        return L.hyb_gemm_lowrank(ctypes.byref(lay), ctypes.byref(P), FAKE, m, 256, t, ldt, u, ldu, rank,
+                                  FAKE, ydt, 256, None)
+    assert call(ydt=4) == 3                         # output type
+    assert call(rank=12) == 2
+    assert call(rank=hb.MAX_RANK + 8) == 2
+    assert call(t=None) == 1
+    assert call(ldt=66) == 1
+    assert call(u=FAKE + 2) == 1
+    assert call(ldu=60) == 1
+    assert call(m=-1) == 2
+    assert call(m=4, t=None) == 1                   # 8 tokens or fewer: the decode entry point's checks
+    assert call(m=0) == 0
+    assert call(m=4, ydt=2, t=None) == 1
+    assert "t is NULL" in hb.last_error()
+
+
 def test_product_m_zero_is_noop(L):
     lay = _good_layout()
     assert _call(L, "hyb_gemv", lay, m=0, x=None, y=None) == 0

@@ -259,7 +259,8 @@ def test_gemv_lowrank(rank, m, b1, b2, dtype, meta):
 
 
 @pytest.mark.parametrize("rank,k,m,dtype", [(64, 4096, 1, "bf16"), (64, 4096, 16, "bf16"), (1, 72, 3, "f16"),
-                                             (256, 5120, 40, "bf16"), (8, 2056, 17, "f16")])
+                                             (256, 5120, 40, "bf16"), (8, 2056, 17, "f16"), (20, 5120, 300, "bf16"),
+                                             (64, 1024, 2048, "f16")])
 def test_lowrank_project(rank, k, m, dtype):
     """T = X V (V held transposed, rank x k) against the oracle's product,
     over token blocks of 16 with a ragged last block and K tails that do
@@ -319,6 +320,102 @@ def test_sparse_lowrank_end_to_end():
     yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
     extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
     assert_close(y[:, rows], yref, s, extra=extra, what="sparse + low-rank")
+
+
+@pytest.mark.parametrize("m,rank,dtype", [(9, 64, "bf16"), (40, 8, "f16"), (130, 256, "bf16"), (300, 64, "f16")])
+def test_gemm_lowrank(m, rank, dtype):
+    """Prefill sizes: the matrix-core product with the T U^T epilogue against
+    the oracle (ragged token tiles); rank 0 and U = 0 give the plain product
+    bitwise."""
+    torch = _torch()
+    note(f"gemm lowrank m={m} r={rank} {dtype}")
+    b1, b2 = 64, 128
+    n, k = 5 * b1, 3 * b2
+    w, tmap = random_case(m + rank, n, k, b1, b2, dtype)
+    rng = np.random.default_rng(m * 3 + rank)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), dtype)
+    t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, "idx2")
+    xt, tt = upload(x, dtype), torch.from_numpy(t).to(dev())
+    y = hb.gemm_lowrank(P, xt, tt, upload(u, dtype))
+    y0 = hb.gemm_lowrank(P, xt, tt, upload(np.zeros_like(u), dtype))
+    yr0 = hb.gemm_lowrank(P, xt, tt[:, :0], upload(u, dtype)[:, :0])
+    yg = hb.gemm(P, xt)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, yg) and torch.equal(yr0, yg)
+    yref, s = oracle.ref_lowrank(oracle.prune(w, tmap, b1, b2), x, t, u, dtype)
+    assert_close(y.cpu().numpy(), yref, s, what="gemm lowrank")
+
+
+def test_gemm_lowrank_small_m_and_strides():
+    """8 tokens or fewer run the fused decode kernel (bitwise the decode
+    entry point); above, a y with a row stride larger than n keeps its
+    padding."""
+    torch = _torch()
+    note("gemm lowrank m <= 8 and strided y")
+    b1, b2, n, k, rank = 128, 128, 256, 512, 32
+    w, tmap = random_case(31, n, k, b1, b2, "bf16")
+    rng = np.random.default_rng(31)
+    u = upload(wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, "bf16"), "bf16")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    for m in (1, 8):
+        x = upload(wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), "bf16"), "bf16")
+        t = torch.randn((m, rank), device=dev())
+        assert torch.equal(hb.gemm_lowrank(P, x, t, u), hb.gemv_lowrank(P, x, t, u))
+    m = 70
+    xb = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), "bf16")
+    tb = rng.standard_normal((m, rank)).astype(np.float32)
+    ybig = torch.full((m, n + 36), 3.0, device=dev())
+    hb.gemm_lowrank(P, upload(xb, "bf16"), torch.from_numpy(tb).to(dev()), u, out=ybig[:, :n])
+    torch.cuda.synchronize()
+    assert torch.all(ybig[:, n:] == 3.0)
+    yref, s = oracle.ref_lowrank(oracle.prune(w, tmap, b1, b2), xb, tb, hb.tensor_to_bits(u), "bf16")
+    assert_close(ybig[:, :n].cpu().numpy(), yref, s, what="strided gemm lowrank")
+
+
+@pytest.mark.parametrize("m", [12, 40, 100, 256])
+def test_sparse_lowrank_prefill_qwen14b_sampled(m):
+    """17408 x 5120 (64 x 64 tiles, 60% 2:4) + rank 64: the projection on
+    the matrix cores (above 16 tokens) and the matrix-core product with the
+    T U^T epilogue, through each kernel variant (register-fed with one and
+    two row groups, k_gemm at 65-128 tokens, the LDS-fed kernel), checked on
+    sampled tile rows; the oracle computes T itself and the bound carries
+    T's own error through |U|."""
+    torch = _torch()
+    note(f"sparse + low-rank prefill qwen14b m={m}")
+    mat, w, tmap = workload_matrix(5, 0)
+    rank = 64
+    rng = np.random.default_rng(65)
+    v = wl.float32_to_bits(rng.standard_normal((rank, mat.k)).astype(np.float32) * 0.02, "bf16")
+    u = wl.float32_to_bits(rng.standard_normal((mat.n, rank)).astype(np.float32) * 0.02, "bf16")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    y = hb.sparse_lowrank_gemm(P, upload(v, "bf16"), upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
+    t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
+    tile_rows = sample_tile_rows(mat, 4, 65)
+    rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
+    sub = oracle.prune(w[rows], tmap[tile_rows], mat.b1, mat.b2)
+    yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
+    extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
+    assert_close(y[:, rows], yref, s, extra=extra, what="prefill sparse + low-rank")
+
+
+def test_gemm_lowrank_output_16bit():
+    """A 16-bit y is rounded once, after the low-rank term is added."""
+    torch = _torch()
+    note("gemm lowrank bf16 out")
+    w, tmap = random_case(41, 256, 512, 128, 128, "bf16")
+    rng = np.random.default_rng(41)
+    x = wl.float32_to_bits(rng.standard_normal((96, 512)).astype(np.float32), "bf16")
+    t = rng.standard_normal((96, 64)).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((256, 64)).astype(np.float32) * 0.05, "bf16")
+    P = pack_gpu(w, tmap, 128, 128, "bf16", "idx2")
+    y = hb.gemm_lowrank(P, upload(x, "bf16"), torch.from_numpy(t).to(dev()), upload(u, "bf16"),
+                        out_dtype=torch.bfloat16)
+    yb = oracle.widen(hb.tensor_to_bits(y), "bf16")
+    yref, s = oracle.ref_lowrank(oracle.prune(w, tmap, 128, 128), x, t, u, "bf16")
+    assert_close(yb, yref, s, extra=np.abs(yref) * 2.0 ** -8 + 2.0 ** -133, what="bf16 out low-rank")
 
 
 def test_gemv_output_16bit():
