@@ -52,7 +52,7 @@ HBM_PEAK_GBS = 8000.0
 # FETCH_SIZE + WRITE_SIZE scaled by a plain 128 MiB copy's readings
 # (profiles/k_gemv_llama8b_up_14336x4096_m1_hbm_traffic.md).  Valid for the
 # kernel as profiled; re-measure after changing it.
-TRAFFIC_BYTES_PER_LAUNCH = 81_898_496
+TRAFFIC_BYTES_PER_LAUNCH = 81_907_712
 MFMA_PEAK_BF16_TFLOPS = 2500.0
 
 
