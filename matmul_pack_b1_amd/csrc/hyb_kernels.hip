@@ -729,21 +729,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_grouped(const uint16_t* __r
 
 // ---------------------------------------------------------------- GEMM ----
 //
-// Y[m, n] = sum_k X[m, k] W'[n, k] for any M on the matrix cores.
-// A workgroup is 4 wavefronts arranged WN (along n) x WK (along K).  Each
-// wavefront owns 64 rows (four 16-row slabs) and, over its share of the K
-// steps, multiplies them with the workgroup's BM = 16 * MB tokens.  A K step
-// is 64 columns.  A dense slab piece is two 16x16x32 MFMA A operands taken
-// straight from the dense stream; a sparse slab piece is one
-// v_smfmac_*_16x16x64 A operand (32 kept values per row) with its 2-bit
-// indices: the stored value chunk and its idx2 word are exactly that
-// instruction's operand layout, so sparse tiles run on the sparse matrix
-// cores at twice the dense rate with no expansion.  Both kinds take the same
-// B operands (X[m][8q..8q+7] and X[m][32+8q..32+8q+7] for lane group q),
-// read from a double-buffered LDS tile of X.  A operands are raw buffer
-// loads one K step ahead (branch-free, as in the decode kernel).  With
-// WK > 1 the partial sums of the K groups are added in a fixed order through
-// LDS, so results are reproducible.
+// Y[m, n] = sum_k X[m, k] W'[n, k] for any M on the matrix cores
+// (k_gemm_rx up to 128 tokens, k_gemm_lds above).  A K step is 64 columns
+// and a wavefront's unit is 64 weight rows (four 16-row slabs).  A sparse
+// slab piece is one v_smfmac_*_16x16x64 A operand (32 kept values per row)
+// with its 2-bit indices: the stored value chunk and its idx2 word are
+// exactly that instruction's operand layout, so sparse tiles run on the
+// sparse matrix cores with no expansion.  Both kinds take the same B
+// operands (X[m][8q..8q+7] and X[m][32+8q..32+8q+7] for lane group q).
+// Partial sums are always added in a fixed order, so results are
+// reproducible.
 
 struct GemmDims {
   int64_t ldx, ldy;
@@ -819,11 +814,6 @@ __device__ __forceinline__ void lr_block(f32x4_t (&c)[NS][NT], const GemmDims& d
   }
 }
 
-struct GemmAStage {
-  uint4 a[4][2];     // per slab: dense chunks 2kb, 2kb+1, or the sparse value chunk in a[.][0]
-  uint32_t word[4];  // per slab: the sparse chunk's metadata word
-};
-
 template <int DT>
 __device__ __forceinline__ f32x4_t smfmac16x16x64(uint4 a, uint4 b0, uint4 b1, uint32_t idx, f32x4_t c) {
   const uint32_t bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
@@ -855,226 +845,6 @@ __device__ __forceinline__ uint32_t idx2_word(uint32_t word) {
   }
 }
 
-// A operands of one K step for the wavefront's four slabs.  The resources
-// cover the four slab pieces of the tile; the second chunk of a sparse slab
-// and the metadata of a dense one fall outside and read as zero with no
-// memory access, as does everything for an out-of-range slot.
-template <int B2>
-__device__ __forceinline__ void gemm_load_a(GemmAStage& st, int32_t ti, int kb,
-                                            const uint4* __restrict__ dense,
-                                            const uint4* __restrict__ val,
-                                            const uint16_t* __restrict__ meta, const GemmDims& d,
-                                            int rs0, int lane) {
-  const bool is_dense = ti >= 0;
-  const int32_t slot = is_dense ? ti : ~ti;
-  const bool ok = is_dense ? (slot < d.n_dense) : (slot < d.n_sparse);
-  const int64_t tile = int64_t(d.b1) * B2;
-  const int32_t slab_bytes = is_dense ? 32 * B2 : 16 * B2;
-  const char* base = is_dense
-      ? reinterpret_cast<const char*>(dense) + (int64_t(slot) * tile + int64_t(rs0) * 16 * B2) * 2
-      : reinterpret_cast<const char*>(val) + (int64_t(slot) * (tile / 2) + int64_t(rs0) * 8 * B2) * 2;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, ok ? 4 * slab_bytes : 0);
-  const int32_t c0 = is_dense ? 2 * kb * 1024 : kb * 1024;
-  const int32_t c1 = is_dense ? c0 + 1024 : 0x40000000;
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    st.a[sl][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-        r, sl * slab_bytes + c0 + lane * 16, 0, HYB_GEMM_W_NT ? HYB_W_AUX : 0));
-    st.a[sl][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-        r, sl * slab_bytes + c1 + lane * 16, 0, HYB_GEMM_W_NT ? HYB_W_AUX : 0));
-  }
-  const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs0) * B2) * 2;
-  const __amdgpu_buffer_rsrc_t mr = make_rsrc(mbase, (ok && !is_dense) ? 4 * 2 * B2 : 0);
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl)
-    st.word[sl] = __builtin_amdgcn_raw_buffer_load_b16(mr, sl * 2 * B2 + lane * (B2 / 32) + kb * 2, 0, 0);
-}
-
-template <int WK, int MB, int WN>
-struct GemmSmem {
-  static constexpr int kRow = 72;  // padded X row in the LDS tile (elements)
-  static constexpr int kXsBytes = WK * 2 * 16 * MB * kRow * 2;
-  static constexpr int kRedBytes = (WK - 1) * WN * 4 * MB * 64 * 16;
-  static constexpr int kBytes = kXsBytes > kRedBytes ? kXsBytes : kRedBytes;
-};
-
-template <int B2, int DT, int META, int WN, int WK, int MB>
-__global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
-                                              const uint4* __restrict__ val,
-                                              const uint16_t* __restrict__ meta,
-                                              const int32_t* __restrict__ tidx,
-                                              const uint16_t* __restrict__ x,
-                                              void* __restrict__ y, GemmDims d) {
-  static_assert(WN * WK == 4, "four wavefronts per workgroup");
-  using Smem = GemmSmem<WK, MB, WN>;
-  constexpr int BM = 16 * MB;
-  constexpr int kRow = Smem::kRow;
-  constexpr int kStepsPerTile = B2 / 64;
-  __shared__ __attribute__((aligned(16))) char smem[Smem::kBytes];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave % WN, wk = wave / WN;
-  const int q = lane >> 4;
-  const int32_t n0 = int32_t(blockIdx.x) * 64 * WN + wn * 64;   // first row of this wavefront
-  const int32_t m0 = int32_t(blockIdx.y) * BM;
-  const bool rows_ok = n0 < d.n;
-  const int32_t tn = n0 / d.b1;
-  const int rs0 = (n0 - tn * d.b1) / 16;
-  const int32_t steps = d.tiles_k * kStepsPerTile;
-  const int32_t s0 = (wk * steps) / WK;
-  const int32_t cnt = ((wk + 1) * steps) / WK - s0;
-  const int32_t iters = (steps + WK - 1) / WK;   // same trip count in every K group
-  const int32_t* __restrict__ trow = tidx + int64_t(tn) * d.tiles_k;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem) + wk * 2 * BM * kRow;
-
-  // X tile loads of this K group: BM rows x 64 columns = BM * 8 pieces over
-  // the 64 * WN threads of the group; rows >= M read as zero.
-  constexpr int kPieces = BM * 8;
-  constexpr int kXr = (kPieces + 64 * WN - 1) / (64 * WN);
-  const int gt = wn * 64 + lane;  // thread index inside the K group
-  const int32_t mrows = d.m - m0 < BM ? d.m - m0 : BM;
-  auto load_x = [&](int32_t it, uint4 (&xr)[kXr]) {
-    const bool live = it < cnt;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(x + int64_t(m0) * d.ldx + int64_t(s0 + it) * 64,
-                                               live ? int32_t(mrows * d.ldx * 2) : 0);
-#pragma unroll
-    for (int i = 0; i < kXr; ++i) {
-      const int pc = gt + 64 * WN * i;
-      const int row = pc >> 3, c8 = pc & 7;
-      const int off = (pc < kPieces) ? int(row * d.ldx * 2) + c8 * 16 : 0x40000000;
-      xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    }
-  };
-  auto store_x = [&](int buf, const uint4 (&xr)[kXr]) {
-#pragma unroll
-    for (int i = 0; i < kXr; ++i) {
-      const int pc = gt + 64 * WN * i;
-      if (pc < kPieces) {
-        const int row = pc >> 3, c8 = pc & 7;
-        *reinterpret_cast<uint4*>(xs + buf * BM * kRow + row * kRow + c8 * 8) = xr[i];
-      }
-    }
-  };
-  constexpr int32_t kNone = INT32_MIN;
-  auto tile_index = [&](int32_t it) -> int32_t {
-    if (!rows_ok || it >= cnt) return kNone;
-    return trow[(s0 + it) / kStepsPerTile];
-  };
-
-  f32x4_t acc[4][MB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const GemmAStage& a, int32_t ti, int buf) {
-    if (ti == kNone) return;
-    const bool is_dense = ti >= 0;
-    if (is_dense ? (ti >= d.n_dense) : (~ti >= d.n_sparse)) return;
-    uint32_t idx[4];
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) idx[sl] = idx2_word<META>(a.word[sl]);
-    const uint16_t* xb = xs + buf * BM * kRow;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint16_t* xrow = xb + (mb * 16 + (lane & 15)) * kRow + q * 8;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(xrow);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(xrow + 32);
-      if (is_dense) {
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-          acc[sl][mb] = mfma16x16x32<DT>(a.a[sl][0], b0, acc[sl][mb]);
-          acc[sl][mb] = mfma16x16x32<DT>(a.a[sl][1], b1, acc[sl][mb]);
-        }
-      } else {
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) acc[sl][mb] = smfmac16x16x64<DT>(a.a[sl][0], b0, b1, idx[sl], acc[sl][mb]);
-      }
-    }
-  };
-
-  // Two-stage ring, unrolled by two so stage registers are never copied.
-  GemmAStage A0, A1;
-  uint4 xr[kXr];
-  int32_t t0 = tile_index(0);
-  gemm_load_a<B2>(A0, t0, (s0 + 0) % kStepsPerTile, dense, val, meta, d, rs0, lane);
-  load_x(0, xr);
-  store_x(0, xr);
-  __syncthreads();
-  for (int32_t it = 0; it < iters; it += 2) {
-    const int32_t t1 = tile_index(it + 1);
-    gemm_load_a<B2>(A1, t1, (s0 + it + 1) % kStepsPerTile, dense, val, meta, d, rs0, lane);
-    load_x(it + 1, xr);
-    compute(A0, t0, 0);
-    store_x(1, xr);
-    __syncthreads();
-    if (it + 1 >= iters) break;
-    t0 = tile_index(it + 2);
-    gemm_load_a<B2>(A0, t0, (s0 + it + 2) % kStepsPerTile, dense, val, meta, d, rs0, lane);
-    load_x(it + 2, xr);
-    compute(A1, t1, 1);
-    store_x(0, xr);
-    __syncthreads();
-  }
-
-  // Partial sums of K groups 1..WK-1 go through LDS to group 0, which adds
-  // them in group order.
-  if constexpr (WK > 1) {
-    float* red = reinterpret_cast<float*>(smem);
-    if (wk > 0) {
-      float* dst = red + ((wk - 1) * WN + wn) * (4 * MB * 64 * 4);
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          *reinterpret_cast<f32x4_t*>(dst + ((sl * MB + mb) * 64 + lane) * 4) = acc[sl][mb];
-    }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int g = 1; g < WK; ++g) {
-      const float* src = red + ((g - 1) * WN + wn) * (4 * MB * 64 * 4);
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[sl][mb] += *reinterpret_cast<const f32x4_t*>(src + ((sl * MB + mb) * 64 + lane) * 4);
-    }
-  }
-
-  if (!rows_ok) return;
-  if (d.rank > 0) lr_block<DT, 4, MB>(acc, d, n0, m0, lane);
-  // acc[sl][mb] lane L holds rows n0 + 16 sl + 4 (L/16) + 0..3 of token
-  // m0 + 16 mb + L%16.
-  const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int64_t m = int64_t(m0) + mb * 16 + (lane & 15);
-    if (m >= d.m) continue;
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const int64_t n = int64_t(n0) + sl * 16 + q * 4;
-      const f32x4_t v = acc[sl][mb];
-      const int64_t base = m * d.ldy + n;
-      if (d.ydt == HYB_F32) {
-        float* dst = static_cast<float*>(y) + base;
-        if (vec_ok) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = v[e];
-        }
-      } else {
-        uint16_t* dst = static_cast<uint16_t*>(y) + base;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
-      }
-    }
-  }
-}
-
 // --------------------------------------------------- GEMM (register-fed) --
 //
 // Memory-bound range (17 to a few hundred tokens): the weights must stream
@@ -1083,7 +853,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ dense,
 // tokens; its WAVES wavefronts split the K steps into contiguous ranges, as
 // the decode kernel's do, and never synchronise inside the K walk.  Each
 // lane loads exactly its operands straight into a STAGES-deep register
-// ring: the slab pieces (as in k_gemm) and, from L2, its B operands
+// ring: its slab pieces and, from L2, its B operands
 // X[m][8q..8q+7] and X[m][32+8q..32+8q+7] of every token block.  Past the
 // end of a wavefront's range, or past the last token row, the loads fall
 // outside the buffer resources and read zero, so every trip issues the same
@@ -2091,16 +1861,6 @@ hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed*
 
 namespace {
 
-template <int B2, int DT, int META, int WN, int WK, int MB>
-hipError_t gemm_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
-  const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
-  if (gm > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(unsigned((L.n + 64 * WN - 1) / (64 * WN)), unsigned(gm));
-  hipLaunchKernelGGL((k_gemm<B2, DT, META, WN, WK, MB>), grid, dim3(256), 0, s, q.dense, q.val, q.meta,
-                     q.tidx, q.x, q.y, d);
-  return hipGetLastError();
-}
-
 template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
 hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
@@ -2146,9 +1906,8 @@ int device_cus() {
 }
 
 // Workgroup shape by token count.  Up to 128 tokens the register-fed
-// kernel k_gemm_rx runs (64 rows per workgroup, wavefronts splitting K),
-// except at 65..128 tokens when its 64-row workgroups do not fit in one
-// round over the CUs (then k_gemm, 2 x 2 wavefronts).  From 129 tokens one
+// kernel k_gemm_rx runs (64 or 128 rows per workgroup, wavefronts
+// splitting K) in the shape that fills the CUs best.  From 129 tokens one
 // of four LDS-fed shapes runs, 256 weight rows by BM = 256,
 // 192, 128 or 64 tokens.  Every workgroup walks all of K, so the time is
 // the number of rounds of workgroups over the compute units times the time
@@ -2159,28 +1918,38 @@ template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   const int64_t cus = device_cus();
   const int64_t groups = L.n / 64;  // 64-row workgroups of the register-fed kernel
-  if (m <= 64) {
+  if (m <= 16) {
     // Eight wavefronts (one workgroup per CU) when the 64-row groups fit in
-    // one round.  Otherwise up to 16 tokens four wavefronts (two workgroups
-    // per CU), and from 17 tokens two row groups per workgroup on four
-    // wavefronts, which halves the reads of X (measured on 17408 x 5120:
-    // 1.0-1.34x at 17-64 tokens; with one round of row groups the loss of
-    // wavefronts costs more than the X reads save).
-    if (groups <= cus) {
-      if (m <= 16) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
-      return m <= 32 ? gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s)
-                     : gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
-    }
-    if (m <= 16) return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
-    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
+    // one round, else four (two workgroups per CU).
+    if (groups <= cus) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
+    return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
   }
   if (m <= 128) {
-    // 128 tokens per wavefront need a SIMD to themselves: only when the row
-    // groups fit in one round.
-    if (groups <= cus) return gemm_rx_go<B2, DT, META, 8, 4, 2>(L, q, m, d, s);
-    // (k_gemm has no 4:8 path: 4:8 weights stay on the register-fed kernel)
-    if constexpr (META == HYB_META_MASK8) return gemm_rx_go<B2, DT, META, 8, 4, 2>(L, q, m, d, s);
-    else return gemm_go<B2, DT, META, 2, 2, 8>(L, q, m, d, s);
+    // Register-fed shapes (token blocks of 16 per workgroup, wavefronts,
+    // 64-row groups per workgroup).  The fewest rounds of workgroups over
+    // the CUs wins, then the most workgroups; on a tie the earlier entry
+    // (one row group before two, then the smaller token block).  Measured
+    // on 1024 to 17408 rows at 17-128 tokens: the pick is the fastest shape
+    // or within 3% of it.
+    constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
+    int best = 0;
+    int64_t best_rounds = 0, best_wgs = 0;
+    for (int i = 0; i < 5; ++i) {
+      const int64_t wgs = ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
+      const int64_t rounds = (wgs + cus - 1) / cus;
+      if (i == 0 || rounds < best_rounds || (rounds == best_rounds && wgs > best_wgs)) {
+        best = i;
+        best_rounds = rounds;
+        best_wgs = wgs;
+      }
+    }
+    switch (best) {
+      case 0: return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
+      case 1: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);
+      case 2: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
+      case 3: return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, s);
+      default: return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
+    }
   }
   const int64_t gn = (L.n + 255) / 256;
   auto cost = [&](int64_t bm, double step) {
