@@ -379,7 +379,7 @@ def test_sparse_lowrank_prefill_qwen14b_sampled(m):
     """17408 x 5120 (64 x 64 tiles, 60% 2:4) + rank 64: the projection on
     the matrix cores (above 16 tokens) and the matrix-core product with the
     T U^T epilogue, through each kernel variant (register-fed with one and
-    two row groups, k_gemm at 65-128 tokens, the LDS-fed kernel), checked on
+    two row groups, 65-128 tokens, the LDS-fed kernel), checked on
     sampled tile rows; the oracle computes T itself and the bound carries
     T's own error through |U|."""
     torch = _torch()
