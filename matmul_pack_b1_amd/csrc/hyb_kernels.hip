@@ -331,57 +331,70 @@ __global__ __launch_bounds__(256) void k_pack(PackParams p) {
 
 // -------------------------------------------------------------- unpack ----
 
+// The slab's 16 rows are assembled row-major in a wavefront-private LDS
+// buffer (LDS accesses of one wavefront complete in order, so no barrier is
+// needed; the wave barrier keeps the compiler from moving them), then
+// stored as whole row segments: each store instruction writes 1 KiB of
+// contiguous row bytes instead of 64-byte halves of 16 rows.
 template <int B2>
 __global__ __launch_bounds__(256) void k_unpack(PackParams p) {
+  constexpr int kRow = B2 + 8;  // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4][16 * kRow];
   const int lane = threadIdx.x & 63;
-  const int rs = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int rs = blockIdx.y * 4 + wv;
   const int64_t t = blockIdx.x;
   const int64_t tn = t / p.tiles_k, tk = t - tn * p.tiles_k;
   const int32_t ti = p.tidx[t];
-  const int64_t row = tn * p.b1 + rs * 16 + (lane & 15);
-  uint16_t* wrow = const_cast<uint16_t*>(p.w) + row * p.ldw + tk * B2;
+  const int r = lane & 15, q = lane >> 4;
+  uint16_t* buf = stage[wv];
   const int64_t tile = int64_t(p.b1) * B2;
   if (ti >= 0) {
     if (ti >= p.n_dense) return;
     const uint16_t* src = p.dense + ti * tile + int64_t(rs) * 16 * B2 + lane * 8;
 #pragma unroll
-    for (int c = 0; c < B2 / 32; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + c * 512);
-      *reinterpret_cast<uint4*>(wrow + c * 32 + (lane >> 4) * 8) = v;
-    }
-    return;
-  }
-  const int64_t s = ~int64_t(ti);
-  if (s >= p.n_sparse) return;
-  const uint16_t* vsrc = p.val + s * (tile / 2) + int64_t(rs) * 8 * B2 + lane * 8;
-  const uint16_t* msrc = p.meta + s * (tile / 16) + int64_t(rs) * B2 + lane * (B2 / 64);
+    for (int c = 0; c < B2 / 32; ++c)
+      *reinterpret_cast<uint4*>(buf + r * kRow + c * 32 + q * 8) = *reinterpret_cast<const uint4*>(src + c * 512);
+  } else {
+    const int64_t s = ~int64_t(ti);
+    if (s >= p.n_sparse) return;
+    const uint16_t* vsrc = p.val + s * (tile / 2) + int64_t(rs) * 8 * B2 + lane * 8;
+    const uint16_t* msrc = p.meta + s * (tile / 16) + int64_t(rs) * B2 + lane * (B2 / 64);
 #pragma unroll
-  for (int c = 0; c < B2 / 64; ++c) {
-    const uint4 v = *reinterpret_cast<const uint4*>(vsrc + c * 512);
-    const uint32_t word = msrc[c];
-    const uint32_t pv[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[8];
-    if (p.meta_kind == HYB_META_MASK8) {
+    for (int c = 0; c < B2 / 64; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(vsrc + c * 512);
+      const uint32_t word = msrc[c];
+      const uint32_t pv[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
+      if (p.meta_kind == HYB_META_MASK8) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[j] = __builtin_amdgcn_perm(v.y, v.x, expand8_selector(word & 0xFFu, j));
-        o[4 + j] = __builtin_amdgcn_perm(v.w, v.z, expand8_selector(word >> 8, j));
+        for (int j = 0; j < 4; ++j) {
+          o[j] = __builtin_amdgcn_perm(v.y, v.x, expand8_selector(word & 0xFFu, j));
+          o[4 + j] = __builtin_amdgcn_perm(v.w, v.z, expand8_selector(word >> 8, j));
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t i0, i1;
+          nibble_positions((word >> (4 * g)) & 0xFu, p.meta_kind, i0, i1);
+          o[2 * g] = __builtin_amdgcn_perm(0u, pv[g], scatter_selector(0, i0, i1));
+          o[2 * g + 1] = __builtin_amdgcn_perm(0u, pv[g], scatter_selector(2, i0, i1));
+        }
       }
-      uint16_t* dst = wrow + c * 64 + (lane >> 4) * 16;
+      uint16_t* dst = buf + r * kRow + c * 64 + q * 16;
       *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-      continue;
     }
+  }
+  __builtin_amdgcn_wave_barrier();
+  constexpr int kLanesPerRow = B2 / 8;             // 16-byte pieces per row
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  const int rr = lane / kLanesPerRow, cc = (lane % kLanesPerRow) * 8;
+  uint16_t* wbase = const_cast<uint16_t*>(p.w) + (tn * p.b1 + rs * 16) * p.ldw + tk * B2 + cc;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t i0, i1;
-      nibble_positions((word >> (4 * q)) & 0xFu, p.meta_kind, i0, i1);
-      o[2 * q] = __builtin_amdgcn_perm(0u, pv[q], scatter_selector(0, i0, i1));
-      o[2 * q + 1] = __builtin_amdgcn_perm(0u, pv[q], scatter_selector(2, i0, i1));
-    }
-    uint16_t* dst = wrow + c * 64 + (lane >> 4) * 16;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+  for (int i = 0; i < 16 / kRowsPerStore; ++i) {
+    const int row = i * kRowsPerStore + rr;
+    *reinterpret_cast<uint4*>(wbase + int64_t(row) * p.ldw) = *reinterpret_cast<const uint4*>(buf + row * kRow + cc);
   }
 }
 
