@@ -688,20 +688,14 @@ def lowrank(hb, torch, wl, dev, meta, rank=64):
 
 
 def sweep(hb, torch, wl, dev, rotate, args):
-    """All workloads: GEMV / GEMM time against the same kernel all-dense."""
+    """All workloads: GEMV / GEMM time against the same kernel all-dense
+    (graph bursts over rotating copies, as the main measurement)."""
     results = []
 
-    def timed(fn, iters, copies):
-        ev = []
-        for i in range(iters + 5):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn(copies[i % len(copies)])
-            e.record()
-            if i >= 5:
-                ev.append((s, e))
-        torch.cuda.synchronize()
-        return statistics.mean([s.elapsed_time(e) for s, e in ev]) * 1e3
+    def timed(fn, copies):
+        # graph burst of 2C launches over the C rotating copies
+        n = len(copies)
+        return graph_us(torch, lambda c: [fn(copies[(3 * i) % n]) for i in range(c)], 2 * n)
 
     for cfg in (1, 2, 3, 4, 5):
         W = wl.workload(cfg)
@@ -723,7 +717,7 @@ def sweep(hb, torch, wl, dev, rotate, args):
                     elif cfg == 5:
                         fns.append(("gemm_mfma", lambda P: hb.gemm_mfma(P, x, out=y)))
                     for fname, fn in fns:
-                        us = timed(fn, 50, copies)
+                        us = timed(fn, copies)
                         results.append({"config": cfg, "matrix": mat.name, "kind": kind, "m": m, "fn": fname,
                                         "us": round(us, 3), "alg_bytes": alg_bytes(L, m),
                                         "GBps": round(alg_bytes(L, m) / us / 1e3, 1),
