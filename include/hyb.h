@@ -159,8 +159,10 @@ hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x
                     int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                     void* stream);
 
-/* Grouped decode product: one launch multiplies the same x (0 <= m <= 16
- * tokens) by `count` packed matrices, Y_g[i, :] = W'_g X[i, :].  A layer's
+/* Grouped decode product: one launch (two when the matrices' sizes call
+ * for different wavefront counts per slab, as hyb_gemv would pick for each
+ * alone) multiplies the same x (0 <= m <= 16 tokens) by `count` packed
+ * matrices, Y_g[i, :] = W'_g X[i, :].  A layer's
  * projections that read the same activations (q, k and v; gate and up) carry
  * their own tile maps and sparsities (PATCH, gist.science, section 3
  * "Contributi Chiave": attention stays denser, MLP matrices sparser), and the
@@ -221,7 +223,8 @@ hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const
 
 /* Sparse + low-rank product for any m >= 0: Y = X W'^T + T U^T as for
  * hyb_gemv_lowrank (3BASiL sections 1 and 4), with the same arguments and
- * checks.  m <= 8 runs the fused decode kernel; larger m the matrix-core
+ * checks.  The fused decode kernel runs where hyb_gemm would run the decode
+ * kernel (m <= 8, or m <= 16 on short matrices); larger m the matrix-core
  * kernels, which add T U^T to each output tile before it is stored (fp32
  * products and sums, rank walked in order), so 16-bit outputs are rounded
  * once.  rank 0 is plain hyb_gemm. */
@@ -232,8 +235,9 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
 
 /* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same
- * arguments as hyb_gemv; m <= 8 runs the decode kernel, larger m the
- * matrix-core kernels. */
+ * arguments as hyb_gemv; m <= 8 runs the decode kernel (also m <= 16 when
+ * the matrix has fewer than two 16-row slabs per compute unit), larger m
+ * the matrix-core kernels. */
 hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x,
                     int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                     void* stream);

@@ -332,7 +332,7 @@ hyb_status check_mfma_limits(int32_t m, int64_t ldx) {
 hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                             int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
                             void* y, int32_t y_dtype, int64_t ldy, void* stream) {
-  if (m >= 0 && m <= hyb::kGemvCrossoverM)
+  if (m >= 0 && (m <= hyb::kGemvCrossoverM || (layout && m <= hyb::kMaxGemvM && hyb::gemv_preferred(*layout, m))))
     return hyb_gemv_lowrank(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
   if (st != HYB_OK) return st;
@@ -359,7 +359,8 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
 
 hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                     int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
-  if (m >= 0 && m <= hyb::kGemvCrossoverM) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (m >= 0 && (m <= hyb::kGemvCrossoverM || (layout && m <= hyb::kMaxGemvM && hyb::gemv_preferred(*layout, m))))
+    return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 

@@ -28,6 +28,10 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
 // Decode product plus the low-rank term T U^T (hyb_gemv_lowrank).
 hipError_t launch_lr_project(const void* v, int64_t ldv, int rank, int64_t k, int dtype, const void* x, int m,
                              int64_t ldx, float* t, int64_t ldt, hipStream_t s);
+// Whether hyb_gemm should run m tokens on the decode kernel (m <= 8, or
+// m <= 16 on a matrix short enough that the decode kernel splits each tile
+// row sixteen ways).
+bool gemv_preferred(const hyb_layout& L, int m);
 hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
                                const float* t, int64_t ldt, const void* u, int64_t ldu, int rank, void* y,
                                int y_dtype, int64_t ldy, hipStream_t s);

@@ -1719,6 +1719,19 @@ namespace {
 constexpr int kGemvWaves = HYB_GEMV_WAVES;
 constexpr int kGemvStages = HYB_GEMV_STAGES;
 
+int device_cus();
+
+// Wavefronts per slab of the decode kernels.  Four when the slabs fill the
+// CUs at least twice (each wavefront walks a quarter of the tile row); a
+// shorter matrix has too few workgroups to keep enough loads in flight, so
+// its tile row is split eight ways (up to 4 tokens) or sixteen (more
+// tokens).  Measured on 1024 and 4096 rows: 1.2x at 1 token, 1.2-1.3x at 4,
+// 1.8-1.9x at 16; on 14336 rows four stay best.
+int gemv_waves(int64_t slabs, int m) {
+  if (slabs >= 2 * int64_t(device_cus())) return kGemvWaves;
+  return m <= 4 ? 8 : 16;
+}
+
 struct GemvPtrs {
   const uint4* dense;
   const uint4* val;
@@ -1728,29 +1741,40 @@ struct GemvPtrs {
   void* y;
 };
 
-template <int MT, int DT, int META, bool LR>
+template <int MT, int DT, int META, bool LR, int W>
 void gemv_b2(int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
-  const dim3 block(64 * kGemvWaves);
+  const dim3 block(64 * W);
   switch (b2) {
     case 64:
-      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, kGemvWaves, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, W, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
       break;
     case 128:
-      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, kGemvWaves, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, W, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
       break;
     default:
-      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, kGemvWaves, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, W, kGemvStages, LR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
       break;
   }
 }
 
+// MT-token variant with the wavefront count of gemv_waves.
+template <int MT, int DT, int META, bool LR>
+void gemv_w(int waves, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
+  if constexpr (MT <= 4) {
+    if (waves == 8) return gemv_b2<MT, DT, META, LR, 8>(b2, grid, s, q, d);
+  } else {
+    if (waves == 16) return gemv_b2<MT, DT, META, LR, 16>(b2, grid, s, q, d);
+  }
+  gemv_b2<MT, DT, META, LR, kGemvWaves>(b2, grid, s, q, d);
+}
+
 template <int DT, int META, bool LR>
-void gemv_mt(int m, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
-  if (m <= 1) gemv_b2<1, DT, META, LR>(b2, grid, s, q, d);
-  else if (m <= 2) gemv_b2<2, DT, META, LR>(b2, grid, s, q, d);
-  else if (m <= 4) gemv_b2<4, DT, META, LR>(b2, grid, s, q, d);
-  else if (m <= 8) gemv_b2<8, DT, META, LR>(b2, grid, s, q, d);
-  else gemv_b2<16, DT, META, LR>(b2, grid, s, q, d);
+void gemv_mt(int m, int waves, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
+  if (m <= 1) gemv_w<1, DT, META, LR>(waves, b2, grid, s, q, d);
+  else if (m <= 2) gemv_w<2, DT, META, LR>(waves, b2, grid, s, q, d);
+  else if (m <= 4) gemv_w<4, DT, META, LR>(waves, b2, grid, s, q, d);
+  else if (m <= 8) gemv_w<8, DT, META, LR>(waves, b2, grid, s, q, d);
+  else gemv_w<16, DT, META, LR>(waves, b2, grid, s, q, d);
 }
 
 }  // namespace
@@ -1778,14 +1802,15 @@ hipError_t launch_gemv_impl(const hyb_layout& L, const hyb_packed& P, const void
   d.ldu = ldu;
   d.rank = rank;
   const dim3 grid(unsigned(L.n / 16));
+  const int w = gemv_waves(L.n / 16, m);
   if (L.dtype == HYB_BF16) {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, L.b2, grid, s, q, d);
-    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, L.b2, grid, s, q, d);
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, w, L.b2, grid, s, q, d);
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, w, L.b2, grid, s, q, d);
+    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, w, L.b2, grid, s, q, d);
   } else {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, L.b2, grid, s, q, d);
-    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, L.b2, grid, s, q, d);
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, w, L.b2, grid, s, q, d);
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, w, L.b2, grid, s, q, d);
+    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, w, L.b2, grid, s, q, d);
   }
   return hipGetLastError();
 }
@@ -1797,6 +1822,14 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
   return launch_gemv_impl<false>(L, P, x, m, ldx, y, y_dtype, ldy, nullptr, 0, nullptr, 0, 0, s);
 }
 
+bool gemv_preferred(const hyb_layout& L, int m) {
+  if (m <= kGemvCrossoverM) return true;
+  // 9-16 tokens on a matrix short enough for 16 wavefronts per slab: the
+  // decode kernel beats the register-fed product there (1024 and 4096 rows
+  // at 16 tokens: 11-12 us against 15-16 us)
+  return m <= kMaxGemvM && gemv_waves(L.n / 16, m) == 16;
+}
+
 hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
                                const float* t, int64_t ldt, const void* u, int64_t ldu, int rank, void* y,
                                int y_dtype, int64_t ldy, hipStream_t s) {
@@ -1805,71 +1838,96 @@ hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const v
 
 namespace {
 
-template <int MT, int DT, int META>
+template <int MT, int DT, int META, int W>
 void gemv_grouped_b2(int b2, dim3 grid, hipStream_t s, const uint16_t* x, const GemvDims& d, const GemvGroup& g) {
-  const dim3 block(64 * kGemvWaves);
+  const dim3 block(64 * W);
   switch (b2) {
     case 64:
-      hipLaunchKernelGGL((k_gemv_grouped<MT, 64, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, x, d, g);
+      hipLaunchKernelGGL((k_gemv_grouped<MT, 64, DT, META, W, kGemvStages>), grid, block, 0, s, x, d, g);
       break;
     case 128:
-      hipLaunchKernelGGL((k_gemv_grouped<MT, 128, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, x, d, g);
+      hipLaunchKernelGGL((k_gemv_grouped<MT, 128, DT, META, W, kGemvStages>), grid, block, 0, s, x, d, g);
       break;
     default:
-      hipLaunchKernelGGL((k_gemv_grouped<MT, 256, DT, META, kGemvWaves, kGemvStages>), grid, block, 0, s, x, d, g);
+      hipLaunchKernelGGL((k_gemv_grouped<MT, 256, DT, META, W, kGemvStages>), grid, block, 0, s, x, d, g);
       break;
   }
 }
 
+template <int MT, int DT, int META>
+void gemv_grouped_w(int waves, int b2, dim3 grid, hipStream_t s, const uint16_t* x, const GemvDims& d,
+                    const GemvGroup& g) {
+  if constexpr (MT <= 4) {
+    if (waves == 8) return gemv_grouped_b2<MT, DT, META, 8>(b2, grid, s, x, d, g);
+  } else {
+    if (waves == 16) return gemv_grouped_b2<MT, DT, META, 16>(b2, grid, s, x, d, g);
+  }
+  gemv_grouped_b2<MT, DT, META, kGemvWaves>(b2, grid, s, x, d, g);
+}
+
 template <int DT, int META>
-void gemv_grouped_mt(int m, int b2, dim3 grid, hipStream_t s, const uint16_t* x, const GemvDims& d,
+void gemv_grouped_mt(int m, int waves, int b2, dim3 grid, hipStream_t s, const uint16_t* x, const GemvDims& d,
                      const GemvGroup& g) {
-  if (m <= 1) gemv_grouped_b2<1, DT, META>(b2, grid, s, x, d, g);
-  else if (m <= 2) gemv_grouped_b2<2, DT, META>(b2, grid, s, x, d, g);
-  else if (m <= 4) gemv_grouped_b2<4, DT, META>(b2, grid, s, x, d, g);
-  else if (m <= 8) gemv_grouped_b2<8, DT, META>(b2, grid, s, x, d, g);
-  else gemv_grouped_b2<16, DT, META>(b2, grid, s, x, d, g);
+  if (m <= 1) gemv_grouped_w<1, DT, META>(waves, b2, grid, s, x, d, g);
+  else if (m <= 2) gemv_grouped_w<2, DT, META>(waves, b2, grid, s, x, d, g);
+  else if (m <= 4) gemv_grouped_w<4, DT, META>(waves, b2, grid, s, x, d, g);
+  else if (m <= 8) gemv_grouped_w<8, DT, META>(waves, b2, grid, s, x, d, g);
+  else gemv_grouped_w<16, DT, META>(waves, b2, grid, s, x, d, g);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
                                int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s) {
-  GemvGroup g{};
-  g.count = count;
-  int64_t slabs = 0;
-  for (int i = 0; i < count; ++i) {
-    g.dense[i] = static_cast<const uint4*>(P[i].dense);
-    g.val[i] = static_cast<const uint4*>(P[i].val);
-    g.meta[i] = static_cast<const uint16_t*>(P[i].meta);
-    g.tidx[i] = P[i].tidx;
-    g.y[i] = y[i];
-    g.ldy[i] = ldy[i];
-    g.n_dense[i] = int32_t(L[i].n_dense);
-    g.n_sparse[i] = int32_t(L[i].n_sparse);
-    g.b1[i] = L[i].b1;
-    g.slab_start[i] = int32_t(slabs);
-    slabs += L[i].n / 16;
-  }
-  g.slab_start[count] = int32_t(slabs);
-  if (slabs == 0) return hipSuccess;
-  GemvDims d{};
-  d.ldx = ldx;
-  d.tiles_k = int32_t(L[0].tiles_k);
-  d.m = m;
-  d.ydt = y_dtype;
-  const dim3 grid(static_cast<unsigned>(slabs));
+  // Each matrix runs with the wavefront count hyb_gemv would give it on its
+  // own (so its result is bitwise that of a separate launch): one launch
+  // per distinct count, at most two.
+  int waves[kMaxGroup];
+  for (int i = 0; i < count; ++i) waves[i] = gemv_waves(L[i].n / 16, m);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (L[0].dtype == HYB_BF16) {
-    if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_BF16, HYB_META_IDX2>(m, L[0].b2, grid, s, xp, d, g);
-    else if (L[0].meta == HYB_META_MASK4) gemv_grouped_mt<HYB_BF16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
-    else gemv_grouped_mt<HYB_BF16, HYB_META_MASK8>(m, L[0].b2, grid, s, xp, d, g);
-  } else {
-    if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_F16, HYB_META_IDX2>(m, L[0].b2, grid, s, xp, d, g);
-    else if (L[0].meta == HYB_META_MASK4) gemv_grouped_mt<HYB_F16, HYB_META_MASK4>(m, L[0].b2, grid, s, xp, d, g);
-    else gemv_grouped_mt<HYB_F16, HYB_META_MASK8>(m, L[0].b2, grid, s, xp, d, g);
+  bool done[kMaxGroup] = {};
+  for (int first = 0; first < count; ++first) {
+    if (done[first]) continue;
+    const int w = waves[first];
+    GemvGroup g{};
+    int64_t slabs = 0;
+    for (int i = first; i < count; ++i) {
+      if (done[i] || waves[i] != w) continue;
+      done[i] = true;
+      const int c = g.count++;
+      g.dense[c] = static_cast<const uint4*>(P[i].dense);
+      g.val[c] = static_cast<const uint4*>(P[i].val);
+      g.meta[c] = static_cast<const uint16_t*>(P[i].meta);
+      g.tidx[c] = P[i].tidx;
+      g.y[c] = y[i];
+      g.ldy[c] = ldy[i];
+      g.n_dense[c] = int32_t(L[i].n_dense);
+      g.n_sparse[c] = int32_t(L[i].n_sparse);
+      g.b1[c] = L[i].b1;
+      g.slab_start[c] = int32_t(slabs);
+      slabs += L[i].n / 16;
+    }
+    g.slab_start[g.count] = int32_t(slabs);
+    if (slabs == 0) continue;
+    GemvDims d{};
+    d.ldx = ldx;
+    d.tiles_k = int32_t(L[0].tiles_k);
+    d.m = m;
+    d.ydt = y_dtype;
+    const dim3 grid(static_cast<unsigned>(slabs));
+    if (L[0].dtype == HYB_BF16) {
+      if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_BF16, HYB_META_IDX2>(m, w, L[0].b2, grid, s, xp, d, g);
+      else if (L[0].meta == HYB_META_MASK4) gemv_grouped_mt<HYB_BF16, HYB_META_MASK4>(m, w, L[0].b2, grid, s, xp, d, g);
+      else gemv_grouped_mt<HYB_BF16, HYB_META_MASK8>(m, w, L[0].b2, grid, s, xp, d, g);
+    } else {
+      if (L[0].meta == HYB_META_IDX2) gemv_grouped_mt<HYB_F16, HYB_META_IDX2>(m, w, L[0].b2, grid, s, xp, d, g);
+      else if (L[0].meta == HYB_META_MASK4) gemv_grouped_mt<HYB_F16, HYB_META_MASK4>(m, w, L[0].b2, grid, s, xp, d, g);
+      else gemv_grouped_mt<HYB_F16, HYB_META_MASK8>(m, w, L[0].b2, grid, s, xp, d, g);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 namespace {
