@@ -431,6 +431,33 @@ def test_gemv_output_16bit():
     assert_close(yb, yref, s, extra=half_ulp, what="bf16 out")
 
 
+@pytest.mark.parametrize("m", [1, 16])
+def test_gemv_grouped_max_count(m):
+    """HYB_MAX_GROUP matrices in one call, short ones (8 or 16 wavefronts
+    per slab) mixed with tall ones (4): bitwise equal to separate launches
+    and within the oracle's bound on every matrix."""
+    torch = _torch()
+    note(f"gemv grouped x{hb.MAX_GROUP} m={m}")
+    k = 512
+    rng = np.random.default_rng(160 + m)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), "bf16")
+    xt = upload(x, "bf16")
+    Ps, refs = [], []
+    for i in range(hb.MAX_GROUP):
+        n = 128 * (1 + i % 3) if i % 2 else 8192
+        w, tmap = random_case(1600 + i, n, k, 128, 128, "bf16", frac=0.2 + 0.04 * i)
+        Ps.append(pack_gpu(w, tmap, 128, 128, "bf16", "idx2"))
+        refs.append((w, tmap))
+    outs = hb.gemv_grouped(Ps, xt)
+    sep = [hb.gemv(P, xt) for P in Ps]
+    torch.cuda.synchronize()
+    for i, ((w, tmap), o, so) in enumerate(zip(refs, outs, sep)):
+        assert torch.equal(o, so), i
+        rows = np.arange(min(w.shape[0], 256))
+        yref, sref = oracle.ref_matmul(oracle.prune(w, tmap, 128, 128)[rows], x, "bf16")
+        assert_close(o.cpu().numpy()[:, rows], yref, sref, what=f"grouped matrix {i}")
+
+
 # ------------------------------------------------------------- GEMM -------
 
 @pytest.mark.parametrize("m", [17, 33, 64, 100, 130, 257])
@@ -502,6 +529,20 @@ def test_gemm_two_row_groups_odd(m):
     torch.cuda.synchronize()
     yref, s = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x, "bf16")
     assert_close(y.cpu().numpy(), yref, s, what="gemm two row groups")
+
+
+def test_gemm_4096_tokens_full():
+    """4096 tokens (16 token blocks of the 256-token LDS shape) on a 1024 x
+    1024 matrix, every output against the oracle."""
+    torch = _torch()
+    note("gemm m=4096 full")
+    w, tmap = random_case(4096, 1024, 1024, 64, 128, "bf16")
+    x = wl.float32_to_bits(np.random.default_rng(4096).standard_normal((4096, 1024)).astype(np.float32), "bf16")
+    P = pack_gpu(w, tmap, 64, 128, "bf16", "idx2")
+    y = hb.gemm(P, upload(x, "bf16"))
+    torch.cuda.synchronize()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, 64, 128), x, "bf16")
+    assert_close(y.cpu().numpy(), yref, s, what="gemm m=4096")
 
 
 def test_gemm_output_16bit():
