@@ -49,7 +49,9 @@
  * Conventions.
  *   - All pointers to device memory are plain device addresses (from
  *     hipMalloc or any allocator on the same device); the library never
- *     allocates or frees device memory and keeps no mutable global state.
+ *     allocates or frees device memory and keeps no mutable global state
+ *     apart from a per-device cache of the compute-unit count (used to
+ *     pick launch shapes).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device calls enqueue work and return; the caller synchronises.
  *   - Every argument is checked on the host before anything is enqueued; a

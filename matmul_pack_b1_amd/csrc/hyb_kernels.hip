@@ -13,6 +13,7 @@
 // and the dense chunk is also the A-operand layout of the 16x16x32 MFMA.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "hyb_internal.h"
@@ -1963,17 +1964,18 @@ constexpr int lds_stages() {
   return GemmLdsCfg<B2, MB, 3, WAVES>::kBytes + (META == HYB_META_MASK8 ? 4096 : 0) <= 160 * 1024 ? 3 : 2;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers on
+// several host threads may race to fill an entry with the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // Workgroup shape by token count.  Up to 128 tokens the register-fed
