@@ -201,7 +201,8 @@ def allocate(layout: HybLayout, tidx_host: np.ndarray, device, dtype: str, meta:
 
 def pack(w, tile_map, b1: int, b2: int, meta: str = "idx2", out: PackedWeight | None = None) -> PackedWeight:
     """Pack a device matrix w (n x k, bf16 or fp16) with the given tile map
-    (uint8 [n/b1, k/b2], 1 = 2:4 sparse).  `out` reuses existing buffers."""
+    (uint8 [n/b1, k/b2], 1 = sparse: 2:4, or 4:8 with meta "mask8").  `out`
+    reuses existing buffers."""
     _check_rows(w, "w")
     dtype = _dtype_name(w)
     n, k = w.shape
