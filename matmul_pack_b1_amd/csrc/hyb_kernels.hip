@@ -39,6 +39,9 @@
 #ifndef HYB_GEMM_C192
 #define HYB_GEMM_C192 0.8
 #endif
+#ifndef HYB_GEMM_C_RX
+#define HYB_GEMM_C_RX 0.29
+#endif
 #ifndef HYB_W_AUX
 #define HYB_W_AUX 2  // non-temporal: the weights are read once per product
 #endif
@@ -1986,7 +1989,12 @@ int device_cus() {
 // the number of rounds of workgroups over the compute units times the time
 // of one workgroup; the relative step costs of the shapes are measured (a
 // 256-token step costs 1, a 192-token step 0.8, a 128-token step 0.64, a
-// 64-token step 0.57), and the shape with the smallest product runs.
+// 64-token step 0.57), and the shape with the smallest product runs.  A
+// matrix with few 256-row blocks (short and deep, e.g. 8192 x 28672) leaves
+// most CUs idle under every LDS shape; there the register-fed shape of 128
+// rows by 64 tokens (its four wavefronts splitting K) runs when its rounds,
+// at 0.29 each on the same scale (measured on 8192 to 28672 rows at 160 to
+// 512 tokens), cost less than 0.9 of the best LDS shape.
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   const int64_t cus = device_cus();
@@ -2031,6 +2039,9 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   const double c256 = cost(256, 1.0), c192 = cost(192, HYB_GEMM_C192), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
   const double best = c256 < c192 ? (c256 < c128 ? (c256 < c64 ? c256 : c64) : (c128 < c64 ? c128 : c64))
                                   : (c192 < c128 ? (c192 < c64 ? c192 : c64) : (c128 < c64 ? c128 : c64));
+  const int64_t rx_wgs = ((L.n + 127) / 128) * ((m + 63) / 64);
+  if (double((rx_wgs + cus - 1) / cus) * HYB_GEMM_C_RX < 0.9 * best)
+    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
   if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
   if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
   if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);

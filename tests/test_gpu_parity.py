@@ -514,6 +514,23 @@ def test_gemm_8b_up_shapes_sampled(m):
     assert_close(y[:, rows], yref, s, what=f"gemm m={m}")
 
 
+@pytest.mark.parametrize("m", [160, 256, 512])
+def test_gemm_tall_70b_sampled(m):
+    """8192x28672 (32 blocks of 256 rows), 128x128 tiles in a checkerboard:
+    at 160 and 256 tokens every LDS shape leaves most CUs of a 256-CU device
+    idle and the launcher runs the register-fed shape (128 rows by 64 tokens,
+    K split over four wavefronts; 160 with a ragged last block); at 512 it
+    runs the 64-token LDS shape."""
+    torch = _torch()
+    mat, w, tmap = workload_matrix(4, 5)
+    note(f"gemm 70b tall m={m}")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
+    y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
+    assert_close(y[:, rows], yref, s, what=f"gemm tall m={m}")
+
+
 @pytest.mark.parametrize("m", [20, 64])
 def test_gemm_two_row_groups_odd(m):
     """16448 rows (257 row groups of 64, more than one round on a 256-CU
