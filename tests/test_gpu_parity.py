@@ -401,6 +401,29 @@ def test_sparse_lowrank_prefill_qwen14b_sampled(m):
     assert_close(y[:, rows], yref, s, extra=extra, what="prefill sparse + low-rank")
 
 
+def test_sparse_lowrank_prefill_tall_sampled():
+    """8192 x 28672 (128 x 128 tiles, checkerboard) + rank 32 at 200 tokens:
+    the register-fed product above 128 tokens (the shape a short, deep
+    matrix takes there) with its T U^T epilogue, on sampled tile rows."""
+    torch = _torch()
+    note("sparse + low-rank prefill 70b tall m=200")
+    mat, w, tmap = workload_matrix(4, 5)
+    rank, m = 32, 200
+    rng = np.random.default_rng(200)
+    v = wl.float32_to_bits(rng.standard_normal((rank, mat.k)).astype(np.float32) * 0.01, "bf16")
+    u = wl.float32_to_bits(rng.standard_normal((mat.n, rank)).astype(np.float32) * 0.02, "bf16")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    y = hb.sparse_lowrank_gemm(P, upload(v, "bf16"), upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
+    t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
+    tile_rows = sample_tile_rows(mat, 2, 200)
+    rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
+    sub = oracle.prune(w[rows], tmap[tile_rows], mat.b1, mat.b2)
+    yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
+    extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
+    assert_close(y[:, rows], yref, s, extra=extra, what="tall prefill sparse + low-rank")
+
+
 def test_gemm_lowrank_output_16bit():
     """A 16-bit y is rounded once, after the low-rank term is added."""
     torch = _torch()
