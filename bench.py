@@ -27,7 +27,9 @@ tiles with 2:4 ones (JSON key "nm48"), and the prefill GEMM is
 measured on its own workload
 (Qwen3-14B-shaped 17408 x 5120, 64 x 64 tiles, M = 2048): hybrid, the same
 kernel all-dense, and the vendor BLAS dense product, with the matrix-core
-roofline (JSON key "prefill").
+roofline (JSON key "prefill"); the same three on a short, deep matrix
+(70B-shaped 8192 x 28672, 128 x 128 tiles in a checkerboard, M = 256, JSON
+key "tall").
 
 Prints one JSON line.  `python bench.py --sweep` also measures the other
 workloads (stderr table plus --sweep-json file).
@@ -153,7 +155,7 @@ def main():
     ap.add_argument("--prefill-m", type=int, default=2048,
                     help="token count of the prefill GEMM measurement")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,prefill)")
+                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,prefill,tall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 128 MiB device copies (torch copy kernel) as a counter reference")
@@ -177,7 +179,7 @@ def main():
     dev = torch.device("cuda:0")
     rotate = int(args.rotate_gib * (1 << 30))
     rows = set(args.only.split(",")) if args.only else {"pack", "gemv", "dense", "unpack", "gemm", "grouped",
-                                                         "lowrank", "nm48", "prefill"}
+                                                         "lowrank", "nm48", "prefill", "tall"}
 
     if args.copy_calibration:
         # A plain copy of known size: 128 MiB read + 128 MiB written per
@@ -410,6 +412,10 @@ def main():
         log(f"[bench] prefill GEMM M={args.prefill_m}")
         out["prefill"] = prefill(hb, torch, wl, dev, args.prefill_m, args.meta)
         log(f"[bench] prefill: {out['prefill']}")
+    if "tall" in rows:
+        log("[bench] prefill GEMM on a short, deep matrix, M=256")
+        out["tall"] = tall(hb, torch, wl, dev, 256, args.meta)
+        log(f"[bench] tall: {out['tall']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(mat, w_bits, tmap, x_bits, L)
@@ -451,6 +457,26 @@ def prefill(hb, torch, wl, dev, m, meta):
     the same kernel on the all-dense map, and torch's bf16 matmul (the
     vendor BLAS) on the dense weights as the library reference."""
     mat = wl.workload(5).matrices[0]
+    return product_row(hb, torch, dev, mat, m, meta,
+                       f"Qwen3-14B gate/up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles",
+                       "k_gemm_lds (256-row x 192-token workgroups on 8 wavefronts at this M on 256 CUs)")
+
+
+def tall(hb, torch, wl, dev, m, meta):
+    """The same three products on the 70B-shaped down projection (8192 x
+    28672, 128 x 128 tiles in a checkerboard): only 32 blocks of 256 rows, so
+    the launcher runs the register-fed shape (128 rows x 64 tokens, K split
+    over four wavefronts) up to a few hundred tokens."""
+    mat = wl.workload(4).matrices[5]
+    return product_row(hb, torch, dev, mat, m, meta,
+                       f"Llama-3.1-70B-shaped down projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles "
+                       f"(checkerboard)",
+                       "k_gemm_rx (128-row x 64-token workgroups, four wavefronts splitting K, at this M)")
+
+
+def product_row(hb, torch, dev, mat, m, meta, name, kernel):
+    """Hybrid GEMM, the same kernel on the all-dense map, and the vendor
+    BLAS's dense bf16 product, each a graph burst over two copies."""
     tmap = mat.tile_map()
     w = hb.bits_to_tensor(mat.weight_bits(), mat.dtype, dev)
     x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
@@ -469,8 +495,7 @@ def prefill(hb, torch, wl, dev, m, meta):
     fl = alg_flops(L, m)
     fl_dense = 2 * m * mat.n * mat.k
     tf = fl / (us_h * 1e-6) / 1e12
-    out = {"workload": f"Qwen3-14B gate/up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles, "
-                       f"{L.n_sparse}/{L.tiles_n * L.tiles_k} tiles 2:4 ({meta}), prefill M={m}",
+    out = {"workload": f"{name}, {L.n_sparse}/{L.tiles_n * L.tiles_k} tiles 2:4 ({meta}), prefill M={m}",
            "m": m, "hybrid_us": round(us_h, 2), "dense_same_kernel_us": round(us_d, 2),
            "vendor_blas_dense_us": round(us_v, 2), "alg_flops": fl, "dense_flops": fl_dense,
            "TFLOPs": round(tf, 1), "dense_same_kernel_TFLOPs": round(fl_dense / (us_d * 1e-6) / 1e12, 1),
@@ -479,7 +504,7 @@ def prefill(hb, torch, wl, dev, m, meta):
            "speedup_vs_vendor_blas": round(us_v / us_h, 4),
            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_BF16_TFLOPS, 4),
-                        "kernel": "k_gemm_lds (256-row x 192-token workgroups on 8 wavefronts at this M on 256 CUs)"},
+                        "kernel": kernel},
            "timing": f"graph burst of {n_launch} launches over 2 rotating copies, median of 5 replays"}
     del hyb, den, wt, w, x, y, yb
     torch.cuda.empty_cache()
