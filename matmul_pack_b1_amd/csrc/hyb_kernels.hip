@@ -2024,6 +2024,12 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
         best_wgs = wgs;
       }
     }
+    // A wide matrix can need two rounds of the 128-row x 64-token shape
+    // while the 64-token LDS shape (256 rows per workgroup) fits the whole
+    // product in one; that round is cheaper than two (28672 x 8192 at 80-128
+    // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
+    if (best == 4 && best_rounds >= 2 && ((L.n + 255) / 256) * ((m + 63) / 64) <= cus)
+      return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4, META>(), 4>(L, q, m, d, s);
     switch (best) {
       case 0: return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
       case 1: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);

@@ -378,10 +378,11 @@ def test_gemm_lowrank_small_m_and_strides():
 def test_sparse_lowrank_prefill_qwen14b_sampled(m):
     """17408 x 5120 (64 x 64 tiles, 60% 2:4) + rank 64: the projection on
     the matrix cores (above 16 tokens) and the matrix-core product with the
-    T U^T epilogue, through each kernel variant (register-fed with one and
-    two row groups, 65-128 tokens, the LDS-fed kernel), checked on
-    sampled tile rows; the oracle computes T itself and the bound carries
-    T's own error through |U|."""
+    T U^T epilogue, through each kernel variant (register-fed with one row
+    group at 12 tokens and two at 40, the LDS-fed kernel's 64-token shape at
+    100 and its larger shapes at 256), checked on sampled tile rows; the
+    oracle computes T itself and the bound carries T's own error through
+    |U|."""
     torch = _torch()
     note(f"sparse + low-rank prefill qwen14b m={m}")
     mat, w, tmap = workload_matrix(5, 0)
@@ -552,6 +553,22 @@ def test_gemm_tall_70b_sampled(m):
     rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
     assert_close(y[:, rows], yref, s, what=f"gemm tall m={m}")
+
+
+@pytest.mark.parametrize("m", [80, 128])
+def test_gemm_wide_70b_sampled(m):
+    """28672x8192 (128x128 tiles, checkerboard) at 80 and 128 tokens: the
+    register-fed pick would need two rounds of 128-row x 64-token workgroups
+    on a 256-CU device, so the launcher runs the 64-token LDS shape, whose
+    224 workgroups fit in one (80: ragged last token block)."""
+    torch = _torch()
+    mat, w, tmap = workload_matrix(4, 2)
+    note(f"gemm 70b wide m={m}")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
+    y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
+    assert_close(y[:, rows], yref, s, what=f"gemm wide m={m}")
 
 
 @pytest.mark.parametrize("m", [20, 64])
