@@ -1989,12 +1989,8 @@ int device_cus() {
 // the number of rounds of workgroups over the compute units times the time
 // of one workgroup; the relative step costs of the shapes are measured (a
 // 256-token step costs 1, a 192-token step 0.8, a 128-token step 0.64, a
-// 64-token step 0.57), and the shape with the smallest product runs.  A
-// matrix with few 256-row blocks (short and deep, e.g. 8192 x 28672) leaves
-// most CUs idle under every LDS shape; there the register-fed shape of 128
-// rows by 64 tokens (its four wavefronts splitting K) runs when its rounds,
-// at 0.29 each on the same scale (measured on 8192 to 28672 rows at 160 to
-// 512 tokens), cost less than 0.9 of the best LDS shape.
+// 64-token step 0.57), and the shape with the smallest product runs,
+// unless a register-fed shape, priced the same way, costs under 0.9 of it.
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
   const int64_t cus = device_cus();
@@ -2005,18 +2001,33 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
     if (groups <= cus) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
     return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
   }
+  // Register-fed shapes: token blocks of 16 per workgroup, wavefronts, 64-row
+  // groups per workgroup; and the time of one round of each, relative to one
+  // round of the 256-token LDS shape over the same K (measured on 1024 to
+  // 8192 rows, K = 4096 to 28672, 24 to 1024 tokens).
+  constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
+  constexpr double kRound[5] = {0.12, 0.155, 0.21, 0.21, HYB_GEMM_C_RX};
+  auto rx_wgs = [&](int i) {
+    return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
+  };
+  auto rx_run = [&](int i) {
+    switch (i) {
+      case 0: return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
+      case 1: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);
+      case 2: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
+      case 3: return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, s);
+      default: return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
+    }
+  };
   if (m <= 128) {
-    // Register-fed shapes (token blocks of 16 per workgroup, wavefronts,
-    // 64-row groups per workgroup).  The fewest rounds of workgroups over
-    // the CUs wins, then the most workgroups; on a tie the earlier entry
-    // (one row group before two, then the smaller token block).  Measured
-    // on 1024 to 17408 rows at 17-128 tokens: the pick is the fastest shape
-    // or within 3% of it.
-    constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
+    // The fewest rounds of workgroups over the CUs wins, then the most
+    // workgroups; on a tie the earlier entry (one row group before two,
+    // then the smaller token block).  Measured on 1024 to 17408 rows at
+    // 17-128 tokens: the pick is the fastest shape or within 3% of it.
     int best = 0;
     int64_t best_rounds = 0, best_wgs = 0;
     for (int i = 0; i < 5; ++i) {
-      const int64_t wgs = ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
+      const int64_t wgs = rx_wgs(i);
       const int64_t rounds = (wgs + cus - 1) / cus;
       if (i == 0 || rounds < best_rounds || (rounds == best_rounds && wgs > best_wgs)) {
         best = i;
@@ -2030,13 +2041,7 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
     // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
     if (best == 4 && best_rounds >= 2 && ((L.n + 255) / 256) * ((m + 63) / 64) <= cus)
       return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4, META>(), 4>(L, q, m, d, s);
-    switch (best) {
-      case 0: return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
-      case 1: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);
-      case 2: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
-      case 3: return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, s);
-      default: return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
-    }
+    return rx_run(best);
   }
   const int64_t gn = (L.n + 255) / 256;
   auto cost = [&](int64_t bm, double step) {
@@ -2045,9 +2050,21 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   const double c256 = cost(256, 1.0), c192 = cost(192, HYB_GEMM_C192), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
   const double best = c256 < c192 ? (c256 < c128 ? (c256 < c64 ? c256 : c64) : (c128 < c64 ? c128 : c64))
                                   : (c192 < c128 ? (c192 < c64 ? c192 : c64) : (c128 < c64 ? c128 : c64));
-  const int64_t rx_wgs = ((L.n + 127) / 128) * ((m + 63) / 64);
-  if (double((rx_wgs + cus - 1) / cus) * HYB_GEMM_C_RX < 0.9 * best)
-    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
+  // A matrix with few 256-row blocks (a short one, or a short and deep one
+  // such as 8192 x 28672) leaves most CUs idle under every LDS shape; the
+  // cheapest register-fed shape runs when it costs under 0.9 of the best LDS
+  // shape (e.g. 1024 x 4096 at 160-1024 tokens: 1.3-1.9x faster; 8192 x
+  // 28672 at 160-256 tokens: 382 -> 169-231 us).
+  int rx_best = 0;
+  double rx_cost = 0.0;
+  for (int i = 0; i < 5; ++i) {
+    const double c = double((rx_wgs(i) + cus - 1) / cus) * kRound[i];
+    if (i == 0 || c < rx_cost) {
+      rx_best = i;
+      rx_cost = c;
+    }
+  }
+  if (rx_cost < 0.9 * best) return rx_run(rx_best);
   if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
   if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
   if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);

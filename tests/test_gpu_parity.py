@@ -501,6 +501,51 @@ def test_gemm_random(m, b1, b2, dtype, meta):
     assert_close(y.cpu().numpy(), yref, s, what="gemm")
 
 
+def random_rows_check(w, tmap, b1, b2, x, y, dtype, seed, meta="idx2", count=3):
+    """Oracle check of `count` sampled tile rows of a random case."""
+    tile_rows = np.sort(np.random.default_rng(seed).choice(tmap.shape[0], size=count, replace=False))
+    rows = np.concatenate([np.arange(t * b1, (t + 1) * b1) for t in tile_rows])
+    yref, s = oracle.ref_matmul(oracle.prune(w[rows], tmap[tile_rows], b1, b2, meta), x, dtype)
+    assert_close(y[:, rows], yref, s, what=f"sampled rows {tile_rows.tolist()}")
+
+
+@pytest.mark.parametrize("n,m", [(8192, 1024), (8192, 2048), (16384, 256)])
+@pytest.mark.parametrize("b1,b2,dtype,meta", [(64, 64, "bf16", "idx2"), (128, 128, "f16", "mask4"),
+                                              (256, 256, "bf16", "mask4"), (64, 128, "bf16", "idx2")])
+def test_gemm_lds_shapes_random(n, m, b1, b2, dtype, meta):
+    """Matrices with enough 256-row blocks that the launcher runs an LDS-fed
+    shape on a 256-CU device: 8192 rows at 1024 tokens (the 128-token
+    shape), 8192 rows at 2048 (the 256-token shape) and 16384 rows at 256
+    (the 64-token shape), in every tile size, dtype and metadata kind of
+    test_gemm_random (whose small matrices take the register-fed kernel at
+    every token count); checked on sampled tile rows."""
+    torch = _torch()
+    note(f"gemm lds shapes n={n} m={m} {b1}x{b2} {dtype} {meta}")
+    k = 2 * b2
+    w, tmap = random_case(n + m + b2, n, k, b1, b2, dtype)
+    x = wl.float32_to_bits(np.random.default_rng(m + n).standard_normal((m, k)).astype(np.float32), dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    y = hb.gemm(P, upload(x, dtype)).cpu().numpy()
+    random_rows_check(w, tmap, b1, b2, x, y, dtype, seed=n + m)
+
+
+@pytest.mark.parametrize("config,index,m", [(3, 1, 384), (3, 0, 160), (3, 6, 256)])
+def test_gemm_small_matrices_above_128_sampled(config, index, m):
+    """Few 256-row blocks above 128 tokens: the launcher prices every
+    register-fed shape against the LDS shapes and, on a 256-CU device, runs
+    32 tokens x 64 rows on eight wavefronts for the 1024 x 4096 k projection
+    at 384 tokens, and 64 tokens x 64 rows on eight wavefronts for the
+    4096-row q (160 tokens, ragged) and down (256 tokens) projections."""
+    torch = _torch()
+    mat, w, tmap = workload_matrix(config, index)
+    note(f"gemm small matrix {mat.name} m={m}")
+    x = mat.activation_bits(m)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
+    y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
+    assert_close(y[:, rows], yref, s, what=f"gemm {mat.name} m={m}")
+
+
 @pytest.mark.parametrize("m", [8, 16, 64, 256, 2048])
 def test_gemm_qwen14b_sampled(m):
     """17408x5120, 64x64 tiles, 60% sparse tiles; M from 16 to 2048 through

@@ -5,7 +5,8 @@ grouped and low-rank decode entry points.  The matrix-core tests pick token
 counts and shapes that reach each kernel variant: the decode kernel (m <= 8
 through hyb_gemm), the register-fed kernel with eight and four wavefronts,
 two row groups per workgroup (17408 rows: more 64-row groups than compute
-units), 65-128 tokens, and the four LDS-fed shapes."""
+units), 65-128 tokens, and the four LDS-fed shapes (17408 rows at 256 and
+2048 tokens, and 8192 or 16384 rows at 256-2048)."""
 import numpy as np
 import pytest
 
@@ -91,6 +92,26 @@ def test_gemm_4of8_random(m, b1, b2, dtype):
     torch.cuda.synchronize()
     yref, s = oracle.ref_matmul(_prune(w, tmap, b1, b2), x, dtype)
     assert_close(y.cpu().numpy(), yref, s, what="gemm 4:8")
+
+
+@pytest.mark.parametrize("n,m", [(8192, 1024), (8192, 2048), (16384, 256)])
+@pytest.mark.parametrize("b1,b2,dtype", [(64, 64, "bf16"), (128, 128, "f16"), (64, 256, "bf16")])
+def test_gemm_4of8_lds_shapes_random(n, m, b1, b2, dtype):
+    """The LDS-fed shapes (128-, 256- and 64-token workgroups on a 256-CU
+    device) on 4:8 tiles in each tile size and dtype; the small matrices of
+    test_gemm_4of8_random take the register-fed kernel at every token
+    count.  Checked on sampled tile rows."""
+    torch = _torch()
+    note(f"gemm 4:8 lds shapes n={n} m={m} {b1}x{b2} {dtype}")
+    k = 2 * b2
+    w, tmap = random_case(n + m + b2 + 8, n, k, b1, b2, dtype)
+    x = wl.float32_to_bits(np.random.default_rng(m + n + 8).standard_normal((m, k)).astype(np.float32), dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, META)
+    y = hb.gemm(P, upload(x, dtype)).cpu().numpy()
+    tile_rows = np.sort(np.random.default_rng(n + m).choice(n // b1, size=3, replace=False))
+    rows = np.concatenate([np.arange(t * b1, (t + 1) * b1) for t in tile_rows])
+    yref, s = oracle.ref_matmul(_prune(w[rows], tmap[tile_rows], b1, b2), x, dtype)
+    assert_close(y[:, rows], yref, s, what=f"4:8 lds shapes n={n} m={m}")
 
 
 @pytest.mark.parametrize("m", [4, 12, 30, 64, 100, 256, 2048])
