@@ -348,6 +348,34 @@ def test_gemm_lowrank(m, rank, dtype):
     assert_close(y.cpu().numpy(), yref, s, what="gemm lowrank")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gemm_lowrank_lds_shape(dtype):
+    """The LDS-fed kernel's T U^T epilogue in both weight dtypes (bf16: T as
+    hi + lo bf16 products; fp16: fp32 16x16x4 products): 8192 rows at 1024
+    tokens run the 128-token LDS shape on a 256-CU device (the small
+    matrices of test_gemm_lowrank take the register-fed kernel).  Sampled
+    tile rows against the oracle; U = 0 gives the plain product bitwise."""
+    torch = _torch()
+    note(f"gemm lowrank lds shape {dtype}")
+    b1, b2, n, k, m, rank = 64, 128, 8192, 256, 1024, 64
+    w, tmap = random_case(8192 + rank, n, k, b1, b2, dtype)
+    rng = np.random.default_rng(1024 + rank)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), dtype)
+    t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, "idx2")
+    xt, tt = upload(x, dtype), torch.from_numpy(t).to(dev())
+    y = hb.gemm_lowrank(P, xt, tt, upload(u, dtype))
+    y0 = hb.gemm_lowrank(P, xt, tt, upload(np.zeros_like(u), dtype))
+    yg = hb.gemm(P, xt)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, yg)
+    tile_rows = np.sort(np.random.default_rng(7).choice(n // b1, size=3, replace=False))
+    rows = np.concatenate([np.arange(tr * b1, (tr + 1) * b1) for tr in tile_rows])
+    yref, s = oracle.ref_lowrank(oracle.prune(w[rows], tmap[tile_rows], b1, b2), x, t, u[rows], dtype)
+    assert_close(y.cpu().numpy()[:, rows], yref, s, what="gemm lowrank lds shape")
+
+
 def test_gemm_lowrank_small_m_and_strides():
     """8 tokens or fewer run the fused decode kernel (bitwise the decode
     entry point); above, a y with a row stride larger than n keeps its
