@@ -821,6 +821,36 @@ def test_corrupt_tile_index_is_skipped():
     del keep
 
 
+def test_corrupt_tile_index_and_16bit_out_lds_shape():
+    """The LDS-fed kernel (8192 rows at 1024 tokens: the 128-token shape on
+    a 256-CU device) skips tidx entries naming slots outside the streams,
+    and rounds a bf16 y once; checked on tile rows that include the two
+    corrupted tiles."""
+    torch = _torch()
+    note("corrupt tidx and bf16 y, lds shape")
+    b1, b2, n, k, m = 64, 128, 8192, 256, 1024
+    w, tmap = random_case(8191, n, k, b1, b2, "bf16")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    bad = P.tidx.cpu().numpy().copy()
+    tk = k // b2
+    t0, t1 = 0, 5 * tk + 1            # tile (0, 0) and tile (5, 1)
+    bad[t0] = 1 << 30                 # a dense slot far out of range
+    bad[t1] = -(1 << 30)              # a sparse slot far out of range
+    P.tidx.copy_(torch.from_numpy(bad))
+    x = wl.float32_to_bits(np.random.default_rng(8191).standard_normal((m, k)).astype(np.float32), "bf16")
+    xt = upload(x, "bf16")
+    y = hb.gemm(P, xt).cpu().numpy()
+    y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=torch.bfloat16)), "bf16")
+    tile_rows = np.array([0, 5, 77])
+    rows = np.concatenate([np.arange(tr * b1, (tr + 1) * b1) for tr in tile_rows])
+    wp = oracle.prune(w[rows], tmap[tile_rows], b1, b2)
+    wp[0:b1, 0:b2] = 0                # tile (0, 0) skipped
+    wp[b1:2 * b1, b2:2 * b2] = 0      # tile (5, 1) skipped
+    yref, s = oracle.ref_matmul(wp, x, "bf16")
+    assert_close(y[:, rows], yref, s, what="lds corrupt tidx")
+    assert_close(y16[:, rows], yref, s, extra=np.abs(yref) * 2.0 ** -8 + 2.0 ** -133, what="lds bf16 y")
+
+
 def test_deterministic():
     torch = _torch()
     note("determinism")
