@@ -1983,7 +1983,8 @@ int device_cus() {
 
 // Workgroup shape by token count.  Up to 128 tokens the register-fed
 // kernel k_gemm_rx runs (64 or 128 rows per workgroup, wavefronts
-// splitting K) in the shape that fills the CUs best.  From 129 tokens one
+// splitting K) in the shape that fills the CUs best (one exception below
+// for wide matrices at 65-128 tokens).  From 129 tokens one
 // of four LDS-fed shapes runs, 256 weight rows by BM = 256,
 // 192, 128 or 64 tokens.  Every workgroup walks all of K, so the time is
 // the number of rounds of workgroups over the compute units times the time
