@@ -2056,16 +2056,19 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   // cheapest register-fed shape runs when it costs under 0.9 of the best LDS
   // shape (e.g. 1024 x 4096 at 160-1024 tokens: 1.3-1.9x faster; 8192 x
   // 28672 at 160-256 tokens: 382 -> 169-231 us).
-  int rx_best = 0;
+  // (a shape needing more than 65535 token blocks, the register-fed grid's
+  // limit, is not a candidate)
+  int rx_best = -1;
   double rx_cost = 0.0;
   for (int i = 0; i < 5; ++i) {
+    if ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
     const double c = double((rx_wgs(i) + cus - 1) / cus) * kRound[i];
-    if (i == 0 || c < rx_cost) {
+    if (rx_best < 0 || c < rx_cost) {
       rx_best = i;
       rx_cost = c;
     }
   }
-  if (rx_cost < 0.9 * best) return rx_run(rx_best);
+  if (rx_best >= 0 && rx_cost < 0.9 * best) return rx_run(rx_best);
   if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
   if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
   if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);

@@ -821,6 +821,28 @@ def test_corrupt_tile_index_is_skipped():
     del keep
 
 
+def test_gemm_millions_of_tokens_one_row_block():
+    """4.3 million tokens on a 64 x 64 matrix: the register-fed shapes would
+    need more token blocks than their grid allows (65535), so the launcher
+    keeps the LDS-fed kernel (1-D grid); 2000 sampled tokens against the
+    oracle."""
+    torch = _torch()
+    note("gemm 4.3M tokens, 64x64")
+    n = k = b1 = b2 = 64
+    m = 4_300_000
+    w, tmap = random_case(4300, n, k, b1, b2, "bf16")
+    rng = np.random.default_rng(4300)
+    x = wl.float32_to_bits(rng.standard_normal((m, k), dtype=np.float32), "bf16")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    y = hb.gemm(P, upload(x, "bf16"))
+    torch.cuda.synchronize()
+    pick = np.sort(rng.choice(m, size=2000, replace=False))
+    pick[-1] = m - 1
+    ys = y[torch.from_numpy(pick).to(dev())].cpu().numpy()
+    yref, s = oracle.ref_matmul(oracle.prune(w, tmap, b1, b2), x[pick], "bf16")
+    assert_close(ys, yref, s, what="4.3M tokens")
+
+
 def test_corrupt_tile_index_and_16bit_out_lds_shape():
     """The LDS-fed kernel (8192 rows at 1024 tokens: the 128-token shape on
     a 256-CU device) skips tidx entries naming slots outside the streams,
