@@ -2041,7 +2041,7 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
     // product in one; that round is cheaper than two (28672 x 8192 at 80-128
     // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
     if (best == 4 && best_rounds >= 2 && ((L.n + 255) / 256) * ((m + 63) / 64) <= cus)
-      return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4, META>(), 4>(L, q, m, d, s);
+      return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, s);
     return rx_run(best);
   }
   const int64_t gn = (L.n + 255) / 256;
@@ -2072,7 +2072,7 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
   if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
   if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);
-  return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 4, META>(), 4>(L, q, m, d, s);
+  return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, s);
 }
 
 template <int DT, int META>
