@@ -458,8 +458,7 @@ def prefill(hb, torch, wl, dev, m, meta):
     vendor BLAS) on the dense weights as the library reference."""
     mat = wl.workload(5).matrices[0]
     return product_row(hb, torch, dev, mat, m, meta,
-                       f"Qwen3-14B gate/up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles",
-                       "k_gemm_lds (256-row x 192-token workgroups on 8 wavefronts at this M on 256 CUs)")
+                       f"Qwen3-14B gate/up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles")
 
 
 def tall(hb, torch, wl, dev, m, meta):
@@ -470,11 +469,21 @@ def tall(hb, torch, wl, dev, m, meta):
     mat = wl.workload(4).matrices[5]
     return product_row(hb, torch, dev, mat, m, meta,
                        f"Llama-3.1-70B-shaped down projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles "
-                       f"(checkerboard)",
-                       "k_gemm_rx (128-row x 64-token workgroups, four wavefronts splitting K, at this M)")
+                       f"(checkerboard)")
 
 
-def product_row(hb, torch, dev, mat, m, meta, name, kernel):
+def kernel_text(hb, layout, m):
+    """The kernel and workgroup shape hyb_gemm launches here (hyb_gemm_shape)."""
+    sh = hb.gemm_shape(layout, m)
+    if sh["kernel"] == "decode":
+        return f"k_gemv ({sh['waves']} wavefronts per 16-row slab)"
+    name = "k_gemm_rx" if sh["kernel"] == "register" else "k_gemm_lds"
+    split = ", wavefronts splitting K" if sh["kernel"] == "register" else ""
+    return (f"{name} ({64 * sh['row_groups']}-row x {16 * sh['token_blocks']}-token workgroups on "
+            f"{sh['waves']} wavefronts{split})")
+
+
+def product_row(hb, torch, dev, mat, m, meta, name):
     """Hybrid GEMM, the same kernel on the all-dense map, and the vendor
     BLAS's dense bf16 product, each a graph burst over two copies."""
     tmap = mat.tile_map()
@@ -504,7 +513,7 @@ def product_row(hb, torch, dev, mat, m, meta, name, kernel):
            "speedup_vs_vendor_blas": round(us_v / us_h, 4),
            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_BF16_TFLOPS, 4),
-                        "kernel": kernel},
+                        "kernel": kernel_text(hb, L, m)},
            "timing": f"graph burst of {n_launch} launches over 2 rotating copies, median of 5 replays"}
     del hyb, den, wt, w, x, y, yb
     torch.cuda.empty_cache()

@@ -250,6 +250,20 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
                          int32_t m, int64_t ldx, void* y, int32_t y_dtype,
                          int64_t ldy, void* stream);
 
+/* Diagnostics, host only (no device work, nothing enqueued): the kernel and
+ * workgroup shape that hyb_gemm would launch for `m` >= 1 tokens on
+ * `layout`'s matrix on the current device (its compute-unit count; 256, the
+ * MI355X's, when no device is visible).  hyb_gemm_mfma launches the same for
+ * m > 16, and for m <= 16 the register-fed shape of out[0] = 2.  Writes
+ * out[4] = {kernel, token blocks of 16 per workgroup, wavefronts per
+ * workgroup, 64-row groups per workgroup}: kernel HYB_KERNEL_DECODE (k_gemv;
+ * out[1] = out[3] = 0, out[2] its wavefronts per 16-row slab),
+ * HYB_KERNEL_REGISTER (k_gemm_rx, wavefronts splitting K) or HYB_KERNEL_LDS
+ * (k_gemm_lds, 4 row groups).  Errors: as the layout checks of hyb_gemm;
+ * out NULL -> HYB_ERR_INVALID_ARG; m < 1 -> HYB_ERR_SHAPE. */
+enum { HYB_KERNEL_DECODE = 1, HYB_KERNEL_REGISTER = 2, HYB_KERNEL_LDS = 3 };
+hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out);
+
 /* Measurement aid (no part of the product computation): reads `bytes`
  * bytes at `p` (device, 16-byte aligned) with the same non-temporal 16-byte
  * buffer loads the decode kernel uses, `grid` workgroups of 256 threads, and

@@ -27,7 +27,9 @@ META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
-            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_stream_read", "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_shape", "hyb_stream_read",
+            "hyb_status_str", "hyb_last_error", "hyb_abi_version")
+KERNEL_NAMES = {1: "decode", 2: "register", 3: "lds"}   # HYB_KERNEL_* of hyb_gemm_shape
 MAX_GROUP = 16
 MAX_RANK = 256
 
@@ -90,6 +92,8 @@ def lib() -> ctypes.CDLL:
         f.restype = I32
     L.hyb_lowrank_project.argtypes = [P, I64, I32, I64, I32, P, I32, I64, P, I64, P]
     L.hyb_lowrank_project.restype = I32
+    L.hyb_gemm_shape.argtypes = [ctypes.POINTER(HybLayout), I32, ctypes.POINTER(I32 * 4)]
+    L.hyb_gemm_shape.restype = I32
     L.hyb_stream_read.argtypes = [P, I64, P, I32, P]
     L.hyb_stream_read.restype = I32
     L.hyb_status_str.argtypes = [I32]
@@ -376,6 +380,14 @@ def gemm(P: PackedWeight, x, out_dtype=None, out=None):
 def gemm_mfma(P: PackedWeight, x, out_dtype=None, out=None):
     """Y = X W'^T on the matrix-core kernel regardless of the token count."""
     return _product("hyb_gemm_mfma", P, x, out_dtype, out)
+
+
+def gemm_shape(layout: HybLayout, m: int) -> dict:
+    """The kernel and workgroup shape hyb_gemm would launch for m tokens on
+    this layout's matrix on the current device (hyb_gemm_shape; host only)."""
+    out = (ctypes.c_int32 * 4)()
+    check(lib().hyb_gemm_shape(ctypes.byref(layout), int(m), ctypes.byref(out)), "hyb_gemm_shape")
+    return {"kernel": KERNEL_NAMES[out[0]], "token_blocks": out[1], "waves": out[2], "row_groups": out[3]}
 
 
 def stream_read(buf, nbytes: int, sink, grid: int) -> None:

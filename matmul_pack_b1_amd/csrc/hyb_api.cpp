@@ -364,6 +364,19 @@ hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 
+hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out) {
+  hyb_status st = check_layout(layout, true);
+  if (st != HYB_OK) return st;
+  if (!out) return fail(HYB_ERR_INVALID_ARG, "out is NULL");
+  if (m < 1) return fail(HYB_ERR_SHAPE, "m = %d, the query needs m >= 1", m);
+  const hyb::GemmRoute r = hyb::gemm_route_device(*layout, m);
+  out[0] = r.kernel;
+  out[1] = r.mb;
+  out[2] = r.waves;
+  out[3] = r.rg;
+  return ok();
+}
+
 hyb_status hyb_stream_read(const void* p, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
   if (bytes < 0 || bytes >= (int64_t(1) << 31)) return fail(HYB_ERR_SHAPE, "bytes must be in [0, 2^31)");
   if (grid < 1 || grid > 65535) return fail(HYB_ERR_INVALID_ARG, "grid must be in [1, 65535]");

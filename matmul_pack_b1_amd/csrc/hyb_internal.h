@@ -41,6 +41,21 @@ constexpr int kMaxRank = HYB_MAX_RANK;
 hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
                                int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s);
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+// Kernel and workgroup shape of a product (hyb_gemm_shape).
+constexpr int kRouteDecode = 1;    // k_gemv
+constexpr int kRouteRegister = 2;  // k_gemm_rx
+constexpr int kRouteLds = 3;       // k_gemm_lds
+struct GemmRoute {
+  int kernel;  // kRoute*
+  int mb;      // token blocks of 16 per workgroup (0: the decode kernel)
+  int waves;   // wavefronts per workgroup
+  int rg;      // 64-row groups per workgroup (0: the decode kernel's 16-row slabs)
+};
+// What the matrix-core kernels run for m >= 1 tokens on an n-row matrix
+// over `cus` compute units.
+GemmRoute gemm_route(int64_t n, int m, int64_t cus);
+// What hyb_gemm runs on the current device (decode kernel included).
+GemmRoute gemm_route_device(const hyb_layout& L, int m);
 // With rank > 0 the kernels add T U^T (t: m x rank fp32, u: n x rank) to
 // every output before it is stored.
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m,

@@ -1934,6 +1934,93 @@ hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed*
   return hipSuccess;
 }
 
+// Workgroup shape by token count.  Up to 16 tokens the register-fed kernel
+// k_gemm_rx runs 16 tokens x 64 rows per workgroup.  Up to 128 tokens it
+// runs in the shape that fills the CUs best (one exception below for wide
+// matrices at 65-128 tokens).  From 129 tokens one of four LDS-fed shapes
+// runs, 256 weight rows by BM = 256, 192, 128 or 64 tokens.  Every
+// workgroup walks all of K, so the time is the number of rounds of
+// workgroups over the compute units times the time of one workgroup; the
+// relative step costs of the shapes are measured (a 256-token step costs 1,
+// a 192-token step 0.8, a 128-token step 0.64, a 64-token step 0.57), and
+// the shape with the smallest product runs, unless a register-fed shape,
+// priced the same way, costs under 0.9 of it.
+GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
+  const int64_t groups = n / 64;  // 64-row workgroups of the register-fed kernel
+  if (m <= 16) {
+    // Eight wavefronts (one workgroup per CU) when the 64-row groups fit in
+    // one round, else four (two workgroups per CU).
+    return GemmRoute{kRouteRegister, 1, groups <= cus ? 8 : 4, 1};
+  }
+  // Register-fed shapes: token blocks of 16 per workgroup, wavefronts, 64-row
+  // groups per workgroup; and the time of one round of each, relative to one
+  // round of the 256-token LDS shape over the same K (measured on 1024 to
+  // 8192 rows, K = 4096 to 28672, 24 to 1024 tokens).
+  constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
+  constexpr double kRound[5] = {0.12, 0.155, 0.21, 0.21, HYB_GEMM_C_RX};
+  auto rx_wgs = [&](int i) {
+    return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
+  };
+  auto rx = [&](int i) { return GemmRoute{kRouteRegister, kShapes[i][0], kShapes[i][1], kShapes[i][2]}; };
+  if (m <= 128) {
+    // The fewest rounds of workgroups over the CUs wins, then the most
+    // workgroups; on a tie the earlier entry (one row group before two,
+    // then the smaller token block).  Measured on 1024 to 17408 rows at
+    // 17-128 tokens: the pick is the fastest shape or within 3% of it.
+    int best = 0;
+    int64_t best_rounds = 0, best_wgs = 0;
+    for (int i = 0; i < 5; ++i) {
+      const int64_t wgs = rx_wgs(i);
+      const int64_t rounds = (wgs + cus - 1) / cus;
+      if (i == 0 || rounds < best_rounds || (rounds == best_rounds && wgs > best_wgs)) {
+        best = i;
+        best_rounds = rounds;
+        best_wgs = wgs;
+      }
+    }
+    // A wide matrix can need two rounds of the 128-row x 64-token shape
+    // while the 64-token LDS shape (256 rows per workgroup) fits the whole
+    // product in one; that round is cheaper than two (28672 x 8192 at 80-128
+    // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
+    if (best == 4 && best_rounds >= 2 && ((n + 255) / 256) * ((m + 63) / 64) <= cus)
+      return GemmRoute{kRouteLds, 4, 8, 4};
+    return rx(best);
+  }
+  const int64_t gn = (n + 255) / 256;
+  auto cost = [&](int64_t bm, double step) {
+    return double((gn * ((m + bm - 1) / bm) + cus - 1) / cus) * step;
+  };
+  const double c256 = cost(256, 1.0), c192 = cost(192, HYB_GEMM_C192), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
+  const double best = c256 < c192 ? (c256 < c128 ? (c256 < c64 ? c256 : c64) : (c128 < c64 ? c128 : c64))
+                                  : (c192 < c128 ? (c192 < c64 ? c192 : c64) : (c128 < c64 ? c128 : c64));
+  // A matrix with few 256-row blocks (a short one, or a short and deep one
+  // such as 8192 x 28672) leaves most CUs idle under every LDS shape; the
+  // cheapest register-fed shape runs when it costs under 0.9 of the best LDS
+  // shape (e.g. 1024 x 4096 at 160-1024 tokens: 1.3-1.9x faster; 8192 x
+  // 28672 at 160-256 tokens: 382 -> 169-231 us).  A shape needing more than
+  // 65535 token blocks, the register-fed grid's limit, is not a candidate.
+  int rx_best = -1;
+  double rx_cost = 0.0;
+  for (int i = 0; i < 5; ++i) {
+    if ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
+    const double c = double((rx_wgs(i) + cus - 1) / cus) * kRound[i];
+    if (rx_best < 0 || c < rx_cost) {
+      rx_best = i;
+      rx_cost = c;
+    }
+  }
+  if (rx_best >= 0 && rx_cost < 0.9 * best) return rx(rx_best);
+  if (c256 == best) return GemmRoute{kRouteLds, 16, 8, 4};
+  if (c192 == best) return GemmRoute{kRouteLds, 12, 8, 4};
+  if (c128 == best) return GemmRoute{kRouteLds, 8, 8, 4};
+  return GemmRoute{kRouteLds, 4, 8, 4};
+}
+
+GemmRoute gemm_route_device(const hyb_layout& L, int m) {
+  if (gemv_preferred(L, m)) return GemmRoute{kRouteDecode, 0, gemv_waves(L.n / 16, m), 0};
+  return gemm_route(L.n, m, device_cus());
+}
+
 namespace {
 
 template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
@@ -1981,98 +2068,28 @@ int device_cus() {
   return n;
 }
 
-// Workgroup shape by token count.  Up to 128 tokens the register-fed
-// kernel k_gemm_rx runs (64 or 128 rows per workgroup, wavefronts
-// splitting K) in the shape that fills the CUs best (one exception below
-// for wide matrices at 65-128 tokens).  From 129 tokens one
-// of four LDS-fed shapes runs, 256 weight rows by BM = 256,
-// 192, 128 or 64 tokens.  Every workgroup walks all of K, so the time is
-// the number of rounds of workgroups over the compute units times the time
-// of one workgroup; the relative step costs of the shapes are measured (a
-// 256-token step costs 1, a 192-token step 0.8, a 128-token step 0.64, a
-// 64-token step 0.57), and the shape with the smallest product runs,
-// unless a register-fed shape, priced the same way, costs under 0.9 of it.
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
-  const int64_t cus = device_cus();
-  const int64_t groups = L.n / 64;  // 64-row workgroups of the register-fed kernel
-  if (m <= 16) {
-    // Eight wavefronts (one workgroup per CU) when the 64-row groups fit in
-    // one round, else four (two workgroups per CU).
-    if (groups <= cus) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
-    return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
-  }
-  // Register-fed shapes: token blocks of 16 per workgroup, wavefronts, 64-row
-  // groups per workgroup; and the time of one round of each, relative to one
-  // round of the 256-token LDS shape over the same K (measured on 1024 to
-  // 8192 rows, K = 4096 to 28672, 24 to 1024 tokens).
-  constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
-  constexpr double kRound[5] = {0.12, 0.155, 0.21, 0.21, HYB_GEMM_C_RX};
-  auto rx_wgs = [&](int i) {
-    return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
-  };
-  auto rx_run = [&](int i) {
-    switch (i) {
-      case 0: return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
-      case 1: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);
-      case 2: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
-      case 3: return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, s);
-      default: return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
-    }
-  };
-  if (m <= 128) {
-    // The fewest rounds of workgroups over the CUs wins, then the most
-    // workgroups; on a tie the earlier entry (one row group before two,
-    // then the smaller token block).  Measured on 1024 to 17408 rows at
-    // 17-128 tokens: the pick is the fastest shape or within 3% of it.
-    int best = 0;
-    int64_t best_rounds = 0, best_wgs = 0;
-    for (int i = 0; i < 5; ++i) {
-      const int64_t wgs = rx_wgs(i);
-      const int64_t rounds = (wgs + cus - 1) / cus;
-      if (i == 0 || rounds < best_rounds || (rounds == best_rounds && wgs > best_wgs)) {
-        best = i;
-        best_rounds = rounds;
-        best_wgs = wgs;
-      }
-    }
-    // A wide matrix can need two rounds of the 128-row x 64-token shape
-    // while the 64-token LDS shape (256 rows per workgroup) fits the whole
-    // product in one; that round is cheaper than two (28672 x 8192 at 80-128
-    // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
-    if (best == 4 && best_rounds >= 2 && ((L.n + 255) / 256) * ((m + 63) / 64) <= cus)
-      return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, s);
-    return rx_run(best);
-  }
-  const int64_t gn = (L.n + 255) / 256;
-  auto cost = [&](int64_t bm, double step) {
-    return double((gn * ((m + bm - 1) / bm) + cus - 1) / cus) * step;
-  };
-  const double c256 = cost(256, 1.0), c192 = cost(192, HYB_GEMM_C192), c128 = cost(128, 0.64), c64 = cost(64, 0.57);
-  const double best = c256 < c192 ? (c256 < c128 ? (c256 < c64 ? c256 : c64) : (c128 < c64 ? c128 : c64))
-                                  : (c192 < c128 ? (c192 < c64 ? c192 : c64) : (c128 < c64 ? c128 : c64));
-  // A matrix with few 256-row blocks (a short one, or a short and deep one
-  // such as 8192 x 28672) leaves most CUs idle under every LDS shape; the
-  // cheapest register-fed shape runs when it costs under 0.9 of the best LDS
-  // shape (e.g. 1024 x 4096 at 160-1024 tokens: 1.3-1.9x faster; 8192 x
-  // 28672 at 160-256 tokens: 382 -> 169-231 us).
-  // (a shape needing more than 65535 token blocks, the register-fed grid's
-  // limit, is not a candidate)
-  int rx_best = -1;
-  double rx_cost = 0.0;
-  for (int i = 0; i < 5; ++i) {
-    if ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
-    const double c = double((rx_wgs(i) + cus - 1) / cus) * kRound[i];
-    if (rx_best < 0 || c < rx_cost) {
-      rx_best = i;
-      rx_cost = c;
+  const GemmRoute r = gemm_route(L.n, m, device_cus());
+  if (r.kernel == kRouteLds) {
+    switch (r.mb) {
+      case 16: return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
+      case 12: return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
+      case 8: return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);
+      default: return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, s);
     }
   }
-  if (rx_best >= 0 && rx_cost < 0.9 * best) return rx_run(rx_best);
-  if (c256 == best) return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
-  if (c192 == best) return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
-  if (c128 == best) return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);
-  return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, s);
+  if (r.rg == 2) {
+    if (r.mb == 2) return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, s);
+    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
+  }
+  switch (r.mb) {
+    case 1:
+      if (r.waves == 8) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
+      return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
+    case 2: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);
+    default: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
+  }
 }
 
 template <int DT, int META>

@@ -308,3 +308,58 @@ def test_product_path_has_no_cpu_fallback():
         if name.endswith(".py"):
             text = open(os.path.join(ROOT, "matmul_pack_b1_amd", name)).read()
             assert "import oracle" not in text and "from oracle" not in text, name
+
+
+# -------------------------------------------------- kernel routing --------
+
+def _layout(n, k, b):
+    L, _ = hb.plan(n, k, b, b, "bf16", "idx2", np.zeros((n // b, k // b), np.uint8))
+    return L
+
+
+# (n, k, tile, m) -> (kernel, token blocks, wavefronts, row groups) on a
+# 256-CU device (the MI355X; also the count assumed when no device is
+# visible).  These are the routes the GPU parity tests' docstrings name.
+ROUTES = [
+    ((14336, 4096, 128, 1), ("decode", 0, 4, 0)),
+    ((1024, 4096, 128, 16), ("decode", 0, 16, 0)),       # short matrix: decode kernel up to 16 tokens
+    ((14336, 4096, 128, 12), ("register", 1, 8, 1)),
+    ((17408, 5120, 64, 12), ("register", 1, 4, 1)),      # more 64-row groups than CUs
+    ((17408, 5120, 64, 16), ("register", 1, 4, 1)),
+    ((17408, 5120, 64, 40), ("register", 4, 4, 2)),
+    ((17408, 5120, 64, 96), ("register", 2, 4, 2)),
+    ((17408, 5120, 64, 100), ("lds", 4, 8, 4)),          # one LDS round instead of two register-fed
+    ((28672, 8192, 128, 96), ("lds", 4, 8, 4)),
+    ((17408, 5120, 64, 2048), ("lds", 12, 8, 4)),
+    ((14336, 4096, 128, 200), ("lds", 4, 8, 4)),
+    ((14336, 4096, 128, 300), ("lds", 8, 8, 4)),
+    ((14336, 4096, 128, 700), ("lds", 12, 8, 4)),
+    ((14336, 4096, 128, 1024), ("lds", 16, 8, 4)),
+    ((14336, 4096, 128, 2048), ("lds", 16, 8, 4)),
+    ((8192, 28672, 128, 256), ("register", 4, 4, 2)),    # few 256-row blocks
+    ((8192, 28672, 128, 512), ("lds", 4, 8, 4)),
+    ((4096, 4096, 128, 160), ("register", 4, 8, 1)),
+    ((1024, 4096, 128, 384), ("register", 2, 8, 1)),
+    ((8192, 256, 64, 1024), ("lds", 8, 8, 4)),
+    ((8192, 256, 64, 2048), ("lds", 16, 8, 4)),
+    ((16384, 256, 64, 256), ("lds", 4, 8, 4)),
+    ((64, 64, 64, 4_300_000), ("lds", 16, 8, 4)),        # register-fed grids would exceed 65535 blocks
+]
+
+
+@pytest.mark.parametrize("case,expect", ROUTES)
+def test_gemm_routes(case, expect):
+    n, k, b, m = case
+    got = hb.gemm_shape(_layout(n, k, b), m)
+    assert (got["kernel"], got["token_blocks"], got["waves"], got["row_groups"]) == expect, got
+
+
+def test_gemm_shape_rejects(L):
+    lay = _layout(1024, 1024, 128)
+    out = (ctypes.c_int32 * 4)()
+    assert L.hyb_gemm_shape(ctypes.byref(lay), 0, ctypes.byref(out)) == 2   # m < 1
+    assert L.hyb_gemm_shape(ctypes.byref(lay), 8, None) == 1                # out NULL
+    assert L.hyb_gemm_shape(None, 8, ctypes.byref(out)) == 1                # layout NULL
+    bad = hb.HybLayout.from_buffer_copy(lay)
+    bad.magic = 0
+    assert L.hyb_gemm_shape(ctypes.byref(bad), 8, ctypes.byref(out)) == 5   # HYB_ERR_FORMAT
