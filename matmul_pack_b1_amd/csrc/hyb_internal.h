@@ -1,5 +1,5 @@
 // Internal interface between the host-side argument checks (hyb_api.cpp) and
-// the kernel launchers (hyb_kernels.hip).  Everything reaching a launcher has
+// the kernel launchers (hyb_pack.hip, hyb_gemv.hip, hyb_gemm.hip, hyb_lowrank.hip).  Everything reaching a launcher has
 // already been validated.
 #pragma once
 
@@ -41,6 +41,12 @@ constexpr int kMaxRank = HYB_MAX_RANK;
 hipError_t launch_gemv_grouped(int count, const hyb_layout* L, const hyb_packed* P, const void* x, int m,
                                int64_t ldx, void* const* y, int y_dtype, const int64_t* ldy, hipStream_t s);
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+// Compute units of the current device (256 when no device is visible);
+// cached per device.
+int device_cus();
+// Wavefronts per 16-row slab of the decode kernel for a matrix of `slabs`
+// slabs at m tokens.
+int gemv_waves(int64_t slabs, int m);
 // Kernel and workgroup shape of a product (hyb_gemm_shape).
 constexpr int kRouteDecode = 1;    // k_gemv
 constexpr int kRouteRegister = 2;  // k_gemm_rx
