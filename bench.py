@@ -50,12 +50,44 @@ sys.path.insert(0, HERE)
 
 METRIC = "hybrid 2:4/dense GEMV µs + achieved HBM GB/s at 8B MLP shape; speedup vs dense"
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per hybrid k_gemv launch at this workload, from rocprofv3
-# FETCH_SIZE + WRITE_SIZE scaled by a plain 128 MiB copy's readings
-# (profiles/k_gemv_llama8b_up_14336x4096_m1_hbm_traffic.md).  Valid for the
-# kernel as profiled; re-measure after changing it.
-TRAFFIC_BYTES_PER_LAUNCH = 81_907_712
+# HBM bytes per hybrid k_gemv launch at this workload, from two rocprofv3
+# --pmc passes (FETCH_SIZE, then WRITE_SIZE) scaled by a plain 128 MiB copy's
+# readings; the summary, its command and the kernel it covers are in
+# TRAFFIC_PROFILE.  Valid for the kernel as profiled; re-measure after
+# changing it.
+TRAFFIC_BYTES_PER_LAUNCH = None
+TRAFFIC_PROFILE = "profiles/k_gemv_llama8b_up_14336x4096_m1_hbm_traffic.md"
+TRAFFIC_KERNEL = "k_gemv<MT=1, B2=128, bf16, idx2, WAVES=4, STAGES=2, LR=false, XR=true>"
 MFMA_PEAK_BF16_TFLOPS = 2500.0
+
+
+def roofline(alg_bytes_: int, flops: int, us: float, kernel: str) -> dict:
+    """Roofline of one product: the larger of bytes / 8 TB/s and flops /
+    2.5 PF (dense bf16 matrix-core peak) bounds it; `frac` is that time over
+    the measured time, `achieved` the rate in the bound's own unit."""
+    t_hbm = alg_bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_BF16_TFLOPS * 1e12)
+    sec = us * 1e-6
+    if t_hbm >= t_mfma:
+        ach = alg_bytes_ / sec / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(t_hbm / sec, 4), "alg_bytes": alg_bytes_, "alg_flops": flops,
+                "roofline_us": round(1e6 * t_hbm, 3), "kernel": kernel}
+    ach = flops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(t_mfma / sec, 4), "alg_bytes": alg_bytes_, "alg_flops": flops,
+            "roofline_us": round(1e6 * t_mfma, 3), "kernel": kernel}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def log(*a):
@@ -108,16 +140,8 @@ def setup_matrix(hb, torch, mat, tmap, meta, rotate_bytes, dev):
     return w, w_bits, copies
 
 
-def cpu_baseline(mat, w_bits, tmap, x_bits, layout, budget_s=12.0):
-    """The oracle as it stands (unpack to dense + float64 product), timed on
-    this host's cores on the full workload matrix."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    P = oracle.pack(w_bits, tmap, mat.b1, mat.b2, "idx2")
+def _oracle_passes(oracle, P, mat, x_bits, budget_s):
+    """Median seconds of (unpack, float64 product) passes of the oracle."""
     times, unp, mm = [], [], []
     t_end = time.perf_counter() + budget_s
     while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 5):
@@ -131,16 +155,42 @@ def cpu_baseline(mat, w_bits, tmap, x_bits, layout, budget_s=12.0):
         mm.append(t2 - t1)
         if time.perf_counter() > t_end and len(times) >= 1:
             break
-    med = statistics.median(times)
+    return statistics.median(times), statistics.median(unp), statistics.median(mm), len(times)
+
+
+def cpu_baseline(mat, w_bits, tmap, x_bits, layout, budget_s=12.0):
+    """The oracle as it stands (unpack to dense + float64 product), timed on
+    this host's cores on the full workload matrix: once with the BLAS
+    threads it starts with, once limited to one thread."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        threads = os.cpu_count() or 1
+    P = oracle.pack(w_bits, tmap, mat.b1, mat.b2, "idx2")
+    gb = alg_bytes(layout, x_bits.shape[0])
+    med, unp, mm, runs = _oracle_passes(oracle, P, mat, x_bits, budget_s)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            med1, unp1, mm1, runs1 = _oracle_passes(oracle, P, mat, x_bits, budget_s / 2)
+        one = {"value": round(gb / med1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "seconds_per_pass": round(med1, 4),
+               "sample": f"median of {runs1} runs ({unp1:.3f} s unpack + {mm1:.3f} s matmul)"}
     return {
-        "value": round(alg_bytes(layout, x_bits.shape[0]) / med / 1e9, 4),
+        "value": round(gb / med / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"whole {mat.n}x{mat.k} matrix, M={x_bits.shape[0]}: oracle unpack + float64 "
-                   f"X.W'^T and |X|.|W'|^T, median of {len(times)} runs "
-                   f"({statistics.median(unp):.3f} s unpack + {statistics.median(mm):.3f} s matmul)"),
+                   f"X.W'^T and |X|.|W'|^T, median of {runs} runs "
+                   f"({unp:.3f} s unpack + {mm:.3f} s matmul)"),
         "seconds_per_pass": round(med, 4),
+        "single_core": one,
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
 
 
@@ -155,7 +205,7 @@ def main():
     ap.add_argument("--prefill-m", type=int, default=2048,
                     help="token count of the prefill GEMM measurement")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,prefill,tall)")
+                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,patterns,prefill,tall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 128 MiB device copies (torch copy kernel) as a counter reference")
@@ -179,7 +229,7 @@ def main():
     dev = torch.device("cuda:0")
     rotate = int(args.rotate_gib * (1 << 30))
     rows = set(args.only.split(",")) if args.only else {"pack", "gemv", "dense", "unpack", "gemm", "grouped",
-                                                         "lowrank", "nm48", "prefill", "tall"}
+                                                         "lowrank", "nm48", "patterns", "prefill", "tall"}
 
     if args.copy_calibration:
         # A plain copy of known size: 128 MiB read + 128 MiB written per
@@ -382,7 +432,9 @@ def main():
         fl = alg_flops(L, args.gemm_m)
         res_rows["gemm"].update({"m": args.gemm_m, "alg_flops": fl,
                                  "TFLOPs": round(fl / (res_rows["gemm"]["us_mean"] * 1e-6) / 1e12, 2),
-                                 "GBps": round(alg_bytes(L, args.gemm_m) / (res_rows["gemm"]["us_mean"] * 1e-6) / 1e9, 2)})
+                                 "GBps": round(alg_bytes(L, args.gemm_m) / (res_rows["gemm"]["us_mean"] * 1e-6) / 1e9, 2),
+                                 "roofline": roofline(alg_bytes(L, args.gemm_m), fl, res_rows["gemm"]["us_mean"],
+                                                      kernel_text(hb, L, args.gemm_m))})
     out["config"] = {"workload": f"Llama-3.1-8B up projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles, "
                                  f"{L.n_sparse}/{L.tiles_n * L.tiles_k} tiles 2:4 ({args.meta}), decode M=1",
                      "n": mat.n, "k": mat.k, "tile": [mat.b1, mat.b2], "n_sparse_tiles": L.n_sparse,
@@ -392,7 +444,10 @@ def main():
     if out["value"] is not None:
         out["roofline"] = {"bound": "hbm", "achieved": out["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(out["value"] / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_BYTES_PER_LAUNCH,
-                           "kernel": "k_gemv<1,128,bf16>", "alg_bytes_per_launch": gb}
+                           "traffic_source": (f"stored figure from {TRAFFIC_PROFILE} (rocprofv3 --pmc FETCH_SIZE "
+                                              f"and WRITE_SIZE of {TRAFFIC_KERNEL}, scaled by a 128 MiB copy)"
+                                              if TRAFFIC_BYTES_PER_LAUNCH else "not measured for this kernel"),
+                           "kernel": TRAFFIC_KERNEL, "alg_bytes_per_launch": gb}
     if stream_ref is not None and out.get("value"):
         stream_ref["gemv_frac_of_stream"] = round(out["value"] / stream_ref["GBps"], 4)
         out["stream_reference"] = stream_ref
@@ -404,6 +459,10 @@ def main():
         log("[bench] 4:8 against 2:4")
         out["nm48"] = nm48(hb, torch, wl, dev)
         log(f"[bench] nm48: {out['nm48']}")
+    if "patterns" in rows:
+        log("[bench] one metadata code throughout against mixed codes")
+        out["patterns"] = patterns(hb, torch, wl, dev, args.meta)
+        log(f"[bench] patterns: {out['patterns']}")
     if "lowrank" in rows:
         log("[bench] sparse + low-rank decode")
         out["lowrank"] = lowrank(hb, torch, wl, dev, args.meta)
@@ -504,6 +563,7 @@ def product_row(hb, torch, dev, mat, m, meta, name):
     fl = alg_flops(L, m)
     fl_dense = 2 * m * mat.n * mat.k
     tf = fl / (us_h * 1e-6) / 1e12
+    ab = alg_bytes(L, m)
     out = {"workload": f"{name}, {L.n_sparse}/{L.tiles_n * L.tiles_k} tiles 2:4 ({meta}), prefill M={m}",
            "m": m, "hybrid_us": round(us_h, 2), "dense_same_kernel_us": round(us_d, 2),
            "vendor_blas_dense_us": round(us_v, 2), "alg_flops": fl, "dense_flops": fl_dense,
@@ -511,12 +571,45 @@ def product_row(hb, torch, dev, mat, m, meta, name):
            "vendor_blas_TFLOPs": round(fl_dense / (us_v * 1e-6) / 1e12, 1),
            "speedup_vs_dense_same_kernel": round(us_d / us_h, 4),
            "speedup_vs_vendor_blas": round(us_v / us_h, 4),
-           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_BF16_TFLOPS, 4),
-                        "kernel": kernel_text(hb, L, m)},
+           "alg_bytes": ab, "GBps": round(ab / (us_h * 1e-6) / 1e9, 1),
+           "roofline": roofline(ab, fl, us_h, kernel_text(hb, L, m)),
            "timing": f"graph burst of {n_launch} launches over 2 rotating copies, median of 5 replays"}
     del hyb, den, wt, w, x, y, yb
     torch.cuda.empty_cache()
+    return out
+
+
+def patterns(hb, torch, wl, dev, meta):
+    """The decode product on the Llama-3.1-8B up projection (M = 1, the same
+    tile map) with the seeded weights, whose 2:4 groups keep all six patterns
+    in equal measure, against weights whose every group keeps positions 0
+    and 1 (columns 2 and 3 of each group zeroed, so one metadata code fills
+    the whole stream).  The kernel reads a fixed stride whatever the codes
+    (SparseDecoding abstract), so the two times should agree."""
+    mat = wl.workload(2).matrices[0]
+    tmap = mat.tile_map()
+    wb = mat.weight_bits()
+    same = wb.copy()
+    same[:, 2::4] = 0
+    same[:, 3::4] = 0
+    x = hb.bits_to_tensor(mat.activation_bits(1), mat.dtype, dev)
+    y = torch.empty((1, mat.n), dtype=torch.float32, device=dev)
+    out = {}
+    for name, bits in (("mixed_patterns", wb), ("one_pattern", same)):
+        w = hb.bits_to_tensor(bits, mat.dtype, dev)
+        P0 = hb.pack(w, tmap, mat.b1, mat.b2, meta)
+        n_copies = copies_for(P0.weight_bytes(), 1 << 30)
+        Ps = [P0] + [hb.pack(w, tmap, mat.b1, mat.b2, meta) for _ in range(n_copies - 1)]
+        torch.cuda.synchronize()
+        if name == "one_pattern":
+            codes = np.unique(P0.meta.cpu().numpy())
+            out["one_pattern_codes"] = [hex(int(c)) for c in codes]
+        us = graph_us(torch, lambda c: [hb.gemv(Ps[(3 * i) % n_copies], x, out=y) for i in range(c)],
+                      2 * n_copies)
+        out[name] = {"us": round(us, 3), "GBps": round(alg_bytes(P0.layout, 1) / (us * 1e-6) / 1e9, 1)}
+        del Ps, P0, w
+        torch.cuda.empty_cache()
+    out["one_over_mixed"] = round(out["one_pattern"]["us"] / out["mixed_patterns"]["us"], 4)
     return out
 
 

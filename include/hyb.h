@@ -130,6 +130,14 @@ hyb_status hyb_plan(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t dtype,
                     int32_t meta, const uint8_t* tile_map, hyb_layout* out,
                     int32_t* tidx_out);
 
+/* Check a layout held by the caller (host only, nothing enqueued): the
+ * magic and version, the geometry rules of hyb_plan, and that the tile
+ * counts and stream sizes agree with each other -- e.g. a header read back
+ * from a file.  Returns HYB_OK, HYB_ERR_INVALID_ARG (NULL), HYB_ERR_FORMAT
+ * (magic, version, counts or sizes), HYB_ERR_SHAPE or HYB_ERR_DTYPE.  Tile
+ * sizes outside {64, 128, 256} pass here; the device calls reject them. */
+hyb_status hyb_layout_check(const hyb_layout* layout);
+
 /* Pack W into the streams of `dst` (the pruning and compression of PATCH
  * section 2 with the magnitude rule above; SparseDecoding abstract for the
  * fixed-stride bitmask storage).
@@ -141,15 +149,24 @@ hyb_status hyb_plan(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t dtype,
 hyb_status hyb_pack(const hyb_layout* layout, const void* w, int64_t ldw,
                     const hyb_packed* dst, void* stream);
 
-/* Rebuild W' (n x k, row stride ldw) from packed streams: dense tiles as
- * stored, sparse groups with their two values at the coded columns and +0.0
- * at the other two.  Same alignment rules as hyb_pack. */
+/* Rebuild W' (n x k, row stride ldw) from packed streams, the inverse of
+ * hyb_pack: dense tiles as stored, sparse groups with their two values at
+ * the coded columns and +0.0 at the other two (PATCH section 2 "Meccanismo
+ * Principale": a sparse tile is the 2:4-pruned tile, the dropped entries
+ * zero; SparseDecoding abstract for the bitmask-indexed storage read back).
+ *   w_out  device, n x k elements of layout->dtype, row stride ldw >= k,
+ *          16-byte aligned, ldw % 8 == 0 (ldw >= 0 even when n or k is 0)
+ *   src    device streams as written by hyb_pack for *layout
+ * Bit-exact: w_out depends only on the stream bytes. */
 hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_out,
                       int64_t ldw, void* stream);
 
 /* Decode product, 0 <= m <= 16 tokens: Y[i, :] = W' X[i, :] for i < m
  * (SparseDecoding abstract: the decode-phase sparse matrix x vector product
- * over the compressed matrix).
+ * over the compressed matrix).  Up to 8 tokens (16 on a matrix with fewer
+ * than two 16-row slabs per compute unit) the decode kernel runs; 9-16
+ * tokens otherwise run the matrix-core kernel, exactly as hyb_gemm routes
+ * them (the decode kernel is bound by its vector arithmetic there).
  *   x       device, m x k of layout->dtype, row stride ldx >= k (elements),
  *           16-byte aligned, ldx % 8 == 0
  *   y       device, m x n, row stride ldy >= n, element type y_dtype in
@@ -164,7 +181,9 @@ hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x
 /* Grouped decode product: one launch (two when the matrices' sizes call
  * for different wavefront counts per slab, as hyb_gemv would pick for each
  * alone) multiplies the same x (0 <= m <= 16 tokens) by `count` packed
- * matrices, Y_g[i, :] = W'_g X[i, :].  A layer's
+ * matrices, Y_g[i, :] = W'_g X[i, :]; a matrix that hyb_gemv would run on
+ * the matrix cores (9-16 tokens on a long matrix) runs there in a launch of
+ * its own, checked with the others before anything is enqueued.  A layer's
  * projections that read the same activations (q, k and v; gate and up) carry
  * their own tile maps and sparsities (PATCH, gist.science, section 3
  * "Contributi Chiave": attention stays denser, MLP matrices sparser), and the
@@ -209,7 +228,8 @@ hyb_status hyb_lowrank_project(const void* v, int64_t ldv, int32_t rank, int64_t
  * product of X (S + U V^T)^T with S = W' packed here (3BASiL section 4
  * "Risultati Sperimentali" pairs 2:4 sparsity with rank 64).  T = X V
  * (m x rank) comes from hyb_lowrank_project; this call adds T U^T inside the
- * decode kernel, after each row's sparse sum.
+ * decode kernel, after each row's sparse sum (9-16 tokens that hyb_gemv
+ * would run on the matrix cores run hyb_gemm_lowrank's kernel instead).
  *   layout, w, x, m, ldx, y, y_dtype, ldy  as for hyb_gemv
  *   t      device fp32, m x rank, row stride ldt >= rank, ldt % 4 == 0,
  *          16-byte aligned

@@ -26,7 +26,7 @@ MAX_GEMV_M = 16
 META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_MASK8}
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
-EXPORTED = ("hyb_plan", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
+EXPORTED = ("hyb_plan", "hyb_layout_check", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
             "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_shape", "hyb_stream_read",
             "hyb_status_str", "hyb_last_error", "hyb_abi_version")
 KERNEL_NAMES = {1: "decode", 2: "register", 3: "lds"}   # HYB_KERNEL_* of hyb_gemm_shape
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.hyb_plan.argtypes = [I64, I64, I32, I32, I32, I32, P, ctypes.POINTER(HybLayout), P]
     L.hyb_plan.restype = I32
+    L.hyb_layout_check.argtypes = [ctypes.POINTER(HybLayout)]
+    L.hyb_layout_check.restype = I32
     L.hyb_pack.argtypes = [ctypes.POINTER(HybLayout), P, I64, ctypes.POINTER(HybPacked), P]
     L.hyb_pack.restype = I32
     L.hyb_unpack.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I64, P]
@@ -158,13 +160,52 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_rows(t, name):
+def _check_2d(t, name):
     if t.dim() != 2:
         raise ValueError(f"{name} must be a 2-D tensor")
     if t.numel() and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride")
+
+
+def _check_gpu(t, name, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_rows(t, name):
+    _check_2d(t, name)
+    _check_gpu(t, name)
+
+
+def _check_x(P: "PackedWeight", x, name="x"):
+    """x must be m x k of the weight's dtype (checked before any device test,
+    so shape and type errors never reach the library)."""
+    _check_2d(x, name)
+    torch = _torch()
+    want = torch.bfloat16 if P.dtype == "bf16" else torch.float16
+    if x.dtype != want:
+        raise TypeError(f"{name} is {x.dtype}, the weight is {P.dtype}")
+    if x.shape[1] != P.shape[1]:
+        raise ValueError(f"{name} has {x.shape[1]} columns, the weight has k = {P.shape[1]}")
+
+
+def _check_out(out, shape, tdt, name="out"):
+    """A caller-supplied output must have exactly the shape and dtype the
+    library will write (it only knows the row stride)."""
+    _check_2d(out, name)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} is {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.dtype != tdt:
+        raise TypeError(f"{name} is {out.dtype}, expected {tdt}")
+
+
+def _check_same_device(P: "PackedWeight", device, what="x"):
+    for name in ("dense", "val", "meta", "tidx"):
+        t = getattr(P, name)
+        if t.numel() and t.device != device:
+            raise ValueError(f"packed {name} is on {t.device}, {what} on {device}")
 
 
 @dataclass
@@ -203,16 +244,79 @@ def allocate(layout: HybLayout, tidx_host: np.ndarray, device, dtype: str, meta:
                         tidx, dtype, meta)
 
 
+# ------------------------------------------------------------ save / load --
+#
+# A saved packed weight is the layout header -- the hyb_layout struct as laid
+# out in memory (104 bytes, little-endian, fixed-width fields) -- followed by
+# the dense, value, metadata and tile-index streams, each exactly the size
+# the header gives.  Loading checks the header with hyb_layout_check before
+# anything is allocated.
+
+DTYPE_NAMES = {v: k for k, v in DTYPE_CODES.items()}
+META_NAMES = {v: k for k, v in META_CODES.items()}
+
+
+def save(P: PackedWeight, path) -> None:
+    """Write a packed weight to `path` (header, then the four streams)."""
+    with open(path, "wb") as f:
+        f.write(bytes(P.layout))
+        for t in (P.dense, P.val, P.meta, P.tidx):
+            f.write(t.detach().cpu().contiguous().numpy().tobytes())
+
+
+def load(path, device) -> PackedWeight:
+    """Read a packed weight written by `save` onto `device`.  A header that
+    fails hyb_layout_check (bad magic, version, counts or sizes) raises
+    HybError with that status; a file of the wrong length raises ValueError."""
+    torch = _torch()
+    with open(path, "rb") as f:
+        head = f.read(ctypes.sizeof(HybLayout))
+        if len(head) != ctypes.sizeof(HybLayout):
+            raise ValueError(f"{path}: shorter than a layout header")
+        L = HybLayout.from_buffer_copy(head)
+        check(lib().hyb_layout_check(ctypes.byref(L)), "hyb_layout_check")
+        parts = []
+        for nbytes in (L.dense_bytes, L.val_bytes, L.meta_bytes, L.tidx_bytes):
+            b = f.read(int(nbytes))
+            if len(b) != nbytes:
+                raise ValueError(f"{path}: truncated stream ({len(b)} of {nbytes} bytes)")
+            parts.append(b)
+        if f.read(1):
+            raise ValueError(f"{path}: trailing bytes after the streams")
+    def dev_u8(b):
+        return torch.frombuffer(bytearray(b), dtype=torch.uint8).to(device) if b else \
+            torch.empty(0, dtype=torch.uint8, device=device)
+    tidx = torch.frombuffer(bytearray(parts[3]), dtype=torch.int32).to(device) if parts[3] else \
+        torch.empty(0, dtype=torch.int32, device=device)
+    return PackedWeight(L, dev_u8(parts[0]), dev_u8(parts[1]), dev_u8(parts[2]), tidx,
+                        DTYPE_NAMES[L.dtype], META_NAMES[L.meta])
+
+
 def pack(w, tile_map, b1: int, b2: int, meta: str = "idx2", out: PackedWeight | None = None) -> PackedWeight:
     """Pack a device matrix w (n x k, bf16 or fp16) with the given tile map
     (uint8 [n/b1, k/b2], 1 = sparse: 2:4, or 4:8 with meta "mask8").  `out`
     reuses existing buffers."""
-    _check_rows(w, "w")
+    _check_2d(w, "w")
     dtype = _dtype_name(w)
     n, k = w.shape
     if out is None:
+        _check_gpu(w, "w")
         L, tidx = plan(n, k, b1, b2, dtype, meta, tile_map)
         out = allocate(L, tidx, w.device, dtype, meta)
+    else:
+        # out's streams were planned for one matrix and map; w and the map
+        # must match them (the tile index on the device is not re-read: the
+        # map is checked through its tile counts)
+        L = out.layout
+        if (n, k) != (L.n, L.k) or (b1, b2) != (L.b1, L.b2):
+            raise ValueError(f"w is {n}x{k} with {b1}x{b2} tiles, out holds {L.n}x{L.k} with {L.b1}x{L.b2}")
+        if dtype != out.dtype or meta != out.meta_kind:
+            raise TypeError(f"w/meta are {dtype}/{meta}, out holds {out.dtype}/{out.meta_kind}")
+        L2, _ = plan(n, k, b1, b2, dtype, meta, tile_map)
+        if (L2.n_dense, L2.n_sparse) != (L.n_dense, L.n_sparse):
+            raise ValueError("the tile map does not match out's layout")
+        _check_gpu(w, "w")
+        _check_same_device(out, w.device, "w")
     P = out.packed_struct()
     st = lib().hyb_pack(ctypes.byref(out.layout), _ptr(w), int(w.stride(0)) if w.numel() else int(k),
                         ctypes.byref(P), _stream(w.device))
@@ -227,7 +331,9 @@ def unpack(P: PackedWeight, out=None):
     tdt = torch.bfloat16 if P.dtype == "bf16" else torch.float16
     if out is None:
         out = torch.empty((n, k), dtype=tdt, device=P.device)
-    _check_rows(out, "out")
+    _check_out(out, (n, k), tdt)
+    _check_gpu(out, "out")
+    _check_same_device(P, out.device, "out")
     st = lib().hyb_unpack(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(out),
                           int(out.stride(0)) if out.numel() else int(k), _stream(P.device))
     check(st, "hyb_unpack")
@@ -247,13 +353,19 @@ def _out_code(P: PackedWeight, out_dtype) -> int:
 
 def _product(fn_name: str, P: PackedWeight, x, out_dtype=None, out=None):
     torch = _torch()
-    _check_rows(x, "x")
+    _check_x(P, x)
     m = x.shape[0]
     n, k = P.shape
+    if out is not None and out_dtype is None:
+        out_dtype = out.dtype
     code = _out_code(P, out_dtype)
     tdt = {HYB_F32: torch.float32, HYB_BF16: torch.bfloat16, HYB_F16: torch.float16}[code]
     if out is None:
         out = torch.empty((m, n), dtype=tdt, device=x.device)
+    _check_out(out, (m, n), tdt)
+    _check_gpu(x, "x")
+    _check_gpu(out, "out", x.device)
+    _check_same_device(P, x.device)
     fn = getattr(lib(), fn_name)
     st = fn(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
             int(x.stride(0)) if x.numel() else int(k), _ptr(out), code,
@@ -273,9 +385,13 @@ def gemv_grouped(Ps, x, out_dtype=None, outs=None):
     matrix."""
     torch = _torch()
     Ps = list(Ps)
-    _check_rows(x, "x")
+    _check_2d(x, "x")
+    for i, P in enumerate(Ps):
+        _check_x(P, x, f"x (matrix {i})")
     m = x.shape[0]
     count = len(Ps)
+    if outs is not None and out_dtype is None and len(outs):
+        out_dtype = outs[0].dtype
     codes = {_out_code(P, out_dtype) for P in Ps} or {HYB_F32}
     if len(codes) != 1:
         raise TypeError("all matrices must share one output type")
@@ -285,6 +401,12 @@ def gemv_grouped(Ps, x, out_dtype=None, outs=None):
         outs = [torch.empty((m, P.shape[0]), dtype=tdt, device=x.device) for P in Ps]
     if len(outs) != count:
         raise ValueError("one output per matrix")
+    for i, (o, P) in enumerate(zip(outs, Ps)):
+        _check_out(o, (m, P.shape[0]), tdt, f"outs[{i}]")
+    _check_gpu(x, "x")
+    for i, (o, P) in enumerate(zip(outs, Ps)):
+        _check_gpu(o, f"outs[{i}]", x.device)
+        _check_same_device(P, x.device)
     layouts = (HybLayout * max(count, 1))(*[P.layout for P in Ps])
     packed = (HybPacked * max(count, 1))(*[P.packed_struct() for P in Ps])
     ys = (ctypes.c_void_p * max(count, 1))(*[_ptr(o) for o in outs])
@@ -301,8 +423,8 @@ def lowrank_project(v, x, out=None):
     """T = X V (fp32, m x rank) for a low-rank factor V (k x rank) held
     transposed: `v` is rank x k with unit column stride, of x's dtype."""
     torch = _torch()
-    _check_rows(v, "v")
-    _check_rows(x, "x")
+    _check_2d(v, "v")
+    _check_2d(x, "x")
     if v.dtype != x.dtype or v.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("v and x must share one dtype, bfloat16 or float16")
     rank, k = v.shape
@@ -311,8 +433,10 @@ def lowrank_project(v, x, out=None):
         raise ValueError(f"x must have {k} columns")
     if out is None:
         out = torch.empty((m, rank), dtype=torch.float32, device=x.device)
-    elif out.shape != (m, rank) or out.dtype != torch.float32:
-        raise ValueError(f"out must be float32 {m} x {rank}")
+    _check_out(out, (m, rank), torch.float32)
+    _check_gpu(x, "x")
+    _check_gpu(v, "v", x.device)
+    _check_gpu(out, "out", x.device)
     code = HYB_BF16 if v.dtype == torch.bfloat16 else HYB_F16
     st = lib().hyb_lowrank_project(_ptr(v), int(v.stride(0)) if v.numel() else int(k), int(rank), int(k), code,
                                    _ptr(x), int(m), int(x.stride(0)) if x.numel() else int(k), _ptr(out),
@@ -323,20 +447,29 @@ def lowrank_project(v, x, out=None):
 
 def _lowrank(fn_name: str, P: PackedWeight, x, t, u, out_dtype, out):
     torch = _torch()
-    _check_rows(x, "x")
-    _check_rows(t, "t")
-    _check_rows(u, "u")
+    _check_x(P, x)
+    _check_2d(t, "t")
+    _check_2d(u, "u")
     m = x.shape[0]
     n, k = P.shape
     rank = t.shape[1]
-    if t.shape[0] != m or u.shape != (n, rank):
+    if t.shape[0] != m or tuple(u.shape) != (n, rank):
         raise ValueError(f"t must be {m} x rank and u {n} x rank")
     if t.dtype != torch.float32:
         raise TypeError("t must be float32")
+    if u.dtype != (torch.bfloat16 if P.dtype == "bf16" else torch.float16):
+        raise TypeError(f"u is {u.dtype}, the weight is {P.dtype}")
+    if out is not None and out_dtype is None:
+        out_dtype = out.dtype
     code = _out_code(P, out_dtype)
     tdt = {HYB_F32: torch.float32, HYB_BF16: torch.bfloat16, HYB_F16: torch.float16}[code]
     if out is None:
         out = torch.empty((m, n), dtype=tdt, device=x.device)
+    _check_out(out, (m, n), tdt)
+    _check_gpu(x, "x")
+    for name, tt in (("t", t), ("u", u), ("out", out)):
+        _check_gpu(tt, name, x.device)
+    _check_same_device(P, x.device)
     st = getattr(lib(), fn_name)(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
                                  int(x.stride(0)) if x.numel() else int(k), _ptr(t),
                                  int(t.stride(0)) if t.numel() else int(rank), _ptr(u),

@@ -96,6 +96,9 @@ hyb_status check_packed(const hyb_layout* L, const hyb_packed* P) {
 }
 
 hyb_status check_matrix_arg(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name) {
+  // A negative stride is rejected even for an empty operand: kernels build
+  // buffer ranges from rows * ld, which must never go negative.
+  if (ld < 0) return fail(HYB_ERR_INVALID_ARG, "%s row stride %lld is negative", name, (long long)ld);
   if (rows == 0 || cols == 0) return HYB_OK;
   if (!p) return fail(HYB_ERR_INVALID_ARG, "%s is NULL", name);
   if (ld < cols) return fail(HYB_ERR_INVALID_ARG, "%s row stride %lld < %lld", name, (long long)ld, (long long)cols);
@@ -121,6 +124,15 @@ hyb_status check_product(const hyb_layout* L, const hyb_packed* P, const void* x
     if (ldy < L->n) return fail(HYB_ERR_INVALID_ARG, "y row stride %lld < n = %lld", (long long)ldy, (long long)L->n);
     if (!aligned(y, elem_size(y_dtype))) return fail(HYB_ERR_INVALID_ARG, "y is not aligned to its element size");
   }
+  return HYB_OK;
+}
+
+// Launch limits of the matrix-core kernels (m > 0, n > 0).
+hyb_status check_mfma_limits(int32_t m, int64_t ldx) {
+  if (ldx < 0) return fail(HYB_ERR_INVALID_ARG, "ldx %lld is negative", (long long)ldx);
+  if (ldx * 2 * 256 >= (int64_t(1) << 31))
+    return fail(HYB_ERR_UNSUPPORTED, "matrix-core kernel needs ldx < 4194304 elements");
+  if ((int64_t(m) + 15) / 16 > 65535 * 8) return fail(HYB_ERR_UNSUPPORTED, "m = %d too large for one launch", m);
   return HYB_OK;
 }
 
@@ -190,10 +202,16 @@ hyb_status hyb_plan(int64_t n, int64_t k, int32_t b1, int32_t b2, int32_t dtype,
   return ok();
 }
 
+hyb_status hyb_layout_check(const hyb_layout* layout) {
+  const hyb_status st = check_layout(layout, false);
+  return st == HYB_OK ? ok() : st;
+}
+
 hyb_status hyb_pack(const hyb_layout* layout, const void* w, int64_t ldw, const hyb_packed* dst,
                     void* stream) {
   hyb_status st = check_layout(layout, true);
   if (st != HYB_OK) return st;
+  if (ldw < 0) return fail(HYB_ERR_INVALID_ARG, "w row stride %lld is negative", (long long)ldw);
   if (layout->n == 0 || layout->k == 0) return ok();
   st = check_packed(layout, dst);
   if (st != HYB_OK) return st;
@@ -207,6 +225,7 @@ hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_o
                       void* stream) {
   hyb_status st = check_layout(layout, true);
   if (st != HYB_OK) return st;
+  if (ldw < 0) return fail(HYB_ERR_INVALID_ARG, "w_out row stride %lld is negative", (long long)ldw);
   if (layout->n == 0 || layout->k == 0) return ok();
   st = check_packed(layout, src);
   if (st != HYB_OK) return st;
@@ -216,8 +235,11 @@ hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_o
                     "unpack launch");
 }
 
-hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
-                    int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+namespace {
+
+// The decode kernel itself (k_gemv), 0 <= m <= 16.
+hyb_status gemv_decode(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m, int64_t ldx,
+                       void* y, int32_t y_dtype, int64_t ldy, void* stream) {
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, hyb::kMaxGemvM);
   if (st != HYB_OK) return st;
   if (m == 0 || layout->n == 0) return ok();
@@ -226,6 +248,25 @@ hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x
   return hip_status(hyb::launch_gemv(*layout, *w, x, m, ldx, y, y_dtype, ldy,
                                      static_cast<hipStream_t>(stream)),
                     "gemv launch");
+}
+
+// Whether m tokens on this matrix run the decode kernel (the crossover of
+// hyb_gemm; a NULL or invalid layout takes the decode path, whose checks
+// report it).
+bool decode_route(const hyb_layout* layout, int32_t m) {
+  return m <= hyb::kGemvCrossoverM || !layout || check_layout(layout, true) != HYB_OK ||
+         (m <= hyb::kMaxGemvM && hyb::gemv_preferred(*layout, m));
+}
+
+}  // namespace
+
+hyb_status hyb_gemv(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                    int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  // 9-16 tokens where the decode kernel is VALU-bound run on the matrix
+  // cores, as in hyb_gemm (the 16-token decode kernel: 35 us on 14336 x
+  // 4096 against 19 us for the register-fed matrix-core kernel).
+  if (m > hyb::kMaxGemvM || decode_route(layout, m)) return gemv_decode(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 
 hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_packed* w, const void* x,
@@ -252,7 +293,36 @@ hyb_status hyb_gemv_grouped(int32_t count, const hyb_layout* layouts, const hyb_
   if (slabs >= (int64_t(1) << 31)) return fail(HYB_ERR_UNSUPPORTED, "too many rows for one launch");
   if (int64_t(m) * ldx * 2 >= (int64_t(1) << 31))
     return fail(HYB_ERR_UNSUPPORTED, "decode kernel needs m * ldx * 2 < 2^31 bytes of x");
-  return hip_status(hyb::launch_gemv_grouped(count, layouts, w, x, m, ldx, y, y_dtype, ldy,
+  // Matrices that hyb_gemv would run on the matrix cores (9-16 tokens on
+  // long matrices) take that kernel, one launch each, so every result stays
+  // bitwise that of hyb_gemv; the rest share the grouped decode launch.  The
+  // matrix-core limits are checked for all of them before anything is
+  // enqueued.
+  for (int32_t g = 0; g < count; ++g) {
+    if (layouts[g].n == 0 || decode_route(&layouts[g], m)) continue;
+    const hyb_status st = check_mfma_limits(m, ldx);
+    if (st != HYB_OK) return st;
+  }
+  hyb_layout dl[hyb::kMaxGroup];
+  hyb_packed dp[hyb::kMaxGroup];
+  void* dy[hyb::kMaxGroup];
+  int64_t dldy[hyb::kMaxGroup];
+  int32_t nd = 0;
+  for (int32_t g = 0; g < count; ++g) {
+    if (layouts[g].n == 0) continue;
+    if (decode_route(&layouts[g], m)) {
+      dl[nd] = layouts[g];
+      dp[nd] = w[g];
+      dy[nd] = y[g];
+      dldy[nd] = ldy[g];
+      ++nd;
+    } else {
+      const hyb_status st = hyb_gemm_mfma(&layouts[g], &w[g], x, m, ldx, y[g], y_dtype, ldy[g], stream);
+      if (st != HYB_OK) return st;
+    }
+  }
+  if (nd == 0) return ok();
+  return hip_status(hyb::launch_gemv_grouped(nd, dl, dp, x, m, ldx, dy, y_dtype, dldy,
                                              static_cast<hipStream_t>(stream)),
                     "grouped gemv launch");
 }
@@ -301,13 +371,16 @@ hyb_status check_rank(int32_t rank) {
 
 }  // namespace
 
-hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
-                            int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
-                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+namespace {
+
+// The fused decode kernel (k_gemv with the low-rank epilogue), 0 <= m <= 16.
+hyb_status gemv_lowrank_decode(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                               int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
+                               void* y, int32_t y_dtype, int64_t ldy, void* stream) {
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, hyb::kMaxGemvM);
   if (st != HYB_OK) return st;
   if ((st = check_rank(rank)) != HYB_OK) return st;
-  if (rank == 0) return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (rank == 0) return gemv_decode(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
   if (m == 0 || layout->n == 0) return ok();
   if ((st = check_lowrank(t, ldt, u, ldu, rank)) != HYB_OK) return st;
   if (int64_t(m) * ldx * 2 >= (int64_t(1) << 31))
@@ -317,23 +390,22 @@ hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const
                     "low-rank gemv launch");
 }
 
-namespace {
+}  // namespace
 
-// Launch limits of the matrix-core kernels (m > 0, n > 0).
-hyb_status check_mfma_limits(int32_t m, int64_t ldx) {
-  if (ldx * 2 * 256 >= (int64_t(1) << 31))
-    return fail(HYB_ERR_UNSUPPORTED, "matrix-core kernel needs ldx < 4194304 elements");
-  if ((int64_t(m) + 15) / 16 > 65535 * 8) return fail(HYB_ERR_UNSUPPORTED, "m = %d too large for one launch", m);
-  return HYB_OK;
+hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                            int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  if (m > hyb::kMaxGemvM || decode_route(layout, m))
+    return gemv_lowrank_decode(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
+  return hyb_gemm_lowrank(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
 }
 
-}  // namespace
 
 hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                             int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
                             void* y, int32_t y_dtype, int64_t ldy, void* stream) {
-  if (m >= 0 && (m <= hyb::kGemvCrossoverM || (layout && m <= hyb::kMaxGemvM && hyb::gemv_preferred(*layout, m))))
-    return hyb_gemv_lowrank(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
+  if (m >= 0 && m <= hyb::kMaxGemvM && decode_route(layout, m))
+    return gemv_lowrank_decode(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
   if (st != HYB_OK) return st;
   if ((st = check_rank(rank)) != HYB_OK) return st;
@@ -359,8 +431,8 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
 
 hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                     int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
-  if (m >= 0 && (m <= hyb::kGemvCrossoverM || (layout && m <= hyb::kMaxGemvM && hyb::gemv_preferred(*layout, m))))
-    return hyb_gemv(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  if (m >= 0 && m <= hyb::kMaxGemvM && decode_route(layout, m))
+    return gemv_decode(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 
@@ -370,6 +442,10 @@ hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out) {
   if (!out) return fail(HYB_ERR_INVALID_ARG, "out is NULL");
   if (m < 1) return fail(HYB_ERR_SHAPE, "m = %d, the query needs m >= 1", m);
   const hyb::GemmRoute r = hyb::gemm_route_device(*layout, m);
+  // hyb_gemm rejects what the matrix-core kernels cannot launch; so does
+  // the query (same limit as check_mfma_limits).
+  if (r.kernel != hyb::kRouteDecode && (int64_t(m) + 15) / 16 > 65535 * 8)
+    return fail(HYB_ERR_UNSUPPORTED, "m = %d too large for one launch", m);
   out[0] = r.kernel;
   out[1] = r.mb;
   out[2] = r.waves;

@@ -768,8 +768,10 @@ GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
   // 8192 rows, K = 4096 to 28672, 24 to 1024 tokens).
   constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
   constexpr double kRound[5] = {0.12, 0.155, 0.21, 0.21, HYB_GEMM_C_RX};
+  // token-block counts in int64: m may be close to INT32_MAX
+  const int64_t m64 = m;
   auto rx_wgs = [&](int i) {
-    return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
+    return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
   };
   auto rx = [&](int i) { return GemmRoute{kRouteRegister, kShapes[i][0], kShapes[i][1], kShapes[i][2]}; };
   if (m <= 128) {
@@ -792,7 +794,7 @@ GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
     // while the 64-token LDS shape (256 rows per workgroup) fits the whole
     // product in one; that round is cheaper than two (28672 x 8192 at 80-128
     // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
-    if (best == 4 && best_rounds >= 2 && ((n + 255) / 256) * ((m + 63) / 64) <= cus)
+    if (best == 4 && best_rounds >= 2 && ((n + 255) / 256) * ((m64 + 63) / 64) <= cus)
       return GemmRoute{kRouteLds, 4, 8, 4};
     return rx(best);
   }
@@ -812,7 +814,7 @@ GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
   int rx_best = -1;
   double rx_cost = 0.0;
   for (int i = 0; i < 5; ++i) {
-    if ((m + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
+    if ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
     const double c = double((rx_wgs(i) + cus - 1) / cus) * kRound[i];
     if (rx_best < 0 || c < rx_cost) {
       rx_best = i;

@@ -363,3 +363,165 @@ def test_gemm_shape_rejects(L):
     bad = hb.HybLayout.from_buffer_copy(lay)
     bad.magic = 0
     assert L.hyb_gemm_shape(ctypes.byref(bad), 8, ctypes.byref(out)) == 5   # HYB_ERR_FORMAT
+
+
+# ------------------------------------------- strides and the m limit -------
+
+def test_negative_strides_rejected_even_when_empty(L):
+    """A negative row stride is an invalid argument even when the operand is
+    empty (k = 0 or n = 0): the kernels size buffer ranges as rows * stride."""
+    lay_k0, _ = hb.plan(256, 0, 128, 128, "bf16", "idx2", np.zeros((2, 0), np.uint8))
+    for fn in ("hyb_gemv", "hyb_gemm", "hyb_gemm_mfma"):
+        assert _call(L, fn, lay_k0, m=20 if fn != "hyb_gemv" else 4, ldx=-8) == 1, fn
+    lay_n0, _ = hb.plan(0, 256, 128, 128, "bf16", "idx2", np.zeros((0, 2), np.uint8))
+    packed = hb.HybPacked(None, None, None, None)
+    assert L.hyb_pack(ctypes.byref(lay_n0), FAKE, -8, ctypes.byref(packed), None) == 1
+    assert L.hyb_unpack(ctypes.byref(lay_n0), ctypes.byref(packed), FAKE, -8, None) == 1
+    good = _good_layout()
+    assert _call(L, "hyb_gemm", good, m=40, ldx=-256) == 1
+
+
+def test_gemm_shape_applies_the_launch_limit():
+    """hyb_gemm_shape reports HYB_ERR_UNSUPPORTED where hyb_gemm_mfma would
+    reject the token count, instead of a register-fed shape computed from an
+    overflowed block count."""
+    lay = _layout(64, 64, 64)
+    for m in (2**31 - 1, 2**31 - 40, 16 * 65535 * 8 + 1):
+        with pytest.raises(hb.HybError) as e:
+            hb.gemm_shape(lay, m)
+        assert e.value.status == 4, m
+    got = hb.gemm_shape(lay, 16 * 65535 * 8)
+    assert got["kernel"] == "lds"
+
+
+# ------------------------------------- binding checks before any launch ----
+
+class _NoLaunch:
+    """Stands in for the library: host planning passes through, any device
+    entry point fails the test."""
+
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        if name in ("hyb_plan", "hyb_status_str", "hyb_last_error"):
+            return getattr(self._real, name)
+        raise AssertionError(f"{name} reached although the arguments are invalid")
+
+
+@pytest.fixture()
+def cpu_weight(monkeypatch):
+    torch = pytest.importorskip("torch")
+    real = hb.lib()
+    n, k, b = 256, 256, 128
+    tmap = np.array([[1, 0], [0, 1]], np.uint8)
+    lay, tidx = hb.plan(n, k, b, b, "bf16", "idx2", tmap)
+    P = hb.allocate(lay, tidx, torch.device("cpu"), "bf16", "idx2")
+    monkeypatch.setattr(hb, "_lib", _NoLaunch(real))
+    return torch, P, tmap
+
+
+def test_binding_rejects_bad_x(cpu_weight):
+    torch, P, _ = cpu_weight
+    with pytest.raises(ValueError, match="columns"):
+        hb.gemv(P, torch.zeros((1, 255), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="weight is bf16"):
+        hb.gemm(P, torch.zeros((3, 256), dtype=torch.float16))
+    with pytest.raises(TypeError, match="weight is bf16"):
+        hb.gemv(P, torch.zeros((1, 256), dtype=torch.float32))
+
+
+def test_binding_rejects_bad_out(cpu_weight):
+    torch, P, _ = cpu_weight
+    x = torch.zeros((2, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"expected \(2, 256\)"):
+        hb.gemv(P, x, out=torch.empty((1, 256), dtype=torch.float32))
+    with pytest.raises(ValueError, match=r"expected \(2, 256\)"):
+        hb.gemm_mfma(P, x, out=torch.empty((2, 300), dtype=torch.float32))
+    with pytest.raises(TypeError, match="expected torch.float32"):
+        hb.gemm(P, x, out_dtype=torch.float32, out=torch.empty((2, 256), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="must be float32 or the weight dtype"):
+        hb.gemv(P, x, out=torch.empty((2, 256), dtype=torch.float16))
+    with pytest.raises(ValueError, match=r"expected \(256, 256\)"):
+        hb.unpack(P, out=torch.empty((256, 128), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="expected torch.bfloat16"):
+        hb.unpack(P, out=torch.empty((256, 256), dtype=torch.float16))
+
+
+def test_binding_rejects_bad_pack_target(cpu_weight):
+    torch, P, tmap = cpu_weight
+    with pytest.raises(ValueError, match="out holds 256x256"):
+        hb.pack(torch.zeros((128, 256), dtype=torch.bfloat16), tmap[:1], 128, 128, out=P)
+    with pytest.raises(TypeError, match="out holds bf16/idx2"):
+        hb.pack(torch.zeros((256, 256), dtype=torch.float16), tmap, 128, 128, out=P)
+    with pytest.raises(ValueError, match="tile map does not match"):
+        hb.pack(torch.zeros((256, 256), dtype=torch.bfloat16), np.ones((2, 2), np.uint8), 128, 128, out=P)
+
+
+def test_binding_rejects_bad_grouped_and_lowrank(cpu_weight):
+    torch, P, _ = cpu_weight
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="columns"):
+        hb.gemv_grouped([P, P], torch.zeros((1, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"outs\[1\]"):
+        hb.gemv_grouped([P, P], x, outs=[torch.empty((1, 256)), torch.empty((2, 256))])
+    t = torch.zeros((1, 8), dtype=torch.float32)
+    with pytest.raises(TypeError, match="u is torch.float16"):
+        hb.gemv_lowrank(P, x, t, torch.zeros((256, 8), dtype=torch.float16))
+    with pytest.raises(ValueError, match="u 256 x rank"):
+        hb.gemm_lowrank(P, x, t, torch.zeros((256, 16), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"expected \(1, 8\)"):
+        hb.lowrank_project(torch.zeros((8, 256), dtype=torch.bfloat16), x, out=torch.empty((1, 16)))
+
+
+# ------------------------------------------------------- save / load -------
+
+def test_layout_check(L):
+    lay = _good_layout()
+    assert L.hyb_layout_check(ctypes.byref(lay)) == 0
+    assert L.hyb_layout_check(None) == 1
+    for field, value in (("magic", 0x31425949), ("version", 2), ("val_bytes", lay.val_bytes + 16),
+                         ("n_sparse", lay.n_sparse + 1), ("tidx_bytes", 0)):
+        bad = hb.HybLayout.from_buffer_copy(lay)
+        setattr(bad, field, value)
+        assert L.hyb_layout_check(ctypes.byref(bad)) == 5, field
+    bad = hb.HybLayout.from_buffer_copy(lay)
+    bad.dtype = 9
+    assert L.hyb_layout_check(ctypes.byref(bad)) == 3
+
+
+def test_save_load_round_trip_and_rejections(tmp_path):
+    """A packed weight written by save() reads back byte for byte; a header
+    with the wrong magic or version is refused with HYB_ERR_FORMAT, and a
+    short or overlong file with ValueError, before anything is allocated."""
+    torch = pytest.importorskip("torch")
+    n, k, b = 256, 384, 128
+    rng = np.random.default_rng(12)
+    tmap = (rng.random((n // b, k // b)) < 0.5).astype(np.uint8)
+    lay, tidx = hb.plan(n, k, b, b, "f16", "mask4", tmap)
+    P = hb.allocate(lay, tidx, torch.device("cpu"), "f16", "mask4")
+    for t in (P.dense, P.val, P.meta):
+        t.copy_(torch.from_numpy(rng.integers(0, 256, t.numel(), dtype=np.uint8)))
+    path = tmp_path / "w.hyb"
+    hb.save(P, path)
+    assert path.stat().st_size == ctypes.sizeof(hb.HybLayout) + lay.dense_bytes + lay.val_bytes + lay.meta_bytes + lay.tidx_bytes
+    Q = hb.load(path, torch.device("cpu"))
+    assert bytes(Q.layout) == bytes(P.layout)
+    assert (Q.dtype, Q.meta_kind) == ("f16", "mask4")
+    for name in ("dense", "val", "meta", "tidx"):
+        assert torch.equal(getattr(Q, name), getattr(P, name)), name
+    raw = path.read_bytes()
+    for offset, value in ((0, b"HYB2"), (4, (2).to_bytes(4, "little"))):
+        bad = tmp_path / f"bad{offset}.hyb"
+        bad.write_bytes(raw[:offset] + value + raw[offset + 4:])
+        with pytest.raises(hb.HybError) as e:
+            hb.load(bad, torch.device("cpu"))
+        assert e.value.status == 5
+    short = tmp_path / "short.hyb"
+    short.write_bytes(raw[:-4])
+    with pytest.raises(ValueError, match="truncated"):
+        hb.load(short, torch.device("cpu"))
+    long_ = tmp_path / "long.hyb"
+    long_.write_bytes(raw + b"\0")
+    with pytest.raises(ValueError, match="trailing"):
+        hb.load(long_, torch.device("cpu"))

@@ -3,8 +3,9 @@ the same seeded inputs.
 
 Bars: pack / unpack bit-exact; products within |y - y_ref| <= 2e-3 * s per
 element (s = sum_k |w x|), plus bitwise closed forms (one-hot, small
-integers, zero input).  Large workloads are checked on whole sampled tile
-rows that the oracle prunes and multiplies on its own."""
+integers, zero input).  Every output of every workload matrix is checked;
+the oracle prunes and multiplies large matrices a chunk of tile rows at a
+time.  Tests that name a kernel route assert it with hyb_gemm_shape."""
 import functools
 import sys
 
@@ -41,10 +42,9 @@ def upload(bits, dtype):
 
 
 def assert_close(y, yref, s, extra=0.0, what=""):
+    """The acceptance rule of the oracle (|y - y_ref| <= 2e-3 * s + extra)."""
     y = np.asarray(y, dtype=np.float64)
-    err = np.abs(y - yref)
-    bound = REL * s + extra
-    bad = err > bound
+    bad = ~oracle.within_bound(y, yref, s, REL, extra)
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside bound; first at {tuple(i)}: "
@@ -85,6 +85,55 @@ def sample_tile_rows(mat, count, seed=0):
     rng = np.random.default_rng(seed)
     tn = mat.n // mat.b1
     return np.sort(rng.choice(tn, size=min(count, tn), replace=False))
+
+
+def oracle_full(w_bits, tmap, b1, b2, x_bits, dtype, meta="idx2", chunk_rows=2048):
+    """Oracle y/s for every output row.  Tile rows are pruned and multiplied
+    a chunk at a time (pruning acts tile by tile, so the chunks give exactly
+    the rows of the whole), which bounds host memory at the 70B shapes."""
+    n = w_bits.shape[0]
+    step = max(b1, (chunk_rows // b1) * b1)
+    ys, ss = [], []
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        sub = oracle.prune(w_bits[r0:r1], tmap[r0 // b1:r1 // b1], b1, b2, meta)
+        y, s = oracle.ref_matmul(sub, x_bits, dtype)
+        ys.append(y)
+        ss.append(s)
+    return np.concatenate(ys, axis=1), np.concatenate(ss, axis=1)
+
+
+def oracle_full_lowrank(w_bits, tmap, b1, b2, x_bits, t, u_bits, dtype, chunk_rows=2048):
+    """oracle.ref_lowrank for every output row, a chunk of tile rows at a
+    time (as oracle_full)."""
+    n = w_bits.shape[0]
+    step = max(b1, (chunk_rows // b1) * b1)
+    ys, ss = [], []
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        sub = oracle.prune(w_bits[r0:r1], tmap[r0 // b1:r1 // b1], b1, b2)
+        y, s = oracle.ref_lowrank(sub, x_bits, t, u_bits[r0:r1], dtype)
+        ys.append(y)
+        ss.append(s)
+    return np.concatenate(ys, axis=1), np.concatenate(ss, axis=1)
+
+
+def device_cus():
+    return _torch().cuda.get_device_properties(0).multi_processor_count
+
+
+def expect_route(P, m, kernel, token_blocks=None, waves=None, row_groups=None):
+    """Assert the kernel and shape hyb_gemm launches for m tokens (the route
+    a test's docstring names).  The route table was measured on a 256-CU
+    device; on another CU count a different route is legitimate, and the
+    test is skipped rather than run on a kernel it does not claim to cover."""
+    got = hb.gemm_shape(P.layout, m)
+    want = {"kernel": kernel, "token_blocks": token_blocks, "waves": waves, "row_groups": row_groups}
+    want = {k: v for k, v in want.items() if v is not None}
+    same = all(got[k] == v for k, v in want.items())
+    if device_cus() != 256 and not same:
+        pytest.skip(f"route measured on 256 CUs; this device has {device_cus()} and runs {got}")
+    assert same, f"m={m}: expected {want}, hyb_gemm_shape gives {got}"
 
 
 def oracle_rows(w_bits, tmap, mat, tile_rows, x_bits):
@@ -147,10 +196,12 @@ def test_gemv_random(m, b1, b2, dtype, meta):
     assert_close(y.cpu().numpy(), yref, s, what="gemv")
 
 
-@pytest.mark.parametrize("config,index,m", [(1, 0, 1), (2, 0, 1), (2, 0, 4), (2, 0, 16),
-                                            (3, 0, 1), (3, 1, 4), (3, 2, 16), (3, 3, 1),
-                                            (3, 4, 4), (3, 5, 16), (3, 6, 1), (3, 6, 16)])
+@pytest.mark.parametrize("config,index,m", [(1, 0, 1), (2, 0, 1), (2, 0, 4), (2, 0, 16)]
+                         + [(3, i, m) for i in range(7) for m in (1, 4, 16)])
 def test_gemv_workloads(config, index, m):
+    """Every output of the 512x512 fp16 matrix, the 8B up projection (1, 4
+    and 16 tokens) and all seven matrices of one 8B decoder layer at 1, 4
+    and 16 tokens, against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(config, index)
     note(f"gemv workload {config}/{mat.name} m={m}")
@@ -162,9 +213,9 @@ def test_gemv_workloads(config, index, m):
 
 
 @pytest.mark.parametrize("index", range(6))
-def test_gemv_70b_endpoints_sampled(index):
+def test_gemv_70b_endpoints_full(index):
     """28672x8192 and 8192x28672 at 0%, 100% and checkerboard sparse tiles,
-    full-size launch, checked on 8 sampled tile rows."""
+    full-size launch, every output against the oracle."""
     torch = _torch()
     mat = wl.workload(4).matrices[index]
     note(f"gemv 70B {mat.name}")
@@ -172,8 +223,8 @@ def test_gemv_70b_endpoints_sampled(index):
     x = mat.activation_bits(1)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
     y = hb.gemv(P, upload(x, mat.dtype)).cpu().numpy()
-    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 8, index), x)
-    assert_close(y[:, rows], yref, s, what=mat.name)
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
+    assert_close(y, yref, s, what=mat.name)
     expect = {"dense": 0, "sparse": tmap.size}.get(mat.name.split("_")[1], tmap.size // 2)
     assert P.layout.n_sparse == expect
 
@@ -182,7 +233,7 @@ def test_gemv_70b_endpoints_sampled(index):
 def test_gemv_grouped_layer(m):
     """One decoder layer's q, k, v and gate, up (same x, own tile maps and
     fractions) in one grouped launch: bitwise equal to separate launches,
-    and within the bound of the oracle on sampled tile rows."""
+    and every output within the bound of the oracle."""
     torch = _torch()
     W = wl.workload(3)
     mats = [mt for mt in W.matrices if mt.name in ("q", "k", "v", "gate", "up")]
@@ -200,8 +251,8 @@ def test_gemv_grouped_layer(m):
     torch.cuda.synchronize()
     for (mt, w, tmap), o, so in zip(refs, outs, sep):
         assert torch.equal(o, so), mt.name
-        rows, yref, sref = oracle_rows(w, tmap, mt, sample_tile_rows(mt, 3, m), x_bits)
-        assert_close(o.cpu().numpy()[:, rows], yref, sref, what=f"grouped {mt.name}")
+        yref, sref = oracle_full(w, tmap, mt.b1, mt.b2, x_bits, mt.dtype)
+        assert_close(o.cpu().numpy(), yref, sref, what=f"grouped {mt.name}")
 
 
 def test_gemv_grouped_mixed_shapes():
@@ -314,12 +365,9 @@ def test_sparse_lowrank_end_to_end():
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
     y = hb.sparse_lowrank_gemv(P, upload(v, "bf16"), upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
     t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
-    tile_rows = sample_tile_rows(mat, 4, 7)
-    rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
-    sub = oracle.prune(w[rows], tmap[tile_rows], mat.b1, mat.b2)
-    yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
-    extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
-    assert_close(y[:, rows], yref, s, extra=extra, what="sparse + low-rank")
+    yref, s = oracle_full_lowrank(w, tmap, mat.b1, mat.b2, x, t_ref, u, "bf16")
+    extra = REL * (s_t @ np.abs(oracle.widen(u, "bf16")).T)
+    assert_close(y, yref, s, extra=extra, what="sparse + low-rank")
 
 
 @pytest.mark.parametrize("m,rank,dtype", [(9, 64, "bf16"), (40, 8, "f16"), (130, 256, "bf16"), (300, 64, "f16")])
@@ -403,12 +451,12 @@ def test_gemm_lowrank_small_m_and_strides():
 
 
 @pytest.mark.parametrize("m", [12, 40, 100, 256])
-def test_sparse_lowrank_prefill_qwen14b_sampled(m):
+def test_sparse_lowrank_prefill_qwen14b(m):
     """17408 x 5120 (64 x 64 tiles, 60% 2:4) + rank 64: the projection on
     the matrix cores (above 16 tokens) and the matrix-core product with the
     T U^T epilogue, through each kernel variant (register-fed with one row
     group at 12 tokens and two at 40, the LDS-fed kernel's 64-token shape at
-    100 and its larger shapes at 256), checked on sampled tile rows; the
+    100 and its larger shapes at 256), every output against the oracle; the
     oracle computes T itself and the bound carries T's own error through
     |U|."""
     torch = _torch()
@@ -422,18 +470,16 @@ def test_sparse_lowrank_prefill_qwen14b_sampled(m):
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
     y = hb.sparse_lowrank_gemm(P, upload(v, "bf16"), upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
     t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
-    tile_rows = sample_tile_rows(mat, 4, 65)
-    rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
-    sub = oracle.prune(w[rows], tmap[tile_rows], mat.b1, mat.b2)
-    yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
-    extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
-    assert_close(y[:, rows], yref, s, extra=extra, what="prefill sparse + low-rank")
+    yref, s = oracle_full_lowrank(w, tmap, mat.b1, mat.b2, x, t_ref, u, "bf16")
+    extra = REL * (s_t @ np.abs(oracle.widen(u, "bf16")).T)
+    assert_close(y, yref, s, extra=extra, what="prefill sparse + low-rank")
 
 
-def test_sparse_lowrank_prefill_tall_sampled():
+def test_sparse_lowrank_prefill_tall():
     """8192 x 28672 (128 x 128 tiles, checkerboard) + rank 32 at 200 tokens:
     the register-fed product above 128 tokens (the shape a short, deep
-    matrix takes there) with its T U^T epilogue, on sampled tile rows."""
+    matrix takes there) with its T U^T epilogue; every output against the
+    oracle."""
     torch = _torch()
     note("sparse + low-rank prefill 70b tall m=200")
     mat, w, tmap = workload_matrix(4, 5)
@@ -445,12 +491,9 @@ def test_sparse_lowrank_prefill_tall_sampled():
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
     y = hb.sparse_lowrank_gemm(P, upload(v, "bf16"), upload(u, "bf16"), upload(x, "bf16")).cpu().numpy()
     t_ref, s_t = oracle.ref_matmul(v, x, "bf16")
-    tile_rows = sample_tile_rows(mat, 2, 200)
-    rows = np.concatenate([np.arange(tr * mat.b1, (tr + 1) * mat.b1) for tr in tile_rows])
-    sub = oracle.prune(w[rows], tmap[tile_rows], mat.b1, mat.b2)
-    yref, s = oracle.ref_lowrank(sub, x, t_ref, u[rows], "bf16")
-    extra = REL * (s_t @ np.abs(oracle.widen(u[rows], "bf16")).T)
-    assert_close(y[:, rows], yref, s, extra=extra, what="tall prefill sparse + low-rank")
+    yref, s = oracle_full_lowrank(w, tmap, mat.b1, mat.b2, x, t_ref, u, "bf16")
+    extra = REL * (s_t @ np.abs(oracle.widen(u, "bf16")).T)
+    assert_close(y, yref, s, extra=extra, what="tall prefill sparse + low-rank")
 
 
 def test_gemm_lowrank_output_16bit():
@@ -505,9 +548,8 @@ def test_gemv_grouped_max_count(m):
     torch.cuda.synchronize()
     for i, ((w, tmap), o, so) in enumerate(zip(refs, outs, sep)):
         assert torch.equal(o, so), i
-        rows = np.arange(min(w.shape[0], 256))
-        yref, sref = oracle.ref_matmul(oracle.prune(w, tmap, 128, 128)[rows], x, "bf16")
-        assert_close(o.cpu().numpy()[:, rows], yref, sref, what=f"grouped matrix {i}")
+        yref, sref = oracle_full(w, tmap, 128, 128, x, "bf16")
+        assert_close(o.cpu().numpy(), yref, sref, what=f"grouped matrix {i}")
 
 
 # ------------------------------------------------------------- GEMM -------
@@ -546,102 +588,113 @@ def test_gemm_lds_shapes_random(n, m, b1, b2, dtype, meta):
     shape), 8192 rows at 2048 (the 256-token shape) and 16384 rows at 256
     (the 64-token shape), in every tile size, dtype and metadata kind of
     test_gemm_random (whose small matrices take the register-fed kernel at
-    every token count); checked on sampled tile rows."""
+    every token count); every output against the oracle."""
     torch = _torch()
     note(f"gemm lds shapes n={n} m={m} {b1}x{b2} {dtype} {meta}")
     k = 2 * b2
     w, tmap = random_case(n + m + b2, n, k, b1, b2, dtype)
     x = wl.float32_to_bits(np.random.default_rng(m + n).standard_normal((m, k)).astype(np.float32), dtype)
     P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    expect_route(P, m, "lds", token_blocks={1024: 8, 2048: 16, 256: 4}[m])
     y = hb.gemm(P, upload(x, dtype)).cpu().numpy()
-    random_rows_check(w, tmap, b1, b2, x, y, dtype, seed=n + m)
+    yref, s = oracle_full(w, tmap, b1, b2, x, dtype)
+    assert_close(y, yref, s, what=f"gemm lds n={n} m={m}")
 
 
-@pytest.mark.parametrize("config,index,m", [(3, 1, 384), (3, 0, 160), (3, 6, 256)])
-def test_gemm_small_matrices_above_128_sampled(config, index, m):
+@pytest.mark.parametrize("config,index,m,route", [(3, 1, 384, (2, 8, 1)), (3, 0, 160, (4, 8, 1)),
+                                                  (3, 6, 256, (4, 8, 1))])
+def test_gemm_small_matrices_above_128(config, index, m, route):
     """Few 256-row blocks above 128 tokens: the launcher prices every
     register-fed shape against the LDS shapes and, on a 256-CU device, runs
     32 tokens x 64 rows on eight wavefronts for the 1024 x 4096 k projection
     at 384 tokens, and 64 tokens x 64 rows on eight wavefronts for the
-    4096-row q (160 tokens, ragged) and down (256 tokens) projections."""
+    4096-row q (160 tokens, ragged) and down (256 tokens) projections.
+    Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(config, index)
     note(f"gemm small matrix {mat.name} m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
+    expect_route(P, m, "register", *route)
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
-    assert_close(y[:, rows], yref, s, what=f"gemm {mat.name} m={m}")
+    assert_close(y, yref, s, what=f"gemm {mat.name} m={m}")
 
 
 @pytest.mark.parametrize("m", [8, 16, 64, 256, 2048])
-def test_gemm_qwen14b_sampled(m):
-    """17408x5120, 64x64 tiles, 60% sparse tiles; M from 16 to 2048 through
-    hyb_gemm and through the matrix-core entry point for every M."""
+def test_gemm_qwen14b_full(m):
+    """17408x5120, 64x64 tiles, 60% sparse tiles; M from 8 to 2048 through
+    hyb_gemm and through the matrix-core entry point, every output against
+    the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(5, 0)
     note(f"gemm qwen14b m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
     xt = upload(x, mat.dtype)
-    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 6, m), x)
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, xt).cpu().numpy()
-    assert_close(y[:, rows], yref, s, what=f"gemm m={m}")
+    assert_close(y, yref, s, what=f"gemm m={m}")
     y2 = hb.gemm_mfma(P, xt).cpu().numpy()
-    assert_close(y2[:, rows], yref, s, what=f"gemm_mfma m={m}")
+    assert_close(y2, yref, s, what=f"gemm_mfma m={m}")
 
 
-@pytest.mark.parametrize("m", [200, 256, 300, 512, 700, 1024])
-def test_gemm_8b_up_shapes_sampled(m):
+@pytest.mark.parametrize("m,tb", [(200, 4), (256, 4), (300, 8), (512, 8), (700, 12), (1024, 16)])
+def test_gemm_8b_up_shapes(m, tb):
     """14336x4096, 128x128 tiles, 70% sparse tiles.  From 129 tokens the
     launcher picks one of four workgroup shapes (256, 192, 128 or 64 tokens
     per workgroup) by the number of workgroup rounds on the device; on a
     256-CU device these token counts select the 64-token shape (200 with a
     ragged last block, 256), the 128-token shape (300 ragged, 512), the
     192-token shape (700 ragged) and the 256-token shape (1024).  The
-    17408-row matrix at 2048 tokens (test_gemm_qwen14b_sampled) also runs
-    the 192-token shape."""
+    17408-row matrix at 2048 tokens (test_gemm_qwen14b_full) also runs
+    the 192-token shape.  Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(2, 0)
     note(f"gemm 8b up m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 4, m), x)
+    expect_route(P, m, "lds", token_blocks=tb)
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
-    assert_close(y[:, rows], yref, s, what=f"gemm m={m}")
+    assert_close(y, yref, s, what=f"gemm m={m}")
 
 
-@pytest.mark.parametrize("m", [160, 256, 512])
-def test_gemm_tall_70b_sampled(m):
+@pytest.mark.parametrize("m,route", [(160, ("register", 4, 4, 2)), (256, ("register", 4, 4, 2)),
+                                     (512, ("lds", 4, 8, 4))])
+def test_gemm_tall_70b(m, route):
     """8192x28672 (32 blocks of 256 rows), 128x128 tiles in a checkerboard:
     at 160 and 256 tokens every LDS shape leaves most CUs of a 256-CU device
     idle and the launcher runs the register-fed shape (128 rows by 64 tokens,
     K split over four wavefronts; 160 with a ragged last block); at 512 it
-    runs the 64-token LDS shape."""
+    runs the 64-token LDS shape.  Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 5)
     note(f"gemm 70b tall m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
+    expect_route(P, m, *route)
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
-    assert_close(y[:, rows], yref, s, what=f"gemm tall m={m}")
+    assert_close(y, yref, s, what=f"gemm tall m={m}")
 
 
 @pytest.mark.parametrize("m", [80, 128])
-def test_gemm_wide_70b_sampled(m):
+def test_gemm_wide_70b(m):
     """28672x8192 (128x128 tiles, checkerboard) at 80 and 128 tokens: the
     register-fed pick would need two rounds of 128-row x 64-token workgroups
     on a 256-CU device, so the launcher runs the 64-token LDS shape, whose
-    224 workgroups fit in one (80: ragged last token block)."""
+    224 workgroups fit in one (80: ragged last token block).  Every output
+    against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 2)
     note(f"gemm 70b wide m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    rows, yref, s = oracle_rows(w, tmap, mat, sample_tile_rows(mat, 3, m), x)
+    expect_route(P, m, "lds", 4, 8, 4)
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
-    assert_close(y[:, rows], yref, s, what=f"gemm wide m={m}")
+    assert_close(y, yref, s, what=f"gemm wide m={m}")
 
 
 @pytest.mark.parametrize("m", [20, 64])
@@ -912,3 +965,66 @@ def test_stream_read_reads_every_byte_once():
         hb.stream_read(buf, words.nbytes, sink, grid)
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(words)
+
+
+# ------------------------------------------- slot order and save / load ----
+
+def _permuted(P, seed):
+    """The same packed weight with its dense slots and its sparse slots in a
+    random order: each slot's bytes move to the new position and tidx names
+    the new slot."""
+    torch = _torch()
+    L = P.layout
+    rng = np.random.default_rng(seed)
+    pd = rng.permutation(L.n_dense)
+    ps = rng.permutation(L.n_sparse)
+    tile = L.b1 * L.b2
+    def move(buf, count, per, perm):
+        if count == 0:
+            return buf.clone()
+        src = buf.view(count, per)
+        out = torch.empty_like(src)
+        out[torch.from_numpy(perm).to(buf.device)] = src
+        return out.view(-1)
+    dense = move(P.dense, L.n_dense, tile * 2, pd)
+    val = move(P.val, L.n_sparse, tile, ps)
+    meta = move(P.meta, L.n_sparse, tile // 8, ps)
+    t = P.tidx.cpu().numpy()
+    t2 = np.where(t >= 0, pd[np.maximum(t, 0)] if L.n_dense else t,
+                  ~(ps[np.maximum(~t, 0)] if L.n_sparse else ~t)).astype(np.int32)
+    return hb.PackedWeight(L, dense, val, meta, torch.from_numpy(t2).to(P.device), P.dtype, P.meta_kind)
+
+
+@pytest.mark.parametrize("meta", ["idx2", "mask8"])
+def test_slot_order_does_not_change_results(meta):
+    """Slots are names only: with the dense and sparse slots permuted (bytes
+    moved, tidx renamed) unpack and every product kernel -- the decode
+    kernel, the register-fed and the LDS-fed matrix-core kernels -- give
+    bitwise the same results."""
+    torch = _torch()
+    note(f"slot order {meta}")
+    n, k, b1, b2 = 8192, 512, 128, 128
+    w, tmap = random_case(91, n, k, b1, b2, "bf16", frac=0.6)
+    P = pack_gpu(w, tmap, b1, b2, "bf16", meta)
+    Q = _permuted(P, 5)
+    assert torch.equal(hb.unpack(P), hb.unpack(Q))
+    for m in (1, 5, 16, 40, 300, 1024):
+        x = upload(wl.float32_to_bits(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32),
+                                      "bf16"), "bf16")
+        assert torch.equal(hb.gemm(P, x), hb.gemm(Q, x)), m
+    torch.cuda.synchronize()
+
+
+def test_save_load_gpu_round_trip(tmp_path):
+    """A packed weight saved from the GPU and loaded back gives bitwise the
+    same decode and prefill products."""
+    torch = _torch()
+    note("save / load round trip")
+    mat, w, tmap = workload_matrix(1, 0)
+    P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    path = tmp_path / "w.hyb"
+    hb.save(P, path)
+    Q = hb.load(path, dev())
+    for m in (1, 64):
+        x = upload(mat.activation_bits(m), mat.dtype)
+        assert torch.equal(hb.gemm(P, x), hb.gemm(Q, x)), m

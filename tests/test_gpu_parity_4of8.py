@@ -13,7 +13,7 @@ import pytest
 import oracle
 from matmul_pack_b1_amd import binding as hb
 from matmul_pack_b1_amd import workloads as wl
-from tests.test_gpu_parity import (_torch, assert_close, note, pack_gpu, random_case, sample_tile_rows, streams,
+from tests.test_gpu_parity import (_torch, assert_close, note, oracle_full, pack_gpu, random_case, sample_tile_rows, streams,
                                    upload, workload_matrix)
 
 pytestmark = pytest.mark.gpu
@@ -100,7 +100,7 @@ def test_gemm_4of8_lds_shapes_random(n, m, b1, b2, dtype):
     """The LDS-fed shapes (128-, 256- and 64-token workgroups on a 256-CU
     device) on 4:8 tiles in each tile size and dtype; the small matrices of
     test_gemm_4of8_random take the register-fed kernel at every token
-    count.  Checked on sampled tile rows."""
+    count.  Every output against the oracle."""
     torch = _torch()
     note(f"gemm 4:8 lds shapes n={n} m={m} {b1}x{b2} {dtype}")
     k = 2 * b2
@@ -108,26 +108,22 @@ def test_gemm_4of8_lds_shapes_random(n, m, b1, b2, dtype):
     x = wl.float32_to_bits(np.random.default_rng(m + n + 8).standard_normal((m, k)).astype(np.float32), dtype)
     P = pack_gpu(w, tmap, b1, b2, dtype, META)
     y = hb.gemm(P, upload(x, dtype)).cpu().numpy()
-    tile_rows = np.sort(np.random.default_rng(n + m).choice(n // b1, size=3, replace=False))
-    rows = np.concatenate([np.arange(t * b1, (t + 1) * b1) for t in tile_rows])
-    yref, s = oracle.ref_matmul(_prune(w[rows], tmap[tile_rows], b1, b2), x, dtype)
-    assert_close(y[:, rows], yref, s, what=f"4:8 lds shapes n={n} m={m}")
+    yref, s = oracle_full(w, tmap, b1, b2, x, dtype, meta=META)
+    assert_close(y, yref, s, what=f"4:8 lds shapes n={n} m={m}")
 
 
 @pytest.mark.parametrize("m", [4, 12, 30, 64, 100, 256, 2048])
-def test_gemm_4of8_qwen14b_sampled(m):
+def test_gemm_4of8_qwen14b(m):
     """17408 x 5120, 64 x 64 tiles, 60% of them 4:8: full-size launches
-    (272 row groups of 64, more than the compute units) checked on 6
-    sampled tile rows."""
+    (272 row groups of 64, more than the compute units), every output
+    against the oracle."""
     mat, w, tmap = workload_matrix(5, 0)
     note(f"gemm 4:8 qwen14b m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, META)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
-    tile_rows = sample_tile_rows(mat, 6, m)
-    rows = np.concatenate([np.arange(t * mat.b1, (t + 1) * mat.b1) for t in tile_rows])
-    yref, s = oracle.ref_matmul(_prune(w[rows], tmap[tile_rows], mat.b1, mat.b2), x, mat.dtype)
-    assert_close(y[:, rows], yref, s, what=f"qwen14b 4:8 m={m}")
+    yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype, meta=META)
+    assert_close(y, yref, s, what=f"qwen14b 4:8 m={m}")
 
 
 @pytest.mark.parametrize("kernel", ["gemv", "gemm_mfma"])

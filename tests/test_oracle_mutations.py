@@ -225,3 +225,70 @@ def test_4of8_per_half_rule_caught_by_magnitude_pin(monkeypatch):
     monkeypatch.setattr(oracle, "kept_positions_nm", _kept_nm_per_half)
     with pytest.raises(FAIL):
         pins.test_4of8_keeps_at_least_the_2of4_magnitude()
+
+
+
+# ------------------------------------------------ value and acceptance pins -
+
+def _widen_swapped(bits, dtype):
+    other = {"f16": "bf16", "bf16": "f16"}.get(dtype, dtype)
+    b = np.asarray(bits, dtype=np.uint16)
+    if other == "f16":
+        return b.view(np.float16).astype(np.float64)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _widen_f16_flush(bits, dtype):
+    """fp16 subnormals flushed to zero (a plausible decoder shortcut)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    v = _widen_swapped(b, "bf16" if dtype == "f16" else "f16")
+    if dtype == "f16":
+        v = np.where((b & 0x7C00) == 0, np.copysign(0.0, v), v)
+    return v
+
+
+@pytest.mark.parametrize("func", [_widen_swapped, _widen_f16_flush])
+def test_widen_mutations_caught(monkeypatch, golden_dir, func):
+    monkeypatch.setattr(ho, "widen", func)
+    monkeypatch.setattr(oracle, "widen", func)
+    with pytest.raises(FAIL):
+        pins.test_widen_golden(golden_dir, "f16", "f16_values.txt")
+
+
+def test_widen_swap_caught_by_f16_product(monkeypatch):
+    monkeypatch.setattr(ho, "widen", _widen_swapped)
+    monkeypatch.setattr(oracle, "widen", _widen_swapped)
+    with pytest.raises(FAIL):
+        pins.test_ref_matmul_integers_exact_f16()
+
+
+def _within_strict(y, y_ref, s, rel=2e-3, extra=0.0):
+    return np.abs(np.asarray(y, dtype=np.float64) - y_ref) < rel * s + extra
+
+
+def _within_rel_ignored(y, y_ref, s, rel=2e-3, extra=0.0):
+    return np.abs(np.asarray(y, dtype=np.float64) - y_ref) <= 2e-3 * s + extra
+
+
+@pytest.mark.parametrize("func", [_within_strict, _within_rel_ignored])
+def test_within_bound_mutations_caught(monkeypatch, func):
+    monkeypatch.setattr(ho, "within_bound", func)
+    monkeypatch.setattr(oracle, "within_bound", func)
+    with pytest.raises(FAIL):
+        pins.test_within_bound_cases()
+
+
+def _ref_rows_all(wp_bits, x_bits, dtype, rows):
+    return ho.ref_matmul(wp_bits, x_bits, dtype)
+
+
+def _ref_rows_sorted(wp_bits, x_bits, dtype, rows):
+    return ho.ref_matmul(np.asarray(wp_bits)[np.sort(np.asarray(rows))], x_bits, dtype)
+
+
+@pytest.mark.parametrize("func", [_ref_rows_all, _ref_rows_sorted])
+def test_ref_rows_mutations_caught(monkeypatch, func):
+    monkeypatch.setattr(ho, "ref_rows", func)
+    monkeypatch.setattr(oracle, "ref_rows", func)
+    with pytest.raises(FAIL):
+        pins.test_ref_rows_selects_rows()

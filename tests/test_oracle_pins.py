@@ -8,6 +8,7 @@ six patterns; SparseDecoding abstract: fixed stride, bitmask metadata)."""
 import itertools
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -519,3 +520,112 @@ def test_ref_lowrank_loops_and_special_cases():
         for j in range(n):
             assert math.isclose(yz[i, j], math.fsum(float(t[i, q]) * uv[j, q] for q in range(r)),
                                 rel_tol=0, abs_tol=1e-12)
+
+
+# --------------------------------------------------------- 16-bit values ----
+
+def load_value_table(golden_dir, name):
+    """(bits, value) rows of a hand-derived value table; value is a Fraction,
+    or one of the strings "-0", "inf", "-inf", "nan"."""
+    rows = []
+    with open(os.path.join(golden_dir, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            h, v = line.split()
+            if v in ("-0", "inf", "-inf", "nan"):
+                val = v
+            elif "*2^" in v:
+                mant, exp = v.split("*2^")
+                val = Fraction(int(mant)) * (Fraction(2) ** int(exp))
+            else:
+                val = Fraction(v)
+            rows.append((int(h, 16), val))
+    return rows
+
+
+@pytest.mark.parametrize("dtype,name", [("f16", "f16_values.txt"), ("bf16", "bf16_values.txt")])
+def test_widen_golden(golden_dir, dtype, name):
+    """Every widening equals the value the format's definition gives by hand
+    (exactly: float64 holds every fp16 and bf16 value)."""
+    rows = load_value_table(golden_dir, name)
+    assert len(rows) >= 20
+    got = oracle.widen(np.array([b for b, _ in rows], dtype=np.uint16), dtype)
+    for (bits, want), v in zip(rows, got):
+        v = float(v)
+        if want == "nan":
+            assert math.isnan(v), hex(bits)
+        elif want in ("inf", "-inf"):
+            assert v == float(want), hex(bits)
+        elif want == "-0":
+            assert v == 0.0 and math.copysign(1.0, v) < 0, hex(bits)
+        else:
+            assert Fraction(v) == want, (hex(bits), v, want)
+            if want == 0:
+                assert math.copysign(1.0, v) > 0, hex(bits)
+
+
+# fp16 bit patterns of the integers -3..3 (binary16 definition: 1 = 0x3C00,
+# 2 = 0x4000, 3 = 0x4200 with exponent 16 and fraction 512, sign bit 0x8000).
+F16_INT_BITS = {-3: 0xC200, -2: 0xC000, -1: 0xBC00, 0: 0x0000, 1: 0x3C00, 2: 0x4000, 3: 0x4200}
+
+
+def test_ref_matmul_integers_exact_f16():
+    """fp16 weights and activations holding small integers (bit patterns
+    from the binary16 definition, not from the oracle): the product is an
+    exact integer that Python computes from the integers themselves."""
+    rng = np.random.default_rng(18)
+    n, k, m = 32, 128, 3
+    wi = rng.integers(-3, 4, size=(n, k))
+    xi = rng.integers(-3, 4, size=(m, k))
+    to_bits = np.vectorize(lambda v: F16_INT_BITS[int(v)])
+    w = to_bits(wi).astype(np.uint16)
+    x = to_bits(xi).astype(np.uint16)
+    tmap = np.array([[1, 0], [0, 1]], dtype=np.uint8)
+    wp = oracle.prune(w, tmap, 16, 64)
+    from_bits = {b: v for v, b in F16_INT_BITS.items()}
+    from_bits[0x8000] = 0
+    wpi = np.vectorize(lambda b: from_bits[int(b)])(wp)
+    y, s = oracle.ref_matmul(wp, x, "f16")
+    exact = np.array([[sum(int(a) * int(b) for a, b in zip(wpi[j], xi[i])) for j in range(n)]
+                      for i in range(m)], dtype=np.float64)
+    absx = np.array([[sum(abs(int(a) * int(b)) for a, b in zip(wpi[j], xi[i])) for j in range(n)]
+                     for i in range(m)], dtype=np.float64)
+    np.testing.assert_array_equal(y, exact)
+    np.testing.assert_array_equal(s, absx)
+
+
+# ------------------------------------------------------ acceptance rule -----
+
+def test_within_bound_cases():
+    """|y - y_ref| <= 2e-3 * s (+ extra), the bound of the product checks,
+    on hand cases: on the bound passes, just past it fails, s = 0 demands
+    equality, and `extra` widens the bound by exactly that much."""
+    s = np.array([1000.0, 1000.0, 0.0, 0.0, 500.0])
+    y_ref = np.array([10.0, 10.0, 3.0, 3.0, -1.0])
+    y = np.array([12.0, 12.0 + 1e-9, 3.0, 3.0 + 1e-12, 0.0])
+    assert oracle.within_bound(y, y_ref, s).tolist() == [True, False, True, False, True]
+    assert oracle.within_bound(np.array([12.5]), np.array([10.0]), np.array([1000.0])).tolist() == [False]
+    assert oracle.within_bound(np.array([12.5]), np.array([10.0]), np.array([1000.0]), extra=0.5).tolist() == [True]
+    # a caller's own relative bound replaces 2e-3 (binary-exact numbers)
+    assert oracle.within_bound(np.array([10.5]), np.array([10.0]), np.array([2.0]), rel=0.25).tolist() == [True]
+    assert oracle.within_bound(np.array([10.5]), np.array([10.0]), np.array([2.0])).tolist() == [False]
+
+
+def test_ref_rows_selects_rows():
+    """Row n of W holds (n % 8) + 1 in column 0 and zeros elsewhere, x = e_0:
+    the restricted product returns exactly those integers for the rows asked,
+    in the order asked."""
+    n, k = 24, 64
+    w = np.zeros((n, k), np.uint16)
+    vals = {1: 0x3F80, 2: 0x4000, 3: 0x4040, 4: 0x4080, 5: 0x40A0, 6: 0x40C0, 7: 0x40E0, 8: 0x4100}
+    for r in range(n):
+        w[r, 0] = vals[(r % 8) + 1]
+    x = np.zeros((1, k), np.uint16)
+    x[0, 0] = 0x3F80
+    rows = [13, 0, 7, 22, 5]
+    y, s = oracle.ref_rows(w, x, "bf16", rows)
+    assert y.shape == (1, len(rows))
+    assert y[0].tolist() == [float((r % 8) + 1) for r in rows]
+    assert s[0].tolist() == y[0].tolist()
