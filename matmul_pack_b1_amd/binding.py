@@ -14,7 +14,9 @@ from dataclasses import dataclass
 import numpy as np
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libhyb.so")
+# The in-tree library; HYB_LIB names another build of the same ABI (the
+# sanitizer test's host-only build).
+LIB_PATH = os.environ.get("HYB_LIB") or os.path.join(PKG_DIR, "libhyb.so")
 
 HYB_OK = 0
 HYB_F16, HYB_BF16, HYB_F32 = 1, 2, 3

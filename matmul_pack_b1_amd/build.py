@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libhyb.so")
-SOURCES = ["hyb_api.cpp", "hyb_pack.hip", "hyb_gemv.hip", "hyb_gemm.hip", "hyb_lowrank.hip"]
+SOURCES = ["hyb_api.cpp", "hyb_route.cpp", "hyb_pack.hip", "hyb_gemv.hip", "hyb_gemm.hip", "hyb_lowrank.hip"]
 ARCH = os.environ.get("HYB_ARCH", "gfx950")
 
 

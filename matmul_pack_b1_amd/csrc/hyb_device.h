@@ -26,9 +26,6 @@
 // Tuning knobs of the decode kernel (defaults chosen by measurement):
 // wavefronts per workgroup splitting a slab's tile columns, tiles kept in
 // flight per wavefront, and the cache-policy bits of the weight loads.
-#ifndef HYB_GEMV_WAVES
-#define HYB_GEMV_WAVES 4
-#endif
 #ifndef HYB_GEMV_STAGES
 #define HYB_GEMV_STAGES 2
 #endif
@@ -40,12 +37,6 @@
 #endif
 #ifndef HYB_GEMM_GROUP_N
 #define HYB_GEMM_GROUP_N 4
-#endif
-#ifndef HYB_GEMM_C192
-#define HYB_GEMM_C192 0.8
-#endif
-#ifndef HYB_GEMM_C_RX
-#define HYB_GEMM_C_RX 0.29
 #endif
 #ifndef HYB_W_AUX
 #define HYB_W_AUX 2  // non-temporal: the weights are read once per product
@@ -304,7 +295,6 @@ struct GemvPtrs {
   void* y;
 };
 
-constexpr int kGemvWaves = HYB_GEMV_WAVES;
 constexpr int kGemvStages = HYB_GEMV_STAGES;
 
 }  // namespace

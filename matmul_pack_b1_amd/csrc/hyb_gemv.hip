@@ -378,16 +378,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_grouped(const uint16_t* __r
 
 }  // namespace
 
-// Wavefronts per slab of the decode kernels.  Four when the slabs fill the
-// CUs at least twice (each wavefront walks a quarter of the tile row); a
-// shorter matrix has too few workgroups to keep enough loads in flight, so
-// its tile row is split eight ways (up to 4 tokens) or sixteen (more
-// tokens).  Measured on 1024 and 4096 rows: 1.2x at 1 token, 1.2-1.3x at 4,
-// 1.8-1.9x at 16; on 14336 rows four stay best.
-int gemv_waves(int64_t slabs, int m) {
-  if (slabs >= 2 * int64_t(device_cus())) return kGemvWaves;
-  return m <= 4 ? 8 : 16;
-}
 
 namespace {
 
@@ -488,13 +478,6 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
   return launch_gemv_impl<false>(L, P, x, m, ldx, y, y_dtype, ldy, nullptr, 0, nullptr, 0, 0, s);
 }
 
-bool gemv_preferred(const hyb_layout& L, int m) {
-  if (m <= kGemvCrossoverM) return true;
-  // 9-16 tokens on a matrix short enough for 16 wavefronts per slab: the
-  // decode kernel beats the register-fed product there (1024 and 4096 rows
-  // at 16 tokens: 11-12 us against 15-16 us)
-  return m <= kMaxGemvM && gemv_waves(L.n / 16, m) == 16;
-}
 
 hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
                                const float* t, int64_t ldt, const void* u, int64_t ldu, int rank, void* y,

@@ -9,6 +9,12 @@
 
 namespace hyb {
 
+// Wavefronts per 16-row slab of the decode kernel on matrices with at least
+// two slabs per compute unit (chosen by measurement; see gemv_waves).
+#ifndef HYB_GEMV_WAVES
+#define HYB_GEMV_WAVES 4
+#endif
+constexpr int kGemvWaves = HYB_GEMV_WAVES;
 // Decode kernel handles up to this many tokens per launch.
 constexpr int kMaxGemvM = 16;
 // hyb_gemm runs the decode kernel up to this many tokens and the
