@@ -536,8 +536,10 @@ def kernel_text(hb, layout, m):
     sh = hb.gemm_shape(layout, m)
     if sh["kernel"] == "decode":
         return f"k_gemv ({sh['waves']} wavefronts per 16-row slab)"
-    name = "k_gemm_rx" if sh["kernel"] == "register" else "k_gemm_lds"
-    split = ", wavefronts splitting K" if sh["kernel"] == "register" else ""
+    name = {"register": "k_gemm_rx", "split": "k_gemm_split + k_gemm_split_sum", "lds": "k_gemm_lds"}[sh["kernel"]]
+    split = {"register": ", wavefronts splitting K",
+             "split": ", wavefronts splitting K, K also split across one workgroup per CU",
+             "lds": ""}[sh["kernel"]]
     return (f"{name} ({64 * sh['row_groups']}-row x {16 * sh['token_blocks']}-token workgroups on "
             f"{sh['waves']} wavefronts{split})")
 

@@ -68,6 +68,7 @@
 #ifndef HYB_H_
 #define HYB_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -259,10 +260,32 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same
  * arguments as hyb_gemv; m <= 8 runs the decode kernel (also m <= 16 when
  * the matrix has fewer than two 16-row slabs per compute unit), larger m
- * the matrix-core kernels. */
+ * the matrix-core kernels.  Where those split K over workgroups
+ * (HYB_KERNEL_SPLIT of hyb_gemm_shape) they keep partial sums in a
+ * workspace that the library allocates (hipMalloc, 16 MiB) at the first
+ * such launch on a (device, stream) pair and holds until the process ends;
+ * launches on one stream share it, so concurrent calls on different
+ * streams stay safe.  Nothing is allocated on a stream that is being
+ * captured into a graph: there (and if the allocation fails) the product
+ * runs unsplit unless the stream already holds its workspace; hyb_gemm_ws
+ * takes a caller-held one. */
 hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x,
                     int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                     void* stream);
+
+/* hyb_gemm with a caller-held workspace instead of the library's (for code
+ * under graph capture, or callers that manage device memory themselves).
+ * hyb_gemm_workspace_size gives the bytes the product needs on the current
+ * device (0 when its route does not split K; m >= 0).  `workspace`: device
+ * memory, 16-byte aligned, no initial contents needed, not read after the
+ * call's work on `stream` completes; launches that overlap on one buffer
+ * race.  workspace_bytes = 0 (workspace may be NULL) runs the same shape
+ * unsplit; a positive size below the need -> HYB_ERR_INVALID_ARG.  Other
+ * arguments and errors as hyb_gemm. */
+hyb_status hyb_gemm_workspace_size(const hyb_layout* layout, int32_t m, size_t* bytes);
+hyb_status hyb_gemm_ws(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                       int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Matrix-core kernel only, any m >= 0 (no switch to the decode kernel);
  * exposed so that the crossover can be measured.  Same arguments. */
@@ -274,14 +297,18 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
  * workgroup shape that hyb_gemm would launch for `m` >= 1 tokens on
  * `layout`'s matrix on the current device (its compute-unit count; 256, the
  * MI355X's, when no device is visible).  hyb_gemm_mfma launches the same for
- * m > 16, and for m <= 16 the register-fed shape of out[0] = 2.  Writes
+ * m > 16, and for m <= 16 the register-fed shape of out[0] = 2 or 4.  Writes
  * out[4] = {kernel, token blocks of 16 per workgroup, wavefronts per
  * workgroup, 64-row groups per workgroup}: kernel HYB_KERNEL_DECODE (k_gemv;
  * out[1] = out[3] = 0, out[2] its wavefronts per 16-row slab),
- * HYB_KERNEL_REGISTER (k_gemm_rx, wavefronts splitting K) or HYB_KERNEL_LDS
- * (k_gemm_lds, 4 row groups).  Errors: as the layout checks of hyb_gemm;
- * out NULL -> HYB_ERR_INVALID_ARG; m < 1 -> HYB_ERR_SHAPE. */
-enum { HYB_KERNEL_DECODE = 1, HYB_KERNEL_REGISTER = 2, HYB_KERNEL_LDS = 3 };
+ * HYB_KERNEL_REGISTER (k_gemm_rx, wavefronts splitting K), HYB_KERNEL_LDS
+ * (k_gemm_lds, 4 row groups) or HYB_KERNEL_SPLIT (k_gemm_split: the
+ * register-fed shape with the (tile, K step) units dealt out evenly over a
+ * fixed number of workgroups, partial tiles added by a second kernel in a
+ * fixed order; it needs a workspace, which hyb_gemm holds per device and
+ * stream).  Errors: as the layout checks of hyb_gemm; out NULL ->
+ * HYB_ERR_INVALID_ARG; m < 1 -> HYB_ERR_SHAPE. */
+enum { HYB_KERNEL_DECODE = 1, HYB_KERNEL_REGISTER = 2, HYB_KERNEL_LDS = 3, HYB_KERNEL_SPLIT = 4 };
 hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out);
 
 /* Measurement aid (no part of the product computation): reads `bytes`

@@ -29,9 +29,10 @@ META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_layout_check", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
-            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_shape", "hyb_stream_read",
+            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_ws", "hyb_gemm_workspace_size", "hyb_gemm_shape",
+            "hyb_stream_read",
             "hyb_status_str", "hyb_last_error", "hyb_abi_version")
-KERNEL_NAMES = {1: "decode", 2: "register", 3: "lds"}   # HYB_KERNEL_* of hyb_gemm_shape
+KERNEL_NAMES = {1: "decode", 2: "register", 3: "lds", 4: "split"}   # HYB_KERNEL_* of hyb_gemm_shape
 MAX_GROUP = 16
 MAX_RANK = 256
 
@@ -87,6 +88,11 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I32, I64, P]
         f.restype = I32
+    L.hyb_gemm_ws.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I32, I64, P,
+                              ctypes.c_size_t, P]
+    L.hyb_gemm_ws.restype = I32
+    L.hyb_gemm_workspace_size.argtypes = [ctypes.POINTER(HybLayout), I32, ctypes.POINTER(ctypes.c_size_t)]
+    L.hyb_gemm_workspace_size.restype = I32
     L.hyb_gemv_grouped.argtypes = [I32, ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64,
                                    ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I64), P]
     L.hyb_gemv_grouped.restype = I32
@@ -353,7 +359,7 @@ def _out_code(P: PackedWeight, out_dtype) -> int:
     raise TypeError(f"output dtype {out_dtype} must be float32 or the weight dtype")
 
 
-def _product(fn_name: str, P: PackedWeight, x, out_dtype=None, out=None):
+def _product(fn_name: str, P: PackedWeight, x, out_dtype=None, out=None, workspace=None):
     torch = _torch()
     _check_x(P, x)
     m = x.shape[0]
@@ -369,9 +375,23 @@ def _product(fn_name: str, P: PackedWeight, x, out_dtype=None, out=None):
     _check_gpu(out, "out", x.device)
     _check_same_device(P, x.device)
     fn = getattr(lib(), fn_name)
-    st = fn(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
+    args = [ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
             int(x.stride(0)) if x.numel() else int(k), _ptr(out), code,
-            int(out.stride(0)) if out.numel() else int(n), _stream(x.device))
+            int(out.stride(0)) if out.numel() else int(n)]
+    if fn_name == "hyb_gemm_ws":
+        # split-K workspace from torch's allocator on the current stream (so
+        # that graph capture takes it from the graph's pool); kept alive by
+        # the stream order of the allocator until the launches complete
+        if workspace is None:
+            need = workspace_bytes(P, m)
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+        if workspace is not None:
+            _check_gpu(workspace, "workspace", x.device)
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
+        args += [_ptr(workspace) if workspace is not None else None,
+                 workspace.numel() * workspace.element_size() if workspace is not None else 0]
+    st = fn(*args, _stream(x.device))
     check(st, fn_name)
     return out
 
@@ -507,9 +527,20 @@ def sparse_lowrank_gemm(P: PackedWeight, v, u, x, out_dtype=None, out=None, t=No
     return gemm_lowrank(P, x, t, u, out_dtype, out)
 
 
-def gemm(P: PackedWeight, x, out_dtype=None, out=None):
-    """Y = X W'^T for any number of tokens (decode kernel up to 8, matrix cores above)."""
-    return _product("hyb_gemm", P, x, out_dtype, out)
+def gemm(P: PackedWeight, x, out_dtype=None, out=None, workspace=None):
+    """Y = X W'^T for any number of tokens (decode kernel up to 8, matrix cores
+    above), through hyb_gemm_ws: a product whose route splits K gets its
+    workspace from torch's allocator unless `workspace` (a contiguous device
+    tensor of at least workspace_bytes(P, m) bytes) is given."""
+    return _product("hyb_gemm_ws", P, x, out_dtype, out, workspace)
+
+
+def workspace_bytes(P: PackedWeight, m: int) -> int:
+    """Workspace bytes of hyb_gemm_ws for m tokens on the current device."""
+    nbytes = ctypes.c_size_t(0)
+    check(lib().hyb_gemm_workspace_size(ctypes.byref(P.layout), int(m), ctypes.byref(nbytes)),
+          "hyb_gemm_workspace_size")
+    return int(nbytes.value)
 
 
 def gemm_mfma(P: PackedWeight, x, out_dtype=None, out=None):

@@ -4,7 +4,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "hyb_internal.h"
 
@@ -139,6 +142,37 @@ hyb_status check_mfma_limits(int32_t m, int64_t ldx) {
 hyb_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(HYB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Workspace of the split-K launches of hyb_gemm and hyb_gemm_lowrank, held
+// by the library: one buffer of kSplitMaxBytes per (device, stream),
+// allocated at the first split launch there and kept until the process
+// ends.  Work on one stream runs in order, so its launches can share the
+// buffer; launches on different streams get different buffers.  Nothing is
+// allocated while the stream is being captured into a graph (HIP refuses
+// that): such a launch runs unsplit unless the stream already holds a
+// buffer.  Returns {nullptr, 0} when the product does not split or no
+// buffer is available (the product then runs unsplit, on the same kernel).
+std::pair<void*, size_t> stream_workspace(const hyb_layout& L, int m, void* stream) {
+  if (hyb::gemm_route(L, m, hyb::device_cus()).kernel != hyb::kRouteSplit) return {nullptr, 0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return {nullptr, 0};
+  static std::mutex mu;
+  static std::map<std::pair<int, void*>, void*> held;
+  std::lock_guard<std::mutex> lock(mu);
+  void*& p = held[{dev, stream}];
+  if (!p) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess ||
+        cap != hipStreamCaptureStatusNone)
+      return {nullptr, 0};
+    if (hipMalloc(&p, hyb::kSplitMaxBytes) != hipSuccess) {
+      p = nullptr;
+      (void)hipGetLastError();
+      return {nullptr, 0};
+    }
+  }
+  return {p, hyb::kSplitMaxBytes};
 }
 
 }  // namespace
@@ -413,8 +447,9 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
   if (layout->n == 0) return ok();
   if ((st = check_lowrank(t, ldt, u, ldu, rank)) != HYB_OK) return st;
   if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
-  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream), t,
-                                     ldt, u, ldu, rank),
+  const std::pair<void*, size_t> ws = stream_workspace(*layout, m, stream);
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream),
+                                     ws.first, ws.second, t, ldt, u, ldu, rank),
                     "low-rank gemm launch");
 }
 
@@ -424,8 +459,9 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
   if (st != HYB_OK) return st;
   if (m == 0 || layout->n == 0) return ok();
   if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
-  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy,
-                                     static_cast<hipStream_t>(stream)),
+  const std::pair<void*, size_t> ws = stream_workspace(*layout, m, stream);
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream),
+                                     ws.first, ws.second),
                     "gemm launch");
 }
 
@@ -434,6 +470,39 @@ hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x
   if (m >= 0 && m <= hyb::kMaxGemvM && decode_route(layout, m))
     return gemv_decode(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+}
+
+hyb_status hyb_gemm_workspace_size(const hyb_layout* layout, int32_t m, size_t* bytes) {
+  hyb_status st = check_layout(layout, true);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARG, "bytes is NULL");
+  if (m < 0) return fail(HYB_ERR_SHAPE, "m = %d is negative", m);
+  *bytes = 0;
+  if (m == 0 || layout->n == 0) return ok();
+  const hyb::GemmRoute r = hyb::gemm_route_device(*layout, m);
+  *bytes = hyb::split_workspace_bytes(r);
+  return ok();
+}
+
+hyb_status hyb_gemm_ws(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m, int64_t ldx,
+                       void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (m >= 0 && m <= hyb::kMaxGemvM && decode_route(layout, m))
+    return gemv_decode(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
+  if (st != HYB_OK) return st;
+  if (workspace_bytes > 0 && (!workspace || !aligned(workspace, 16)))
+    return fail(HYB_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned with workspace_bytes = %zu",
+                workspace_bytes);
+  if (m == 0 || layout->n == 0) return ok();
+  if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
+  const size_t need = hyb::split_workspace_bytes(hyb::gemm_route(*layout, m, hyb::device_cus()));
+  if (workspace_bytes > 0 && workspace_bytes < need)
+    return fail(HYB_ERR_INVALID_ARG, "workspace_bytes = %zu, this product needs %zu (or 0: unsplit)",
+                workspace_bytes, need);
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream),
+                                     workspace_bytes > 0 ? workspace : nullptr, workspace_bytes),
+                    "gemm launch");
 }
 
 hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out) {

@@ -143,16 +143,21 @@ struct GemmRxStage {
   int32_t ti[RG];
 };
 
-// With four wavefronts and up to 64 tokens the launch bound asks for two
-// wavefronts per SIMD (at most 256 registers each), so that two workgroups
-// share a CU; 128 tokens, or two row groups per wavefront, need the whole
-// register file of a SIMD.  RG is the number of 64-row groups per
-// workgroup (each wavefront multiplies all of them over its K range: two
-// groups halve the X reads per weight byte).
+// One piece of a register-fed product: K steps [k0, k1) of the tile of
+// 64*RG weight rows from n0 and BM = 16*MB tokens from m0.  The WAVES
+// wavefronts split the piece's K steps into contiguous ranges and never
+// synchronise inside the K walk; their sums are then added through LDS
+// (WAVES/2 wavefront-sized buffers) in a fixed tree order, so that
+// wavefront 0 ends with the piece's sum in `acc` (the other wavefronts'
+// `acc` are left partial).  The piece that starts at K step 0 also adds the
+// low-rank term.  The LDS arrays are declared here rather than passed in so
+// that every access to them is a known LDS access.
 template <int B2, int DT, int META, int MB, int WAVES, int STAGES, int RG>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 : 1) void k_gemm_rx(
-    const uint4* __restrict__ dense, const uint4* __restrict__ val, const uint16_t* __restrict__ meta,
-    const int32_t* __restrict__ tidx, const uint16_t* __restrict__ x, void* __restrict__ y, GemmDims d) {
+__device__ __forceinline__ void rx_piece(const uint4* __restrict__ dense, const uint4* __restrict__ val,
+                                         const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
+                                         const uint16_t* __restrict__ x, const GemmDims& d, int32_t n0,
+                                         int32_t m0, int32_t k0, int32_t k1, f32x4_t (&acc_out)[RG][4][MB]) {
+  f32x4_t acc[RG][4][MB];
   static_assert(WAVES == 4 || WAVES == 8, "tree reduction over 4 or 8 wavefronts");
   constexpr int BM = 16 * MB;
   constexpr int kStepsPerTile = B2 / 64;
@@ -163,16 +168,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
     fill_expand8_lut(lut8);
     __syncthreads();
   }
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int r = lane & 15;
-  const int32_t n0 = int32_t(blockIdx.x) * 64 * RG;
-  const int32_t m0 = int32_t(blockIdx.y) * BM;
-  const int32_t steps = d.tiles_k * kStepsPerTile;
-  const int32_t s0 = (wave * steps) / WAVES;
-  const int32_t cnt = ((wave + 1) * steps) / WAVES - s0;
+  const int32_t steps = k1 - k0;
+  const int32_t s0 = k0 + (wave * steps) / WAVES;
+  const int32_t cnt = k0 + ((wave + 1) * steps) / WAVES - s0;
   const int32_t mrows = d.m - m0 < BM ? d.m - m0 : BM;
   const int64_t tile = int64_t(d.b1) * B2;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + int64_t(m0) * d.ldx, mrows * int32_t(d.ldx) * 2);
@@ -222,7 +224,6 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
     }
   };
 
-  f32x4_t acc[RG][4][MB];
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
 
   // Low-rank term: token block mb by wavefront mb % WAVES, into that
   // wavefront's partial sums (the tree below keeps a fixed order).
-  if (d.rank > 0) {
+  if (d.rank > 0 && k0 == 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb % WAVES != wave) continue;
@@ -330,7 +331,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
   }
 
   // Tree reduction: wavefronts w >= h hand their sums to w - h, for
-  // h = WAVES/2, ..., 1.
+  // h = WAVES/2, ..., 1.  The closing barrier also keeps `red` free for the
+  // next piece.
 #pragma unroll
   for (int h = WAVES / 2; h >= 1; h /= 2) {
     if (wave >= h && wave < 2 * h) {
@@ -356,39 +358,194 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && MB <= 4 && RG == 1) ? 2 
     }
     __syncthreads();
   }
-  if (wave != 0) return;
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc_out[g][sl][mb] = acc[g][sl][mb];
+}
 
-  // acc[g][sl][mb] lane L holds rows n0 + 64 g + 16 sl + 4 (L/16) + 0..3 of
-  // token m0 + 16 mb + L%16.
-  const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+// Four outputs y[m][n..n+3] (fp32, or rounded to bf16 / fp16).
+__device__ __forceinline__ void store_row4(void* y, const GemmDims& d, int64_t m, int64_t n, f32x4_t v,
+                                           bool vec_ok) {
+  const int64_t base = m * d.ldy + n;
+  if (d.ydt == HYB_F32) {
+    float* dst = static_cast<float*>(y) + base;
+    if (vec_ok) {
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = v[e];
+    }
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(y) + base;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
+  }
+}
+
+__device__ __forceinline__ bool y_vec_ok(const void* y, const GemmDims& d) {
+  return (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+}
+
+// acc[g][sl][mb] lane L holds rows n0 + 64 g + 16 sl + 4 (L/16) + 0..3 of
+// token m0 + 16 mb + L%16.
+template <int MB, int RG>
+__device__ __forceinline__ void rx_store(const f32x4_t (&acc)[RG][4][MB], void* y, const GemmDims& d, int32_t n0,
+                                         int32_t m0, int lane) {
+  const bool vec_ok = y_vec_ok(y, d);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int64_t m = int64_t(m0) + mb * 16 + r;
+    const int64_t m = int64_t(m0) + mb * 16 + (lane & 15);
     if (m >= d.m) continue;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       if (n0 + 64 * g >= d.n) continue;
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const int64_t n = int64_t(n0) + 64 * g + sl * 16 + q * 4;
-        const f32x4_t v = acc[g][sl][mb];
-        const int64_t base = m * d.ldy + n;
-        if (d.ydt == HYB_F32) {
-          float* dst = static_cast<float*>(y) + base;
-          if (vec_ok) {
-            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = v[e];
-          }
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(y) + base;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
-        }
-      }
+      for (int sl = 0; sl < 4; ++sl)
+        store_row4(y, d, m, int64_t(n0) + 64 * g + sl * 16 + (lane >> 4) * 4, acc[g][sl][mb], vec_ok);
     }
   }
+}
+
+// With four wavefronts and up to 64 tokens the launch bound asks for two
+// wavefronts per SIMD (at most 256 registers each), so that two workgroups
+// share a CU; 128 tokens, or two row groups per wavefront, need the whole
+// register file of a SIMD.  RG is the number of 64-row groups per
+// workgroup (each wavefront multiplies all of them over its K range: two
+// groups halve the X reads per weight byte).
+template <int MB, int WAVES, int RG>
+constexpr int rx_occupancy() {
+  return (WAVES == 4 && MB <= 4 && RG == 1) ? 2 : 1;
+}
+
+template <int B2, int DT, int META, int MB, int WAVES, int STAGES, int RG>
+__global__ __launch_bounds__(64 * WAVES, (rx_occupancy<MB, WAVES, RG>())) void k_gemm_rx(
+    const uint4* __restrict__ dense, const uint4* __restrict__ val, const uint16_t* __restrict__ meta,
+    const int32_t* __restrict__ tidx, const uint16_t* __restrict__ x, void* __restrict__ y, GemmDims d) {
+  const int32_t n0 = int32_t(blockIdx.x) * 64 * RG;
+  const int32_t m0 = int32_t(blockIdx.y) * 16 * MB;
+  f32x4_t acc[RG][4][MB];
+  rx_piece<B2, DT, META, MB, WAVES, STAGES, RG>(dense, val, meta, tidx, x, d, n0, m0, 0,
+                                                d.tiles_k * (B2 / 64), acc);
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) rx_store<MB, RG>(acc, y, d, n0, m0, threadIdx.x & 63);
+}
+
+// ------------------------------------------- GEMM (register-fed, split K) --
+//
+// When the tiles of a register-fed shape fill the compute units poorly
+// (e.g. 136 tiles of 128 rows x 64 tokens on 256 CUs), the (row block, K
+// step) units are dealt out evenly instead (the stream-K schedule).  Every
+// token block gets the same G' workgroups' worth of split: unit
+// u = nb * S + k (S K steps per tile) of token block mb, and of the G'
+// ranges the first U mod G' hold floor(U / G') + 1 consecutive units, the
+// rest floor(U / G') (U = row blocks * S).  Workgroup w = j * gm + mb runs
+// range j of token block mb, so the gm workgroups that read the same weight
+// rows at the same K steps are neighbours in launch order.  A workgroup's
+// range covers whole tiles, stored directly, and at most two partial
+// pieces: the piece its range starts in (workspace slot 2w) and the one it
+// ends in (slot 2w + 1).  A second kernel then adds the pieces of every
+// split tile in range order, a fixed order, so results are reproducible on
+// a given device.
+struct SplitPlan {
+  int32_t units;   // U = row blocks * steps (< 2^31)
+  int32_t steps;   // S, K steps per tile
+  int32_t groups;  // G', ranges per token block (1 <= G' <= U)
+  int32_t gm;      // token blocks
+  int32_t q, r;    // U = q G' + r
+};
+
+constexpr int32_t kSplitXcds = 8;
+
+// Launch arguments of a split product (groups 0: unsplit).
+struct SplitArgs {
+  int32_t groups;
+  float* ws;
+};
+
+__device__ __forceinline__ int32_t split_begin(int32_t j, const SplitPlan& p) {
+  return j * p.q + (j < p.r ? j : p.r);
+}
+
+// The range that holds unit u.
+__device__ __forceinline__ int32_t split_owner(int32_t u, const SplitPlan& p) {
+  const int32_t big = p.r * (p.q + 1);
+  return u < big ? u / (p.q + 1) : p.r + (u - big) / p.q;
+}
+
+template <int B2, int DT, int META, int MB, int WAVES, int STAGES, int RG>
+__global__ __launch_bounds__(64 * WAVES, (rx_occupancy<MB, WAVES, RG>())) void k_gemm_split(
+    const uint4* __restrict__ dense, const uint4* __restrict__ val, const uint16_t* __restrict__ meta,
+    const int32_t* __restrict__ tidx, const uint16_t* __restrict__ x, void* __restrict__ y, GemmDims d,
+    SplitPlan p, float* __restrict__ ws) {
+  constexpr int kPart = RG * 4 * MB * 64 * 4;
+  const int lane = threadIdx.x & 63;
+  const bool lead = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  // XCD-major order: launch slot L runs on XCD L % 8, and the workgroups of
+  // one XCD take consecutive w, so neighbours in w share that XCD's L2.
+  const int32_t G = int32_t(gridDim.x), L = int32_t(blockIdx.x);
+  const int32_t xcd = L % kSplitXcds, per = G / kSplitXcds, extra = G % kSplitXcds;
+  const int32_t w = xcd * per + (xcd < extra ? xcd : extra) + L / kSplitXcds;
+  const int32_t j = w / p.gm, mb = w - j * p.gm;
+  const int32_t m0 = mb * 16 * MB;
+  const int32_t u1 = split_begin(j + 1, p);
+  int slot = 0;
+  for (int32_t u = split_begin(j, p); u < u1; ++slot) {
+    const int32_t nb = u / p.steps;
+    const int32_t ts = nb * p.steps;
+    const int32_t k0 = u - ts;
+    const int32_t k1 = (u1 < ts + p.steps ? u1 : ts + p.steps) - ts;
+    const int32_t n0 = nb * 64 * RG;
+    f32x4_t acc[RG][4][MB];
+    rx_piece<B2, DT, META, MB, WAVES, STAGES, RG>(dense, val, meta, tidx, x, d, n0, m0, k0, k1, acc);
+    if (lead) {
+      if (k0 == 0 && k1 == p.steps) {
+        rx_store<MB, RG>(acc, y, d, n0, m0, lane);
+      } else {
+        float* part = ws + (2 * int64_t(w) + (slot == 0 ? 0 : 1)) * kPart;
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+              *reinterpret_cast<f32x4_t*>(part + (((g * 4 + sl) * MB + b) * 64 + lane) * 4) = acc[g][sl][b];
+      }
+    }
+    u = ts + k1;
+  }
+}
+
+// Adds the pieces of every split tile in workgroup order (the first
+// owner's piece is its end piece unless its range starts at the tile, every
+// later owner's is its start piece) and stores the sums.  One thread per
+// four outputs (one float4 of a piece): kBlocks workgroups of 256 threads
+// per tile; the workgroups of unsplit tiles return at once.
+template <int MB, int RG>
+__global__ __launch_bounds__(256) void k_gemm_split_sum(const float* __restrict__ ws, void* __restrict__ y,
+                                                        GemmDims d, SplitPlan p) {
+  constexpr int kVec = RG * 4 * MB * 64;  // float4 per piece
+  constexpr int kBlocks = kVec / 256;
+  const int32_t t = int32_t(blockIdx.x) / kBlocks;  // tile (row block t / gm, token block t % gm)
+  const int32_t nb = t / p.gm, mt = t - nb * p.gm;
+  const int32_t ts = nb * p.steps;
+  const int32_t ja = split_owner(ts, p), jb = split_owner(ts + p.steps - 1, p);
+  if (ja == jb) return;
+  const int f = (int(blockIdx.x) % kBlocks) * 256 + int(threadIdx.x);
+  const int64_t first = 2 * (int64_t(ja) * p.gm + mt) + (split_begin(ja, p) >= ts ? 0 : 1);
+  f32x4_t s = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ws + (first * kVec + f) * 4));
+  for (int32_t j = ja + 1; j <= jb; ++j)
+    s += __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4_t*>(ws + (2 * (int64_t(j) * p.gm + mt) * kVec + f) * 4));
+  const int lane = f & 63;
+  const int mb = (f >> 6) % MB;
+  const int sl = ((f >> 6) / MB) & 3;
+  const int g = (f >> 6) / (4 * MB);
+  const int32_t n0 = nb * 64 * RG;
+  const int64_t m = int64_t(mt) * 16 * MB + mb * 16 + (lane & 15);
+  if (m >= d.m || n0 + 64 * g >= d.n) return;
+  store_row4(y, d, m, int64_t(n0) + 64 * g + sl * 16 + (lane >> 4) * 4, s, y_vec_ok(y, d));
 }
 
 // ------------------------------------------------------------ GEMM (LDS) --
@@ -763,10 +920,34 @@ hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const Gemm
 }
 
 template <int B2, int DT, int META, int MB, int WAVES, int STAGES, int RG = 1>
-hipError_t gemm_rx_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+hipError_t gemm_rx_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, const SplitArgs& sp,
+                      hipStream_t s) {
   const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
+  const int64_t gn = (L.n + 64 * RG - 1) / (64 * RG);
+  if (sp.groups > 0) {
+    // K split over sp.groups workgroups in all, sp.groups / gm per token
+    // block (the caller has checked the workspace against
+    // split_workspace_bytes, which covers sp.groups workgroups)
+    const int64_t steps = int64_t(d.tiles_k) * (B2 / 64), units = gn * steps;
+    const int64_t per_block = sp.groups / gm;
+    if (units >= (int64_t(1) << 31) || units < 1 || per_block < 1) return hipErrorInvalidConfiguration;
+    SplitPlan p{};
+    p.gm = int32_t(gm);
+    p.steps = int32_t(steps);
+    p.units = int32_t(units);
+    p.groups = int32_t(per_block < units ? per_block : units);
+    p.q = p.units / p.groups;
+    p.r = p.units % p.groups;
+    hipLaunchKernelGGL((k_gemm_split<B2, DT, META, MB, WAVES, STAGES, RG>), dim3(unsigned(p.groups * gm)),
+                       dim3(64 * WAVES), 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, p, sp.ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_split_sum<MB, RG>), dim3(unsigned(gn * gm * (RG * MB))), dim3(256), 0, s,
+                       static_cast<const float*>(sp.ws), q.y, d, p);
+    return hipGetLastError();
+  }
   if (gm > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(unsigned((L.n + 64 * RG - 1) / (64 * RG)), unsigned(gm));
+  const dim3 grid{unsigned(gn), unsigned(gm), 1u};
   hipLaunchKernelGGL((k_gemm_rx<B2, DT, META, MB, WAVES, STAGES, RG>), grid, dim3(64 * WAVES), 0, s, q.dense,
                      q.val, q.meta, q.tidx, q.x, q.y, d);
   return hipGetLastError();
@@ -781,8 +962,8 @@ constexpr int lds_stages() {
 
 
 template <int B2, int DT, int META>
-hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
-  const GemmRoute r = gemm_route(L.n, m, device_cus());
+hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, const GemmRoute& r,
+                      const SplitArgs& sp, hipStream_t s) {
   if (r.kernel == kRouteLds) {
     switch (r.mb) {
       case 16: return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
@@ -792,32 +973,38 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
     }
   }
   if (r.rg == 2) {
-    if (r.mb == 2) return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, s);
-    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, s);
+    if (r.mb == 2) return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, sp, s);
+    return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, sp, s);
+  }
+  if (r.waves == 4) {
+    switch (r.mb) {
+      case 1: return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, sp, s);
+      case 2: return gemm_rx_go<B2, DT, META, 2, 4, 2>(L, q, m, d, sp, s);
+      default: return gemm_rx_go<B2, DT, META, 4, 4, 2>(L, q, m, d, sp, s);
+    }
   }
   switch (r.mb) {
-    case 1:
-      if (r.waves == 8) return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, s);
-      return gemm_rx_go<B2, DT, META, 1, 4, 2>(L, q, m, d, s);
-    case 2: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, s);
-    default: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, s);
+    case 1: return gemm_rx_go<B2, DT, META, 1, 8, 2>(L, q, m, d, sp, s);
+    case 2: return gemm_rx_go<B2, DT, META, 2, 8, 2>(L, q, m, d, sp, s);
+    default: return gemm_rx_go<B2, DT, META, 4, 8, 2>(L, q, m, d, sp, s);
   }
 }
 
 template <int DT, int META>
-hipError_t gemm_b2(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+hipError_t gemm_b2(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, const GemmRoute& r,
+                   const SplitArgs& sp, hipStream_t s) {
   switch (L.b2) {
-    case 64: return gemm_shape<64, DT, META>(L, q, m, d, s);
-    case 128: return gemm_shape<128, DT, META>(L, q, m, d, s);
-    default: return gemm_shape<256, DT, META>(L, q, m, d, s);
+    case 64: return gemm_shape<64, DT, META>(L, q, m, d, r, sp, s);
+    case 128: return gemm_shape<128, DT, META>(L, q, m, d, r, sp, s);
+    default: return gemm_shape<256, DT, META>(L, q, m, d, r, sp, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
-                       void* y, int y_dtype, int64_t ldy, hipStream_t s, const float* t, int64_t ldt,
-                       const void* u, int64_t ldu, int rank) {
+                       void* y, int y_dtype, int64_t ldy, hipStream_t s, void* ws, size_t ws_bytes,
+                       const float* t, int64_t ldt, const void* u, int64_t ldu, int rank) {
   GemvPtrs q{static_cast<const uint4*>(P.dense), static_cast<const uint4*>(P.val),
              static_cast<const uint16_t*>(P.meta), P.tidx, static_cast<const uint16_t*>(x), y};
   GemmDims d{};
@@ -835,14 +1022,18 @@ hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, 
   d.ldt = ldt;
   d.ldu = ldu;
   d.rank = rank;
+  const GemmRoute r = gemm_route(L, m, device_cus());
+  // Without a large enough workspace a split route runs its shape unsplit.
+  SplitArgs sp{0, nullptr};
+  if (r.kernel == kRouteSplit && ws && ws_bytes >= split_workspace_bytes(r)) sp = SplitArgs{r.groups, static_cast<float*>(ws)};
   if (L.dtype == HYB_BF16) {
-    if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, s);
-    if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, s);
-    return gemm_b2<HYB_BF16, HYB_META_MASK8>(L, q, m, d, s);
+    if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, r, sp, s);
+    if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, r, sp, s);
+    return gemm_b2<HYB_BF16, HYB_META_MASK8>(L, q, m, d, r, sp, s);
   }
-  if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_F16, HYB_META_IDX2>(L, q, m, d, s);
-  if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_F16, HYB_META_MASK4>(L, q, m, d, s);
-  return gemm_b2<HYB_F16, HYB_META_MASK8>(L, q, m, d, s);
+  if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_F16, HYB_META_IDX2>(L, q, m, d, r, sp, s);
+  if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_F16, HYB_META_MASK4>(L, q, m, d, r, sp, s);
+  return gemm_b2<HYB_F16, HYB_META_MASK8>(L, q, m, d, r, sp, s);
 }
 
 }  // namespace hyb

@@ -57,22 +57,37 @@ int gemv_waves(int64_t slabs, int m);
 constexpr int kRouteDecode = 1;    // k_gemv
 constexpr int kRouteRegister = 2;  // k_gemm_rx
 constexpr int kRouteLds = 3;       // k_gemm_lds
+constexpr int kRouteSplit = 4;     // k_gemm_split + k_gemm_split_sum
 struct GemmRoute {
   int kernel;  // kRoute*
   int mb;      // token blocks of 16 per workgroup (0: the decode kernel)
   int waves;   // wavefronts per workgroup
   int rg;      // 64-row groups per workgroup (0: the decode kernel's 16-row slabs)
+  int groups;  // workgroups of a split launch (0 otherwise)
 };
-// What the matrix-core kernels run for m >= 1 tokens on an n-row matrix
+// A split launch runs one workgroup per CU on at most this many CUs (its
+// workgroups hold partial sums in a workspace of at most kSplitMaxBytes) ...
+constexpr int64_t kSplitMaxCus = 256;
+// ... and gives each wavefront at least this many K steps.
+constexpr int64_t kSplitMinSteps = 2;
+// Largest split_workspace_bytes of any route: 256 workgroups x 2 pieces x
+// (128 rows x 64 tokens x 4 bytes).
+constexpr size_t kSplitMaxBytes = size_t(kSplitMaxCus) * 2 * 2 * 4 * 4096;
+// What the matrix-core kernels run for m >= 1 tokens on an n x k matrix
 // over `cus` compute units.
-GemmRoute gemm_route(int64_t n, int m, int64_t cus);
+GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus);
+GemmRoute gemm_route(const hyb_layout& L, int m, int64_t cus);
+// Workspace bytes of a route (nonzero only for a split launch).
+size_t split_workspace_bytes(const GemmRoute& r);
 // What hyb_gemm runs on the current device (decode kernel included).
 GemmRoute gemm_route_device(const hyb_layout& L, int m);
 // With rank > 0 the kernels add T U^T (t: m x rank fp32, u: n x rank) to
-// every output before it is stored.
+// every output before it is stored.  A split route runs split when `ws`
+// holds at least split_workspace_bytes of it (device memory, 16-byte
+// aligned, no initial contents needed), else as the same shape unsplit.
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m,
-                       int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s,
-                       const float* t = nullptr, int64_t ldt = 0, const void* u = nullptr, int64_t ldu = 0,
-                       int rank = 0);
+                       int64_t ldx, void* y, int y_dtype, int64_t ldy, hipStream_t s, void* ws,
+                       size_t ws_bytes, const float* t = nullptr, int64_t ldt = 0, const void* u = nullptr,
+                       int64_t ldu = 0, int rank = 0);
 
 }  // namespace hyb

@@ -13,6 +13,9 @@
 #ifndef HYB_GEMM_C_RX
 #define HYB_GEMM_C_RX 0.29
 #endif
+#ifndef HYB_GEMM_SPLIT_COST
+#define HYB_GEMM_SPLIT_COST 30.0
+#endif
 
 namespace hyb {
 
@@ -60,25 +63,88 @@ bool gemv_preferred(const hyb_layout& L, int m) {
 // a 192-token step 0.8, a 128-token step 0.64, a 64-token step 0.57), and
 // the shape with the smallest product runs, unless a register-fed shape,
 // priced the same way, costs under 0.9 of it.
-GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
+//
+// A register-fed shape whose last round of workgroups would leave compute
+// units idle can instead split K over one workgroup per CU (the stream-K
+// schedule of k_gemm_split), which then takes tiles / CUs of a round plus a
+// fixed cost of kSplitCost / S rounds for S K steps per tile (the partial
+// sums, the pieces' pipeline starts and the second kernel that adds them).
+// Measured on 1024 to 28672 rows, K = 4096 to 28672, 16 to 300 tokens: a
+// cost of 30 K steps picks the faster of plain and split in every case but
+// one (28672 x 8192 at 128 tokens, where the LDS shape runs, 7% slower).
+namespace {
+
+constexpr double kSplitCost = HYB_GEMM_SPLIT_COST;
+
+struct Priced {
+  GemmRoute r;
+  double rounds;  // rounds of this shape's workgroups over the CUs
+};
+
+// The cheaper of the plain and the split launch of one register-fed shape
+// (steps: K steps of 64 columns per tile).  A plain launch costs its
+// workgroups per CU, rounded up; with two workgroups per CU resident (the
+// shapes of rx_occupancy) the second still shares the CU, which costs about
+// as much as running after the first.
+Priced rx_priced(int64_t n, int64_t steps, int64_t m, int mb, int waves, int rg, int64_t cus) {
+  const int64_t gn = (n + 64 * rg - 1) / (64 * rg), gm = (m + 16 * mb - 1) / (16 * mb);
+  const int64_t tiles = gn * gm;
+  const int64_t rounds = (tiles + cus - 1) / cus;
+  Priced p{GemmRoute{kRouteRegister, mb, waves, rg, 0}, double(rounds)};
+  // Each wavefront of a split workgroup keeps at least kSplitMinSteps K
+  // steps; every token block gets the same number of workgroups.
+  int64_t groups = tiles * steps / (int64_t(waves) * kSplitMinSteps);
+  const int64_t max_groups = cus < kSplitMaxCus ? cus : kSplitMaxCus;
+  if (groups > max_groups) groups = max_groups;
+  groups -= groups % gm;
+  if (tiles % cus != 0 && groups > 1 && gn * steps < (int64_t(1) << 31)) {
+    const double c = double(tiles) / double(groups) + kSplitCost / double(steps);
+    if (c < p.rounds) p = Priced{GemmRoute{kRouteSplit, mb, waves, rg, int32_t(groups)}, c};
+  }
+  return p;
+}
+
+}  // namespace
+
+size_t split_workspace_bytes(const GemmRoute& r) {
+  return r.kernel == kRouteSplit ? size_t(r.groups) * 2 * size_t(r.rg) * size_t(r.mb) * 4096 : 0;
+}
+
+GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   const int64_t groups = n / 64;  // 64-row workgroups of the register-fed kernel
+  const int64_t steps = (k + 63) / 64;
+  const int64_t m64 = m;  // token-block counts in int64: m may be close to INT32_MAX
   if (m <= 16) {
     // Eight wavefronts (one workgroup per CU) when the 64-row groups fit in
-    // one round, else four (two workgroups per CU).
-    return GemmRoute{kRouteRegister, 1, groups <= cus ? 8 : 4, 1};
+    // one round, else four (two workgroups per CU); split as priced above.
+    return rx_priced(n, steps, m64, 1, groups <= cus ? 8 : 4, 1, cus).r;
   }
   // Register-fed shapes: token blocks of 16 per workgroup, wavefronts, 64-row
   // groups per workgroup; and the time of one round of each, relative to one
   // round of the 256-token LDS shape over the same K (measured on 1024 to
   // 8192 rows, K = 4096 to 28672, 24 to 1024 tokens).
-  constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {4, 8, 1}, {2, 4, 2}, {4, 4, 2}};
+  // (32 tokens x 128 rows on four wavefronts runs ahead of 64 tokens x 64
+  // rows on eight: of equal rounds it was the faster in every case measured.)
+  constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {2, 4, 2}, {4, 8, 1}, {4, 4, 2}};
   constexpr double kRound[5] = {0.12, 0.155, 0.21, 0.21, HYB_GEMM_C_RX};
-  // token-block counts in int64: m may be close to INT32_MAX
-  const int64_t m64 = m;
   auto rx_wgs = [&](int i) {
     return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
   };
-  auto rx = [&](int i) { return GemmRoute{kRouteRegister, kShapes[i][0], kShapes[i][1], kShapes[i][2]}; };
+  // The cheapest split launch of any register-fed shape (cost relative to
+  // the 256-token LDS round, as kRound).
+  auto best_split = [&](double& cost) {
+    GemmRoute best{0, 0, 0, 0, 0};
+    for (int i = 0; i < 5; ++i) {
+      if ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
+      const Priced p = rx_priced(n, steps, m64, kShapes[i][0], kShapes[i][1], kShapes[i][2], cus);
+      if (p.r.kernel == kRouteSplit && (best.kernel == 0 || p.rounds * kRound[i] < cost)) {
+        best = p.r;
+        cost = p.rounds * kRound[i];
+      }
+    }
+    return best;
+  };
+  auto rx = [&](int i) { return GemmRoute{kRouteRegister, kShapes[i][0], kShapes[i][1], kShapes[i][2], 0}; };
   if (m <= 128) {
     // The fewest rounds of workgroups over the CUs wins, then the most
     // workgroups; on a tie the earlier entry (one row group before two,
@@ -95,13 +161,19 @@ GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
         best_wgs = wgs;
       }
     }
+    double plain = double(best_rounds) * kRound[best];
+    GemmRoute pick = rx(best);
     // A wide matrix can need two rounds of the 128-row x 64-token shape
     // while the 64-token LDS shape (256 rows per workgroup) fits the whole
     // product in one; that round is cheaper than two (28672 x 8192 at 80-128
     // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
-    if (best == 4 && best_rounds >= 2 && ((n + 255) / 256) * ((m64 + 63) / 64) <= cus)
-      return GemmRoute{kRouteLds, 4, 8, 4};
-    return rx(best);
+    if (best == 4 && best_rounds >= 2 && ((n + 255) / 256) * ((m64 + 63) / 64) <= cus) {
+      pick = GemmRoute{kRouteLds, 4, 8, 4, 0};
+      plain = 0.57;
+    }
+    double split = 0.0;
+    const GemmRoute s = best_split(split);
+    return (s.kernel == kRouteSplit && split < plain) ? s : pick;
   }
   const int64_t gn = (n + 255) / 256;
   auto cost = [&](int64_t bm, double step) {
@@ -126,16 +198,21 @@ GemmRoute gemm_route(int64_t n, int m, int64_t cus) {
       rx_cost = c;
     }
   }
+  double split = 0.0;
+  const GemmRoute s = best_split(split);
+  if (s.kernel == kRouteSplit && split < rx_cost && split < 0.9 * best) return s;
   if (rx_best >= 0 && rx_cost < 0.9 * best) return rx(rx_best);
-  if (c256 == best) return GemmRoute{kRouteLds, 16, 8, 4};
-  if (c192 == best) return GemmRoute{kRouteLds, 12, 8, 4};
-  if (c128 == best) return GemmRoute{kRouteLds, 8, 8, 4};
-  return GemmRoute{kRouteLds, 4, 8, 4};
+  if (c256 == best) return GemmRoute{kRouteLds, 16, 8, 4, 0};
+  if (c192 == best) return GemmRoute{kRouteLds, 12, 8, 4, 0};
+  if (c128 == best) return GemmRoute{kRouteLds, 8, 8, 4, 0};
+  return GemmRoute{kRouteLds, 4, 8, 4, 0};
 }
 
+GemmRoute gemm_route(const hyb_layout& L, int m, int64_t cus) { return gemm_route(L.n, L.tiles_k * L.b2, m, cus); }
+
 GemmRoute gemm_route_device(const hyb_layout& L, int m) {
-  if (gemv_preferred(L, m)) return GemmRoute{kRouteDecode, 0, gemv_waves(L.n / 16, m), 0};
-  return gemm_route(L.n, m, device_cus());
+  if (gemv_preferred(L, m)) return GemmRoute{kRouteDecode, 0, gemv_waves(L.n / 16, m), 0, 0};
+  return gemm_route(L, m, device_cus());
 }
 
 }  // namespace hyb

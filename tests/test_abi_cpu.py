@@ -324,12 +324,20 @@ ROUTES = [
     ((14336, 4096, 128, 1), ("decode", 0, 4, 0)),
     ((1024, 4096, 128, 16), ("decode", 0, 16, 0)),       # short matrix: decode kernel up to 16 tokens
     ((14336, 4096, 128, 12), ("register", 1, 8, 1)),
-    ((17408, 5120, 64, 12), ("register", 1, 4, 1)),      # more 64-row groups than CUs
-    ((17408, 5120, 64, 16), ("register", 1, 4, 1)),
-    ((17408, 5120, 64, 40), ("register", 4, 4, 2)),
-    ((17408, 5120, 64, 96), ("register", 2, 4, 2)),
-    ((17408, 5120, 64, 100), ("lds", 4, 8, 4)),          # one LDS round instead of two register-fed
+    ((17408, 5120, 64, 12), ("split", 1, 4, 1)),         # 272 64-row groups: K split over 256 workgroups
+    ((17408, 5120, 64, 16), ("split", 1, 4, 1)),
+    ((17408, 5120, 64, 40), ("split", 4, 4, 2)),         # 136 tiles of 128 rows x 64 tokens on 256 CUs
+    ((17408, 5120, 64, 64), ("split", 4, 4, 2)),
+    ((17408, 5120, 64, 96), ("split", 2, 4, 2)),
+    ((17408, 5120, 64, 100), ("split", 4, 4, 2)),        # 272 tiles: split instead of two rounds
+    ((17408, 5120, 64, 128), ("split", 4, 4, 2)),
+    ((14336, 4096, 128, 64), ("register", 2, 4, 2)),
+    ((14336, 4096, 128, 128), ("register", 4, 4, 2)),    # 224 tiles fill the CUs well enough
     ((28672, 8192, 128, 96), ("lds", 4, 8, 4)),
+    ((8192, 28672, 128, 16), ("split", 1, 8, 1)),        # 128 groups on 256 CUs, 448 K steps
+    ((8192, 28672, 128, 64), ("split", 4, 4, 2)),
+    ((8192, 28672, 128, 128), ("split", 4, 4, 2)),
+    ((1024, 4096, 128, 32), ("split", 1, 8, 1)),
     ((17408, 5120, 64, 2048), ("lds", 12, 8, 4)),
     ((14336, 4096, 128, 200), ("lds", 4, 8, 4)),
     ((14336, 4096, 128, 300), ("lds", 8, 8, 4)),
@@ -338,7 +346,7 @@ ROUTES = [
     ((14336, 4096, 128, 2048), ("lds", 16, 8, 4)),
     ((8192, 28672, 128, 256), ("register", 4, 4, 2)),    # few 256-row blocks
     ((8192, 28672, 128, 512), ("lds", 4, 8, 4)),
-    ((4096, 4096, 128, 160), ("register", 4, 8, 1)),
+    ((4096, 4096, 128, 160), ("register", 2, 4, 2)),
     ((1024, 4096, 128, 384), ("register", 2, 8, 1)),
     ((8192, 256, 64, 1024), ("lds", 8, 8, 4)),
     ((8192, 256, 64, 2048), ("lds", 16, 8, 4)),
@@ -352,6 +360,44 @@ def test_gemm_routes(case, expect):
     n, k, b, m = case
     got = hb.gemm_shape(_layout(n, k, b), m)
     assert (got["kernel"], got["token_blocks"], got["waves"], got["row_groups"]) == expect, got
+
+
+def test_split_workspace_sizes(L):
+    """hyb_gemm_workspace_size: 2 pieces x (rows x tokens x 4 bytes) per
+    workgroup of a split route, 0 for every other route and for m = 0;
+    never above the 16 MiB the library holds per stream."""
+    for (n, k, b, m), expect in ROUTES:
+        lay = _layout(n, k, b)
+        size = ctypes.c_size_t(7)
+        assert L.hyb_gemm_workspace_size(ctypes.byref(lay), m, ctypes.byref(size)) == 0
+        if expect[0] == "split":
+            _, mb, _, rg = expect
+            tiles_per_group = 2 * (64 * rg) * (16 * mb) * 4
+            assert size.value > 0 and size.value % tiles_per_group == 0, (n, k, m, size.value)
+            assert size.value // tiles_per_group <= 256
+            assert size.value <= 16 << 20
+        else:
+            assert size.value == 0, (n, k, m)
+    lay = _layout(17408, 5120, 64)
+    size = ctypes.c_size_t(7)
+    assert L.hyb_gemm_workspace_size(ctypes.byref(lay), 0, ctypes.byref(size)) == 0 and size.value == 0
+    assert L.hyb_gemm_workspace_size(ctypes.byref(lay), -1, ctypes.byref(size)) == 2
+    assert L.hyb_gemm_workspace_size(ctypes.byref(lay), 100, None) == 1
+    assert L.hyb_gemm_workspace_size(None, 100, ctypes.byref(size)) == 1
+
+
+def test_gemm_ws_rejects_before_launch(L):
+    """hyb_gemm_ws: a positive size with a NULL or misaligned workspace, or a
+    size below the need, is HYB_ERR_INVALID_ARG before anything runs."""
+    fn = L.hyb_gemm_ws
+    L2, _ = hb.plan(2048, 16384, 128, 128, "bf16", "idx2", np.zeros((16, 128), np.uint8))
+    need = ctypes.c_size_t(0)
+    assert L.hyb_gemm_workspace_size(ctypes.byref(L2), 100, ctypes.byref(need)) == 0 and need.value > 0
+    packed = hb.HybPacked(FAKE, FAKE, FAKE, FAKE)
+    args = lambda ws, nb: (ctypes.byref(L2), ctypes.byref(packed), FAKE, 100, 16384, FAKE, 3, 2048, ws, nb, None)
+    assert fn(*args(None, need.value)) == 1                 # NULL with a size
+    assert fn(*args(FAKE + 8, need.value)) == 1             # misaligned
+    assert fn(*args(FAKE, need.value - 16)) == 1            # below the need
 
 
 def test_gemm_shape_rejects(L):

@@ -601,21 +601,23 @@ def test_gemm_lds_shapes_random(n, m, b1, b2, dtype, meta):
     assert_close(y, yref, s, what=f"gemm lds n={n} m={m}")
 
 
-@pytest.mark.parametrize("config,index,m,route", [(3, 1, 384, (2, 8, 1)), (3, 0, 160, (4, 8, 1)),
-                                                  (3, 6, 256, (4, 8, 1))])
+@pytest.mark.parametrize("config,index,m,route", [(3, 1, 384, ("register", 2, 8, 1)),
+                                                  (3, 0, 160, ("register", 2, 4, 2)),
+                                                  (3, 6, 256, ("split", 4, 4, 2))])
 def test_gemm_small_matrices_above_128(config, index, m, route):
     """Few 256-row blocks above 128 tokens: the launcher prices every
-    register-fed shape against the LDS shapes and, on a 256-CU device, runs
-    32 tokens x 64 rows on eight wavefronts for the 1024 x 4096 k projection
-    at 384 tokens, and 64 tokens x 64 rows on eight wavefronts for the
-    4096-row q (160 tokens, ragged) and down (256 tokens) projections.
-    Every output against the oracle."""
+    register-fed shape, plain and split, against the LDS shapes and, on a
+    256-CU device, runs 32 tokens x 64 rows on eight wavefronts for the 1024
+    x 4096 k projection at 384 tokens, 32 tokens x 128 rows on four
+    wavefronts for the 4096-row q projection at 160 tokens (ragged), and 64
+    tokens x 128 rows split over 256 workgroups for the 4096 x 14336 down
+    projection at 256 tokens.  Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(config, index)
     note(f"gemm small matrix {mat.name} m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    expect_route(P, m, "register", *route)
+    expect_route(P, m, *route)
     yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
     assert_close(y, yref, s, what=f"gemm {mat.name} m={m}")
@@ -660,14 +662,16 @@ def test_gemm_8b_up_shapes(m, tb):
     assert_close(y, yref, s, what=f"gemm m={m}")
 
 
-@pytest.mark.parametrize("m,route", [(160, ("register", 4, 4, 2)), (256, ("register", 4, 4, 2)),
-                                     (512, ("lds", 4, 8, 4))])
+@pytest.mark.parametrize("m,route", [(64, ("split", 4, 4, 2)), (160, ("split", 4, 4, 2)),
+                                     (256, ("register", 4, 4, 2)), (512, ("lds", 4, 8, 4))])
 def test_gemm_tall_70b(m, route):
     """8192x28672 (32 blocks of 256 rows), 128x128 tiles in a checkerboard:
-    at 160 and 256 tokens every LDS shape leaves most CUs of a 256-CU device
-    idle and the launcher runs the register-fed shape (128 rows by 64 tokens,
-    K split over four wavefronts; 160 with a ragged last block); at 512 it
-    runs the 64-token LDS shape.  Every output against the oracle."""
+    up to a few hundred tokens every LDS shape leaves most CUs of a 256-CU
+    device idle and the launcher runs the register-fed shape (128 rows by 64
+    tokens, K split over four wavefronts): at 64 and 160 tokens (ragged)
+    with K also split across 256 workgroups, at 256 tokens (256 tiles, one
+    per CU) plain; at 512 it runs the 64-token LDS shape.  Every output
+    against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 5)
     note(f"gemm 70b tall m={m}")

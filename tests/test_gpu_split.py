@@ -1,0 +1,154 @@
+"""GPU parity of the split-K register-fed launch (k_gemm_split + the kernel
+that adds the partial tiles): every split shape the launcher uses, in every
+dtype, metadata kind and tile size, with ragged row and token blocks, the
+low-rank epilogue, corrupt tile indices, 16-bit outputs, the caller-held
+workspace of hyb_gemm_ws, and replays of a captured graph.  Every output
+against the oracle (same acceptance rule as test_gpu_parity)."""
+import numpy as np
+import pytest
+
+import oracle
+from matmul_pack_b1_amd import binding as hb
+from matmul_pack_b1_amd import workloads as wl
+from test_gpu_parity import (_torch, assert_close, dev, expect_route, note, oracle_full, oracle_full_lowrank,
+                             pack_gpu, random_case, upload)
+
+pytestmark = pytest.mark.gpu
+
+# (n, k, b1, b2, m, dtype, meta) -> split shape (token blocks, wavefronts,
+# row groups) on a 256-CU device.  2112 rows leave the last 128-row block
+# half outside the matrix; 100 and 70 tokens leave a ragged token block.
+CASES = [
+    ((256, 4096, 128, 128, 33, "bf16", "idx2"), (1, 8, 1)),
+    ((192, 8192, 64, 128, 17, "f16", "mask8"), (1, 8, 1)),
+    ((1024, 16384, 64, 256, 20, "f16", "mask4"), (2, 8, 1)),
+    ((2048, 8192, 256, 64, 65, "bf16", "mask8"), (2, 4, 2)),
+    ((2112, 16384, 64, 128, 70, "bf16", "mask4"), (2, 4, 2)),
+    ((2048, 16384, 128, 128, 100, "f16", "idx2"), (4, 4, 2)),
+    ((2112, 16384, 64, 128, 100, "bf16", "idx2"), (4, 4, 2)),
+]
+
+
+def _case(n, k, b1, b2, m, dtype, meta):
+    w, tmap = random_case(n + k + m, n, k, b1, b2, dtype, frac=0.6)
+    x = wl.float32_to_bits(np.random.default_rng(n + m).standard_normal((m, k)).astype(np.float32), dtype)
+    return w, tmap, x
+
+
+@pytest.mark.parametrize("case,shape", CASES)
+def test_split_shapes_every_output(case, shape):
+    """hyb_gemm (torch workspace), hyb_gemm_mfma (library-held workspace) and
+    hyb_gemm_ws with an explicit workspace give the same bits (same launch);
+    hyb_gemm_ws without a workspace runs the same shape unsplit.  All four
+    against the oracle on every output; a second call repeats the bits."""
+    torch = _torch()
+    n, k, b1, b2, m, dtype, meta = case
+    note(f"split {case}")
+    w, tmap, x = _case(*case)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    expect_route(P, m, "split", *shape)
+    need = hb.workspace_bytes(P, m)
+    assert 0 < need <= 16 << 20
+    xt = upload(x, dtype)
+    y = hb.gemm(P, xt)
+    y_again = hb.gemm(P, xt)
+    y_held = hb.gemm_mfma(P, xt)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev())
+    y_ws = hb.gemm(P, xt, workspace=ws)
+    y_plain = hb.gemm(P, xt, workspace=torch.empty(0, dtype=torch.uint8, device=dev()))
+    torch.cuda.synchronize()
+    for other in (y_again, y_held, y_ws):
+        assert torch.equal(y.view(torch.int32), other.view(torch.int32))
+    yref, s = oracle_full(w, tmap, b1, b2, x, dtype, meta)
+    assert_close(y.cpu().numpy(), yref, s, what=f"split {case}")
+    assert_close(y_plain.cpu().numpy(), yref, s, what=f"unsplit {case}")
+
+
+def test_split_lowrank_and_bf16_out():
+    """The low-rank term is added by the piece that starts at K step 0, and
+    the split tiles' sums are rounded once to a bf16 y."""
+    torch = _torch()
+    n, k, b1, b2, m, rank = 2112, 16384, 64, 128, 100, 64
+    note("split lowrank + bf16 y")
+    w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
+    rng = np.random.default_rng(99)
+    t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, "bf16")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    expect_route(P, m, "split", 4, 4, 2)
+    xt, tt = upload(x, "bf16"), torch.from_numpy(t).to(dev())
+    y = hb.gemm_lowrank(P, xt, tt, upload(u, "bf16"))
+    y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=torch.bfloat16)), "bf16")
+    torch.cuda.synchronize()
+    yref, s = oracle_full_lowrank(w, tmap, b1, b2, x, t, u, "bf16")
+    assert_close(y.cpu().numpy(), yref, s, what="split lowrank")
+    y0ref, s0 = oracle_full(w, tmap, b1, b2, x, "bf16")
+    assert_close(y16, y0ref, s0, extra=np.abs(y0ref) * 2.0 ** -8 + 2.0 ** -133, what="split bf16 y")
+
+
+def test_split_skips_corrupt_tile_index():
+    """tidx entries naming slots outside the streams are skipped inside the
+    split pieces too (the kernels' own bounds checks)."""
+    torch = _torch()
+    n, k, b1, b2, m = 2048, 16384, 128, 128, 100
+    note("split corrupt tidx")
+    w, tmap, x = _case(n, k, b1, b2, m, "f16", "idx2")
+    P = pack_gpu(w, tmap, b1, b2, "f16", "idx2")
+    expect_route(P, m, "split", 4, 4, 2)
+    tk = k // b2
+    bad = P.tidx.cpu().numpy().copy()
+    t0, t1 = 3 * tk + 50, 9 * tk + tk - 1      # tile (3, 50) and tile (9, last)
+    bad[t0] = 1 << 30
+    bad[t1] = -(1 << 30)
+    P.tidx.copy_(torch.from_numpy(bad))
+    y = hb.gemm(P, upload(x, "f16")).cpu().numpy()
+    wp = oracle.prune(w, tmap, b1, b2)
+    wp[3 * b1:4 * b1, 50 * b2:51 * b2] = 0
+    wp[9 * b1:10 * b1, (tk - 1) * b2:tk * b2] = 0
+    yref, s = oracle.ref_matmul(wp, x, "f16")
+    assert_close(y, yref, s, what="split corrupt tidx")
+
+
+def test_split_in_a_captured_graph():
+    """A split product captured into a graph: each of three replays, with
+    eager work and synchronisations between them, gives the eager bits."""
+    torch = _torch()
+    n, k, b1, b2, m = 2048, 16384, 128, 128, 100
+    note("split graph replays")
+    w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    expect_route(P, m, "split", 4, 4, 2)
+    xt = upload(x, "bf16")
+    eager = hb.gemm(P, xt)
+    y = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        g.capture_begin()
+        hb.gemm(P, xt, out=y)
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.fill_(float("nan"))
+        hb.gemm(P, xt[: m // 2])            # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), eager.view(torch.int32)), f"replay {i}"
+    del g
+
+
+def test_split_workspace_checks():
+    """hyb_gemm_ws rejects a workspace below the need, before any launch."""
+    torch = _torch()
+    n, k, b1, b2, m = 2048, 16384, 128, 128, 100
+    w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    need = hb.workspace_bytes(P, m)
+    small = torch.empty(need - 16, dtype=torch.uint8, device=dev())
+    with pytest.raises(hb.HybError) as e:
+        hb.gemm(P, upload(x, "bf16"), workspace=small)
+    assert e.value.status == 1
