@@ -287,6 +287,21 @@ hyb_status hyb_gemm_ws(const hyb_layout* layout, const hyb_packed* w, const void
                        int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): hyb_gemm with no
+ * allocation at all.  Where hyb_gemm would split K it uses a scratch array
+ * that the library holds in static device memory, 16 MiB per GPU from the
+ * library's load until the process ends, instead of a workspace (its
+ * address is looked up once per device, at the first call there).  The
+ * array keeps the last call's contents and needs no clearing; all calls on
+ * one GPU share it, so calls that overlap on one GPU (concurrent streams or
+ * host threads) race and must be serialised by the caller.  A product that
+ * would need more than the array holds -> HYB_ERR_UNSUPPORTED (none does on
+ * up to 256 CUs).  Arguments and other errors as hyb_gemm. */
+hyb_status hyb_gemm_noalloc(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                            int32_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                            void* stream);
+
 /* Matrix-core kernel only, any m >= 0 (no switch to the decode kernel);
  * exposed so that the crossover can be measured.  Same arguments. */
 hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x,

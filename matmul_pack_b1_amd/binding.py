@@ -29,7 +29,8 @@ META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_layout_check", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
-            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_ws", "hyb_gemm_workspace_size", "hyb_gemm_shape",
+            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_ws", "hyb_gemm_workspace_size", "hyb_gemm_noalloc",
+            "hyb_gemm_shape",
             "hyb_stream_read",
             "hyb_status_str", "hyb_last_error", "hyb_abi_version")
 KERNEL_NAMES = {1: "decode", 2: "register", 3: "lds", 4: "split"}   # HYB_KERNEL_* of hyb_gemm_shape
@@ -84,7 +85,7 @@ def lib() -> ctypes.CDLL:
     L.hyb_pack.restype = I32
     L.hyb_unpack.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I64, P]
     L.hyb_unpack.restype = I32
-    for name in ("hyb_gemv", "hyb_gemm", "hyb_gemm_mfma"):
+    for name in ("hyb_gemv", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_noalloc"):
         f = getattr(L, name)
         f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I32, I64, P]
         f.restype = I32
@@ -533,6 +534,12 @@ def gemm(P: PackedWeight, x, out_dtype=None, out=None, workspace=None):
     workspace from torch's allocator unless `workspace` (a contiguous device
     tensor of at least workspace_bytes(P, m) bytes) is given."""
     return _product("hyb_gemm_ws", P, x, out_dtype, out, workspace)
+
+
+def gemm_noalloc(P: PackedWeight, x, out_dtype=None, out=None):
+    """hyb_gemm with no device allocation: a split product uses the library's
+    static device scratch (calls that overlap on one GPU race)."""
+    return _product("hyb_gemm_noalloc", P, x, out_dtype, out)
 
 
 def workspace_bytes(P: PackedWeight, m: int) -> int:

@@ -472,6 +472,27 @@ hyb_status hyb_gemm(const hyb_layout* layout, const hyb_packed* w, const void* x
   return hyb_gemm_mfma(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
 }
 
+hyb_status hyb_gemm_noalloc(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m, int64_t ldx,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  if (m >= 0 && m <= hyb::kMaxGemvM && decode_route(layout, m))
+    return gemv_decode(layout, w, x, m, ldx, y, y_dtype, ldy, stream);
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
+  if (st != HYB_OK) return st;
+  if (m == 0 || layout->n == 0) return ok();
+  if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
+  const size_t need = hyb::split_workspace_bytes(hyb::gemm_route(*layout, m, hyb::device_cus()));
+  if (need > hyb::kSplitMaxBytes)
+    return fail(HYB_ERR_UNSUPPORTED, "this product needs %zu bytes of scratch, above the %zu bytes held per device",
+                need, hyb::kSplitMaxBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    if ((st = hip_status(hyb::split_scratch(&ws), "device scratch address")) != HYB_OK) return st;
+  }
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream),
+                                     ws, need > 0 ? hyb::kSplitMaxBytes : 0),
+                    "gemm launch");
+}
+
 hyb_status hyb_gemm_workspace_size(const hyb_layout* layout, int32_t m, size_t* bytes) {
   hyb_status st = check_layout(layout, true);
   if (st != HYB_OK) return st;

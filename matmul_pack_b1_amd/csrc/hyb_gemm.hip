@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-
+#include <mutex>
 
 #include "hyb_device.h"
 
@@ -1001,6 +1001,31 @@ hipError_t gemm_b2(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims
 }
 
 }  // namespace
+
+// Device scratch of hyb_gemm_noalloc's split launches (the partial tiles),
+// in place of a workspace: one array per GPU, held from the library's load
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device array: only the address that hipGetSymbolAddress returns
+// for the current device may reach a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[kSplitMaxBytes];
+
+hipError_t split_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
                        void* y, int y_dtype, int64_t ldy, hipStream_t s, void* ws, size_t ws_bytes,

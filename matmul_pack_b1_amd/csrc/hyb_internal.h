@@ -81,6 +81,9 @@ GemmRoute gemm_route(const hyb_layout& L, int m, int64_t cus);
 size_t split_workspace_bytes(const GemmRoute& r);
 // What hyb_gemm runs on the current device (decode kernel included).
 GemmRoute gemm_route_device(const hyb_layout& L, int m);
+// Device address, on the current device, of the library's static scratch
+// array of kSplitMaxBytes (looked up once per device; no allocation).
+hipError_t split_scratch(void** out);
 // With rank > 0 the kernels add T U^T (t: m x rank fp32, u: n x rank) to
 // every output before it is stored.  A split route runs split when `ws`
 // holds at least split_workspace_bytes of it (device memory, 16-byte

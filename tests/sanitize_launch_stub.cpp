@@ -31,6 +31,7 @@ hipError_t launch_gemv_grouped(int, const hyb_layout*, const hyb_packed*, const 
   return hipErrorNoDevice;
 }
 hipError_t launch_stream_read(const void*, int64_t, uint32_t*, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t split_scratch(void**) { return hipErrorNoDevice; }
 hipError_t launch_gemm(const hyb_layout&, const hyb_packed&, const void*, int, int64_t, void*, int, int64_t,
                        hipStream_t, void*, size_t, const float*, int64_t, const void*, int64_t, int) {
   return hipErrorNoDevice;

@@ -122,7 +122,7 @@ def _call(L, fn, lay, packed=None, x=FAKE, m=1, ldx=256, y=FAKE, ydt=3, ldy=256)
                           x, m, ldx, y, ydt, ldy, None)
 
 
-@pytest.mark.parametrize("fn", ["hyb_gemv", "hyb_gemm", "hyb_gemm_mfma"])
+@pytest.mark.parametrize("fn", ["hyb_gemv", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_noalloc"])
 def test_product_rejects(L, fn):
     lay = _good_layout()
     assert _call(L, fn, None) == 1                          # null layout
@@ -417,7 +417,7 @@ def test_negative_strides_rejected_even_when_empty(L):
     """A negative row stride is an invalid argument even when the operand is
     empty (k = 0 or n = 0): the kernels size buffer ranges as rows * stride."""
     lay_k0, _ = hb.plan(256, 0, 128, 128, "bf16", "idx2", np.zeros((2, 0), np.uint8))
-    for fn in ("hyb_gemv", "hyb_gemm", "hyb_gemm_mfma"):
+    for fn in ("hyb_gemv", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_noalloc"):
         assert _call(L, fn, lay_k0, m=20 if fn != "hyb_gemv" else 4, ldx=-8) == 1, fn
     lay_n0, _ = hb.plan(0, 256, 128, 128, "bf16", "idx2", np.zeros((0, 2), np.uint8))
     packed = hb.HybPacked(None, None, None, None)
