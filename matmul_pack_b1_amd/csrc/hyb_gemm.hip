@@ -974,6 +974,7 @@ hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmD
   }
   if (r.rg == 2) {
     if (r.mb == 2) return gemm_rx_go<B2, DT, META, 2, 4, 2, 2>(L, q, m, d, sp, s);
+    if (r.mb == 3) return gemm_rx_go<B2, DT, META, 3, 4, 2, 2>(L, q, m, d, sp, s);
     return gemm_rx_go<B2, DT, META, 4, 4, 2, 2>(L, q, m, d, sp, s);
   }
   if (r.waves == 4) {

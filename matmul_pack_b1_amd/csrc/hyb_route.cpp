@@ -125,8 +125,13 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   // 8192 rows, K = 4096 to 28672, 24 to 1024 tokens).
   // (32 tokens x 128 rows on four wavefronts runs ahead of 64 tokens x 64
   // rows on eight: of equal rounds it was the faster in every case measured.)
-  constexpr int kShapes[5][3] = {{1, 8, 1}, {2, 8, 1}, {2, 4, 2}, {4, 8, 1}, {4, 4, 2}};
-  constexpr double kRound[5] = {0.12, 0.155, 0.21, 0.21, HYB_GEMM_C_RX};
+  // (48 tokens x 128 rows costs less per round than 64 x 128: it needs
+  // fewer registers; 0.26 against 0.29 on 8192 and 17408 rows, and split
+  // 0.23, where the 64-token shape's split kernel spills.)
+  constexpr int kNumShapes = 6;
+  constexpr int kShapes[kNumShapes][3] = {{1, 8, 1}, {2, 8, 1}, {2, 4, 2}, {4, 8, 1}, {3, 4, 2}, {4, 4, 2}};
+  constexpr double kRound[kNumShapes] = {0.12, 0.155, 0.21, 0.21, 0.26, HYB_GEMM_C_RX};
+  constexpr double kSplitRound[kNumShapes] = {0.12, 0.155, 0.21, 0.21, 0.23, HYB_GEMM_C_RX};
   auto rx_wgs = [&](int i) {
     return ((groups + kShapes[i][2] - 1) / kShapes[i][2]) * ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]));
   };
@@ -134,12 +139,12 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   // the 256-token LDS round, as kRound).
   auto best_split = [&](double& cost) {
     GemmRoute best{0, 0, 0, 0, 0};
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < kNumShapes; ++i) {
       if ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
       const Priced p = rx_priced(n, steps, m64, kShapes[i][0], kShapes[i][1], kShapes[i][2], cus);
-      if (p.r.kernel == kRouteSplit && (best.kernel == 0 || p.rounds * kRound[i] < cost)) {
+      if (p.r.kernel == kRouteSplit && (best.kernel == 0 || p.rounds * kSplitRound[i] < cost)) {
         best = p.r;
-        cost = p.rounds * kRound[i];
+        cost = p.rounds * kSplitRound[i];
       }
     }
     return best;
@@ -152,7 +157,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
     // 17-128 tokens: the pick is the fastest shape or within 3% of it.
     int best = 0;
     int64_t best_rounds = 0, best_wgs = 0;
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < kNumShapes; ++i) {
       const int64_t wgs = rx_wgs(i);
       const int64_t rounds = (wgs + cus - 1) / cus;
       if (i == 0 || rounds < best_rounds || (rounds == best_rounds && wgs > best_wgs)) {
@@ -167,7 +172,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
     // while the 64-token LDS shape (256 rows per workgroup) fits the whole
     // product in one; that round is cheaper than two (28672 x 8192 at 80-128
     // tokens: 125 against 145-160 us; 17408 x 5120 at 128: 73 against 77).
-    if (best == 4 && best_rounds >= 2 && ((n + 255) / 256) * ((m64 + 63) / 64) <= cus) {
+    if (best == kNumShapes - 1 && best_rounds >= 2 && ((n + 255) / 256) * ((m64 + 63) / 64) <= cus) {
       pick = GemmRoute{kRouteLds, 4, 8, 4, 0};
       plain = 0.57;
     }
@@ -190,7 +195,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   // 65535 token blocks, the register-fed grid's limit, is not a candidate.
   int rx_best = -1;
   double rx_cost = 0.0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < kNumShapes; ++i) {
     if ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
     const double c = double((rx_wgs(i) + cus - 1) / cus) * kRound[i];
     if (rx_best < 0 || c < rx_cost) {
@@ -200,7 +205,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   }
   double split = 0.0;
   const GemmRoute s = best_split(split);
-  if (s.kernel == kRouteSplit && split < rx_cost && split < 0.9 * best) return s;
+  if (s.kernel == kRouteSplit && split < rx_cost && split < best) return s;
   if (rx_best >= 0 && rx_cost < 0.9 * best) return rx(rx_best);
   if (c256 == best) return GemmRoute{kRouteLds, 16, 8, 4, 0};
   if (c192 == best) return GemmRoute{kRouteLds, 12, 8, 4, 0};

@@ -326,14 +326,15 @@ ROUTES = [
     ((14336, 4096, 128, 12), ("register", 1, 8, 1)),
     ((17408, 5120, 64, 12), ("split", 1, 4, 1)),         # 272 64-row groups: K split over 256 workgroups
     ((17408, 5120, 64, 16), ("split", 1, 4, 1)),
-    ((17408, 5120, 64, 40), ("split", 4, 4, 2)),         # 136 tiles of 128 rows x 64 tokens on 256 CUs
+    ((17408, 5120, 64, 40), ("split", 3, 4, 2)),         # 136 tiles of 128 rows x 48 tokens on 256 CUs
     ((17408, 5120, 64, 64), ("split", 4, 4, 2)),
-    ((17408, 5120, 64, 96), ("split", 2, 4, 2)),
+    ((17408, 5120, 64, 96), ("split", 3, 4, 2)),
     ((17408, 5120, 64, 100), ("split", 4, 4, 2)),        # 272 tiles: split instead of two rounds
     ((17408, 5120, 64, 128), ("split", 4, 4, 2)),
     ((14336, 4096, 128, 64), ("register", 2, 4, 2)),
     ((14336, 4096, 128, 128), ("register", 4, 4, 2)),    # 224 tiles fill the CUs well enough
-    ((28672, 8192, 128, 96), ("lds", 4, 8, 4)),
+    ((28672, 8192, 128, 96), ("split", 3, 4, 2)),        # split 48-token tiles beat one LDS round
+    ((28672, 8192, 128, 128), ("lds", 4, 8, 4)),
     ((8192, 28672, 128, 16), ("split", 1, 8, 1)),        # 128 groups on 256 CUs, 448 K steps
     ((8192, 28672, 128, 64), ("split", 4, 4, 2)),
     ((8192, 28672, 128, 128), ("split", 4, 4, 2)),

@@ -683,19 +683,19 @@ def test_gemm_tall_70b(m, route):
     assert_close(y, yref, s, what=f"gemm tall m={m}")
 
 
-@pytest.mark.parametrize("m", [80, 128])
-def test_gemm_wide_70b(m):
-    """28672x8192 (128x128 tiles, checkerboard) at 80 and 128 tokens: the
-    register-fed pick would need two rounds of 128-row x 64-token workgroups
-    on a 256-CU device, so the launcher runs the 64-token LDS shape, whose
-    224 workgroups fit in one (80: ragged last token block).  Every output
-    against the oracle."""
+@pytest.mark.parametrize("m,route", [(80, ("split", 3, 4, 2)), (128, ("lds", 4, 8, 4))])
+def test_gemm_wide_70b(m, route):
+    """28672x8192 (128x128 tiles, checkerboard): at 80 tokens (ragged) the
+    launcher splits 48-token x 128-row tiles over 256 workgroups; at 128 the
+    register-fed shapes would need two rounds on a 256-CU device and the
+    64-token LDS shape, 224 workgroups, fits in one.  Every output against
+    the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 2)
     note(f"gemm 70b wide m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    expect_route(P, m, "lds", 4, 8, 4)
+    expect_route(P, m, *route)
     yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
     assert_close(y, yref, s, what=f"gemm wide m={m}")

@@ -17,13 +17,17 @@ pytestmark = pytest.mark.gpu
 
 # (n, k, b1, b2, m, dtype, meta) -> split shape (token blocks, wavefronts,
 # row groups) on a 256-CU device.  2112 rows leave the last 128-row block
-# half outside the matrix; 100 and 70 tokens leave a ragged token block.
+# half outside the matrix; 100, 90 and 70 tokens leave a ragged token block.
 CASES = [
     ((256, 4096, 128, 128, 33, "bf16", "idx2"), (1, 8, 1)),
     ((192, 8192, 64, 128, 17, "f16", "mask8"), (1, 8, 1)),
     ((1024, 16384, 64, 256, 20, "f16", "mask4"), (2, 8, 1)),
-    ((2048, 8192, 256, 64, 65, "bf16", "mask8"), (2, 4, 2)),
-    ((2112, 16384, 64, 128, 70, "bf16", "mask4"), (2, 4, 2)),
+    ((4096, 16384, 64, 128, 20, "bf16", "mask4"), (2, 4, 2)),
+    ((2048, 8192, 256, 64, 65, "bf16", "mask8"), (3, 4, 2)),
+    ((2112, 16384, 64, 128, 70, "bf16", "mask4"), (3, 4, 2)),
+    ((1024, 16384, 64, 64, 48, "bf16", "mask4"), (3, 4, 2)),
+    ((2112, 16384, 64, 128, 90, "f16", "mask8"), (3, 4, 2)),
+    ((1088, 8192, 64, 128, 100, "f16", "idx2"), (4, 8, 1)),
     ((2048, 16384, 128, 128, 100, "f16", "idx2"), (4, 4, 2)),
     ((2112, 16384, 64, 128, 100, "bf16", "idx2"), (4, 4, 2)),
 ]
