@@ -205,7 +205,8 @@ def main():
     ap.add_argument("--prefill-m", type=int, default=2048,
                     help="token count of the prefill GEMM measurement")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,patterns,prefill,tall)")
+                    help="comma list of parts to run (pack,gemv,dense,unpack,gemm,grouped,lowrank,nm48,patterns,"
+                         "prefill,tall,mid)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 128 MiB device copies (torch copy kernel) as a counter reference")
@@ -229,7 +230,7 @@ def main():
     dev = torch.device("cuda:0")
     rotate = int(args.rotate_gib * (1 << 30))
     rows = set(args.only.split(",")) if args.only else {"pack", "gemv", "dense", "unpack", "gemm", "grouped",
-                                                         "lowrank", "nm48", "patterns", "prefill", "tall"}
+                                                         "lowrank", "nm48", "patterns", "prefill", "tall", "mid"}
 
     if args.copy_calibration:
         # A plain copy of known size: 128 MiB read + 128 MiB written per
@@ -475,6 +476,13 @@ def main():
         log("[bench] prefill GEMM on a short, deep matrix, M=256")
         out["tall"] = tall(hb, torch, wl, dev, 256, args.meta)
         log(f"[bench] tall: {out['tall']}")
+    if "mid" in rows:
+        # the memory-bound range of the matrix-core kernels (16 to a few
+        # hundred tokens), against the vendor BLAS on the same shapes
+        log("[bench] GEMM in the memory-bound range: Qwen3-14B gate/up at 64, 96, 128 tokens; 70B down at 64, 128")
+        out["mid"] = ([prefill(hb, torch, wl, dev, m, args.meta) for m in (64, 96, 128)] +
+                      [tall(hb, torch, wl, dev, m, args.meta) for m in (64, 128)])
+        log(f"[bench] mid: {out['mid']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(mat, w_bits, tmap, x_bits, L)
@@ -523,8 +531,9 @@ def prefill(hb, torch, wl, dev, m, meta):
 def tall(hb, torch, wl, dev, m, meta):
     """The same three products on the 70B-shaped down projection (8192 x
     28672, 128 x 128 tiles in a checkerboard): only 32 blocks of 256 rows, so
-    the launcher runs the register-fed shape (128 rows x 64 tokens, K split
-    over four wavefronts) up to a few hundred tokens."""
+    up to a few hundred tokens the launcher runs a register-fed shape (128
+    rows x 48 or 64 tokens, K split over four wavefronts), with K also split
+    across one workgroup per CU where its tiles would leave CUs idle."""
     mat = wl.workload(4).matrices[5]
     return product_row(hb, torch, dev, mat, m, meta,
                        f"Llama-3.1-70B-shaped down projection {mat.n}x{mat.k} bf16, {mat.b1}x{mat.b2} tiles "
