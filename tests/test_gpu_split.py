@@ -156,3 +156,33 @@ def test_split_workspace_checks():
     with pytest.raises(hb.HybError) as e:
         hb.gemm(P, upload(x, "bf16"), workspace=small)
     assert e.value.status == 1
+
+
+def test_split_two_streams_held_workspaces():
+    """hyb_gemm_mfma keeps one workspace per (device, stream): split products
+    enqueued on two streams at once, each on its own inputs, give the bits of
+    the same products run one after the other."""
+    torch = _torch()
+    n, k, b1, b2 = 2048, 16384, 128, 128
+    note("split on two streams")
+    cases = []
+    for m, seed in ((100, 1), (48, 2)):
+        w, tmap = random_case(seed, n, k, b1, b2, "bf16", frac=0.6)
+        x = wl.float32_to_bits(np.random.default_rng(seed).standard_normal((m, k)).astype(np.float32), "bf16")
+        P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+        assert hb.gemm_shape(P.layout, m)["kernel"] == "split"
+        cases.append((P, upload(x, "bf16")))
+    serial = [hb.gemm_mfma(P, x) for P, x in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(y) for y in serial]
+    for rep in range(3):
+        for s_ in streams:
+            s_.wait_stream(torch.cuda.current_stream())
+        for (P, x), s_, out in zip(cases, streams, outs):
+            with torch.cuda.stream(s_):
+                for _ in range(4):
+                    hb.gemm_mfma(P, x, out=out)
+        torch.cuda.synchronize()
+        for y, out in zip(serial, outs):
+            assert torch.equal(y.view(torch.int32), out.view(torch.int32)), f"repeat {rep}"
