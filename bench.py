@@ -545,9 +545,12 @@ def kernel_text(hb, layout, m):
     sh = hb.gemm_shape(layout, m)
     if sh["kernel"] == "decode":
         return f"k_gemv ({sh['waves']} wavefronts per 16-row slab)"
-    name = {"register": "k_gemm_rx", "split": "k_gemm_split + k_gemm_split_sum", "lds": "k_gemm_lds"}[sh["kernel"]]
+    lds_split = sh["kernel"] == "split" and sh["row_groups"] == 4
+    name = {"register": "k_gemm_rx", "lds": "k_gemm_lds",
+            "split": "k_gemm_lds_split + k_gemm_lds_split_sum" if lds_split else "k_gemm_split + k_gemm_split_sum"}[sh["kernel"]]
     split = {"register": ", wavefronts splitting K",
-             "split": ", wavefronts splitting K, K also split across one workgroup per CU",
+             "split": (", K split across one workgroup per CU" if lds_split
+                       else ", wavefronts splitting K, K also split across one workgroup per CU"),
              "lds": ""}[sh["kernel"]]
     return (f"{name} ({64 * sh['row_groups']}-row x {16 * sh['token_blocks']}-token workgroups on "
             f"{sh['waves']} wavefronts{split})")

@@ -645,13 +645,17 @@ struct GemmLdsCfg {
   static constexpr int kMBW = MB / kSplit;                    // token blocks per wavefront
 };
 
+// K steps [k0, k1) of the 256-row block nb and token block mbk: each
+// wavefront ends with the sums of its own outputs in acc_out (wavefront w:
+// row group w % 4, token half w / 4); no wavefront shares an output, so no
+// reduction follows.  The closing barrier frees the LDS stages for the next
+// piece.
 template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict__ dense,
-                                                  const uint4* __restrict__ val,
-                                                  const uint16_t* __restrict__ meta,
-                                                  const int32_t* __restrict__ tidx,
-                                                  const uint16_t* __restrict__ x,
-                                                  void* __restrict__ y, GemmDims d) {
+__device__ __forceinline__ void lds_piece(const uint4* __restrict__ dense, const uint4* __restrict__ val,
+                                          const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
+                                          const uint16_t* __restrict__ x, const GemmDims& d, int32_t nb,
+                                          int32_t mbk, int32_t k0, int32_t k1,
+                                          f32x4_t (&acc_out)[4][GemmLdsCfg<B2, MB, STAGES, WAVES>::kMBW]) {
   using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
   static_assert(Cfg::kXLoads >= 1 && Cfg::kXLoads * WAVES * 1024 == Cfg::kXBytes, "X tile split");
   constexpr int MBW = Cfg::kMBW;
@@ -668,14 +672,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
   const int wn = wave % 4;            // row group
   const int wm = wave / 4;            // token half (WAVES = 8)
   const int q = lane >> 4;
-  int32_t nb, mbk;
-  xcd_grouped_block((d.n + 255) / 256, nb, mbk);
   const int32_t n0 = nb * 256 + wn * 64;
   const int32_t m0 = mbk * BM;
   const bool rows_ok = n0 < d.n;
   const int32_t tn = n0 / d.b1;
   const int rs0 = (n0 - tn * d.b1) / 16;
-  const int32_t steps = d.tiles_k * kStepsPerTile;
   const int32_t* __restrict__ trow = tidx + int64_t(tn) * d.tiles_k;
   const int32_t mrows = d.m - m0 < BM ? d.m - m0 : BM;
   const int64_t tile = int64_t(d.b1) * B2;
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
 
   constexpr int32_t kNone = INT32_MIN;
   auto tile_index = [&](int32_t st) -> int32_t {
-    if (!rows_ok || st >= steps) return kNone;
+    if (!rows_ok || st >= k1) return kNone;
     const int32_t ti = trow[st / kStepsPerTile];
     const bool ok = ti >= 0 ? (ti < d.n_dense) : (~ti < d.n_sparse);
     return ok ? ti : kNone;
@@ -715,7 +716,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
     // X tile: piece j (8 rows x 128 B); wavefront w loads pieces
     // w * kXLoads ..; lane l -> row 8j + l/8, LDS slot l%8 holding global
     // 16-byte column (l%8) ^ ((row >> 1) & 7).
-    const srd_t xr = make_srd(x + int64_t(m0) * d.ldx, st < steps ? uint32_t(mrows * d.ldx * 2) : 0u);
+    const srd_t xr = make_srd(x + int64_t(m0) * d.ldx, st < k1 ? uint32_t(mrows * d.ldx * 2) : 0u);
     const uint32_t xdst = stage + Cfg::kABytes;
 #pragma unroll
     for (int i = 0; i < Cfg::kXLoads; ++i) {
@@ -852,8 +853,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
 
   // Prologue: steps 0 .. STAGES-2.
 #pragma unroll
-  for (int sg = 0; sg < STAGES - 1; ++sg) issue(sg, sg, tile_index(sg));
-  for (int32_t s0 = 0; s0 < steps; s0 += STAGES) {
+  for (int sg = 0; sg < STAGES - 1; ++sg) issue(k0 + sg, sg, tile_index(k0 + sg));
+  for (int32_t s0 = k0; s0 < k1; s0 += STAGES) {
 #pragma unroll
     for (int sg = 0; sg < STAGES; ++sg) {
       const int32_t st = s0 + sg;
@@ -864,38 +865,128 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
       __syncthreads();
       constexpr int kAhead = STAGES - 1;
       issue(st + kAhead, (sg + kAhead) % STAGES, tile_index(st + kAhead));
-      if (st < steps) compute(sg, st);
+      if (st < k1) compute(sg, st);
     }
   }
   wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) acc_out[i][j] = acc[i][j];
+}
 
-  if (!rows_ok) return;
-  if (d.rank > 0) lr_block<DT, 4, MBW>(acc, d, n0, m0 + wm * MBW * 16, lane);
-  const bool vec_ok = (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+// Stores a wavefront's outputs of an LDS-fed tile (lane L: rows
+// n0 + 16 sl + 4 (L/16) + 0..3, token mt0 + 16 mb + L%16), adding the
+// low-rank term first when `lr` is set.
+template <int DT, int MBW>
+__device__ __forceinline__ void lds_store(f32x4_t (&acc)[4][MBW], void* y, const GemmDims& d, int32_t n0,
+                                          int32_t mt0, bool lr) {
+  const int lane = threadIdx.x & 63;
+  if (n0 >= d.n) return;
+  if (lr && d.rank > 0) lr_block<DT, 4, MBW>(acc, d, n0, mt0, lane);
+  const bool vec_ok = y_vec_ok(y, d);
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
-    const int64_t m = int64_t(m0) + (wm * MBW + mb) * 16 + (lane & 15);
+    const int64_t m = int64_t(mt0) + mb * 16 + (lane & 15);
     if (m >= d.m) continue;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const int64_t n = int64_t(n0) + sl * 16 + q * 4;
-      const f32x4_t v = acc[sl][mb];
-      const int64_t base = m * d.ldy + n;
-      if (d.ydt == HYB_F32) {
-        float* dst = static_cast<float*>(y) + base;
-        if (vec_ok) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = v[e];
-        }
-      } else {
-        uint16_t* dst = static_cast<uint16_t*>(y) + base;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = d.ydt == HYB_BF16 ? round16<HYB_BF16>(v[e]) : round16<HYB_F16>(v[e]);
-      }
-    }
+    for (int sl = 0; sl < 4; ++sl) store_row4(y, d, m, int64_t(n0) + sl * 16 + (lane >> 4) * 4, acc[sl][mb], vec_ok);
   }
+}
+
+template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict__ dense,
+                                                  const uint4* __restrict__ val,
+                                                  const uint16_t* __restrict__ meta,
+                                                  const int32_t* __restrict__ tidx,
+                                                  const uint16_t* __restrict__ x,
+                                                  void* __restrict__ y, GemmDims d) {
+  using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int32_t nb, mbk;
+  xcd_grouped_block((d.n + 255) / 256, nb, mbk);
+  f32x4_t acc[4][Cfg::kMBW];
+  lds_piece<B2, DT, META, MB, STAGES, WAVES>(dense, val, meta, tidx, x, d, nb, mbk, 0, d.tiles_k * (B2 / 64), acc);
+  lds_store<DT, Cfg::kMBW>(acc, y, d, nb * 256 + (wave % 4) * 64, mbk * 16 * MB + (wave / 4) * Cfg::kMBW * 16,
+                           true);
+}
+
+// The LDS-fed 256-row shape with K split across workgroups, on the schedule
+// of k_gemm_split (units u = nb * S + k of each token block, G' ranges per
+// token block, workgroup w = j * gm + mb, XCD-major).  A partial piece's
+// outputs go to workspace slot 2w (the piece the range starts in) or 2w + 1,
+// each wavefront writing its own outputs.
+template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_lds_split(const uint4* __restrict__ dense,
+                                                        const uint4* __restrict__ val,
+                                                        const uint16_t* __restrict__ meta,
+                                                        const int32_t* __restrict__ tidx,
+                                                        const uint16_t* __restrict__ x, void* __restrict__ y,
+                                                        GemmDims d, SplitPlan p, float* __restrict__ ws) {
+  using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
+  constexpr int MBW = Cfg::kMBW;
+  constexpr int kWave = 4 * MBW * 64 * 4;     // floats of one wavefront's outputs
+  constexpr int kPart = WAVES * kWave;        // floats of one piece (256 rows x 16 MB tokens)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t G = int32_t(gridDim.x), L = int32_t(blockIdx.x);
+  const int32_t xcd = L % kSplitXcds, per = G / kSplitXcds, extra = G % kSplitXcds;
+  const int32_t w = xcd * per + (xcd < extra ? xcd : extra) + L / kSplitXcds;
+  const int32_t j = w / p.gm, mbk = w - j * p.gm;
+  const int32_t u1 = split_begin(j + 1, p);
+  const int32_t n_wave = (wave % 4) * 64, mt0 = mbk * 16 * MB + (wave / 4) * MBW * 16;
+  int slot = 0;
+  for (int32_t u = split_begin(j, p); u < u1; ++slot) {
+    const int32_t nb = u / p.steps;
+    const int32_t ts = nb * p.steps;
+    const int32_t k0 = u - ts;
+    const int32_t k1 = (u1 < ts + p.steps ? u1 : ts + p.steps) - ts;
+    f32x4_t acc[4][MBW];
+    lds_piece<B2, DT, META, MB, STAGES, WAVES>(dense, val, meta, tidx, x, d, nb, mbk, k0, k1, acc);
+    if (k0 == 0 && k1 == p.steps) {
+      lds_store<DT, MBW>(acc, y, d, nb * 256 + n_wave, mt0, true);
+    } else {
+      if (k0 == 0 && d.rank > 0 && nb * 256 + n_wave < d.n) lr_block<DT, 4, MBW>(acc, d, nb * 256 + n_wave, mt0, lane);
+      float* part = ws + (2 * int64_t(w) + (slot == 0 ? 0 : 1)) * kPart + wave * kWave;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+          *reinterpret_cast<f32x4_t*>(part + ((sl * MBW + mb) * 64 + lane) * 4) = acc[sl][mb];
+    }
+    u = ts + k1;
+  }
+}
+
+// k_gemm_split_sum for the LDS-fed pieces: float4 f of a piece is wavefront
+// f / (4 MBW 64), slab (f / (MBW 64)) % 4, token block (f / 64) % MBW, lane
+// f % 64.
+template <int MB, int WAVES>
+__global__ __launch_bounds__(256) void k_gemm_lds_split_sum(const float* __restrict__ ws, void* __restrict__ y,
+                                                            GemmDims d, SplitPlan p) {
+  constexpr int MBW = MB / (WAVES / 4);
+  constexpr int kVec = WAVES * 4 * MBW * 64;  // float4 per piece
+  constexpr int kBlocks = kVec / 256;
+  const int32_t t = int32_t(blockIdx.x) / kBlocks;
+  const int32_t nb = t / p.gm, mt = t - nb * p.gm;
+  const int32_t ts = nb * p.steps;
+  const int32_t ja = split_owner(ts, p), jb = split_owner(ts + p.steps - 1, p);
+  if (ja == jb) return;
+  const int f = (int(blockIdx.x) % kBlocks) * 256 + int(threadIdx.x);
+  const int64_t first = 2 * (int64_t(ja) * p.gm + mt) + (split_begin(ja, p) >= ts ? 0 : 1);
+  f32x4_t s = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ws + (first * kVec + f) * 4));
+  for (int32_t jj = ja + 1; jj <= jb; ++jj)
+    s += __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4_t*>(ws + (2 * (int64_t(jj) * p.gm + mt) * kVec + f) * 4));
+  const int lane = f & 63;
+  const int mb = (f >> 6) % MBW;
+  const int sl = ((f >> 6) / MBW) & 3;
+  const int wave = (f >> 6) / (4 * MBW);
+  const int32_t n0 = nb * 256 + (wave % 4) * 64;
+  const int64_t m = int64_t(mt) * 16 * MB + ((wave / 4) * MBW + mb) * 16 + (lane & 15);
+  if (m >= d.m || n0 >= d.n) return;
+  store_row4(y, d, m, int64_t(n0) + sl * 16 + (lane >> 4) * 4, s, y_vec_ok(y, d));
 }
 
 }  // namespace
@@ -906,12 +997,37 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds(const uint4* __restrict
 namespace {
 
 template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
-hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, hipStream_t s) {
+hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, const SplitArgs& sp,
+                       hipStream_t s) {
   using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
   static_assert(Cfg::kBytes <= 160 * 1024, "LDS budget");
   const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
   const int64_t gn = (L.n + 255) / 256;
   if (gn * gm >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+  if constexpr (MB == 4) {
+    if (sp.groups > 0) {
+      // K split over sp.groups workgroups in all, sp.groups / gm per token
+      // block (workspace checked by the caller, as for gemm_rx_go)
+      const int64_t steps = int64_t(d.tiles_k) * (B2 / 64), units = gn * steps;
+      const int64_t per_block = sp.groups / gm;
+      if (units >= (int64_t(1) << 31) || units < 1 || per_block < 1) return hipErrorInvalidConfiguration;
+      SplitPlan p{};
+      p.gm = int32_t(gm);
+      p.steps = int32_t(steps);
+      p.units = int32_t(units);
+      p.groups = int32_t(per_block < units ? per_block : units);
+      p.q = p.units / p.groups;
+      p.r = p.units % p.groups;
+      hipLaunchKernelGGL((k_gemm_lds_split<B2, DT, META, MB, STAGES, WAVES>), dim3(unsigned(p.groups * gm)),
+                         dim3(64 * WAVES), size_t(Cfg::kBytes), s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, p,
+                         sp.ws);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((k_gemm_lds_split_sum<MB, WAVES>), dim3(unsigned(gn * gm * (4 * MB))), dim3(256), 0, s,
+                         static_cast<const float*>(sp.ws), q.y, d, p);
+      return hipGetLastError();
+    }
+  }
   // 1-D launch of gn * gm workgroups, mapped to (row block, token block)
   // inside the kernel.
   hipLaunchKernelGGL((k_gemm_lds<B2, DT, META, MB, STAGES, WAVES>), dim3(unsigned(gn * gm)), dim3(64 * WAVES),
@@ -964,12 +1080,12 @@ constexpr int lds_stages() {
 template <int B2, int DT, int META>
 hipError_t gemm_shape(const hyb_layout& L, const GemvPtrs& q, int m, const GemmDims& d, const GemmRoute& r,
                       const SplitArgs& sp, hipStream_t s) {
-  if (r.kernel == kRouteLds) {
+  if (r.kernel == kRouteLds || r.rg == 4) {
     switch (r.mb) {
-      case 16: return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, s);
-      case 12: return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, s);
-      case 8: return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, s);
-      default: return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, s);
+      case 16: return gemm_lds_go<B2, DT, META, 16, lds_stages<B2, 16, 8, META>(), 8>(L, q, m, d, sp, s);
+      case 12: return gemm_lds_go<B2, DT, META, 12, lds_stages<B2, 12, 8, META>(), 8>(L, q, m, d, sp, s);
+      case 8: return gemm_lds_go<B2, DT, META, 8, lds_stages<B2, 8, 8, META>(), 8>(L, q, m, d, sp, s);
+      default: return gemm_lds_go<B2, DT, META, 4, lds_stages<B2, 4, 8, META>(), 8>(L, q, m, d, sp, s);
     }
   }
   if (r.rg == 2) {

@@ -57,12 +57,13 @@ int gemv_waves(int64_t slabs, int m);
 constexpr int kRouteDecode = 1;    // k_gemv
 constexpr int kRouteRegister = 2;  // k_gemm_rx
 constexpr int kRouteLds = 3;       // k_gemm_lds
-constexpr int kRouteSplit = 4;     // k_gemm_split + k_gemm_split_sum
+constexpr int kRouteSplit = 4;     // k_gemm_split or k_gemm_lds_split (rg 4), then its sum kernel
 struct GemmRoute {
   int kernel;  // kRoute*
   int mb;      // token blocks of 16 per workgroup (0: the decode kernel)
   int waves;   // wavefronts per workgroup
-  int rg;      // 64-row groups per workgroup (0: the decode kernel's 16-row slabs)
+  int rg;      // 64-row groups per workgroup (0: the decode kernel's 16-row slabs;
+               // 4: the LDS-fed kernel, also when split)
   int groups;  // workgroups of a split launch (0 otherwise)
 };
 // A split launch runs one workgroup per CU on at most this many CUs (its
@@ -71,8 +72,8 @@ constexpr int64_t kSplitMaxCus = 256;
 // ... and gives each wavefront at least this many K steps.
 constexpr int64_t kSplitMinSteps = 2;
 // Largest split_workspace_bytes of any route: 256 workgroups x 2 pieces x
-// (128 rows x 64 tokens x 4 bytes).
-constexpr size_t kSplitMaxBytes = size_t(kSplitMaxCus) * 2 * 2 * 4 * 4096;
+// (256 rows x 64 tokens x 4 bytes), the LDS-fed shape.
+constexpr size_t kSplitMaxBytes = size_t(kSplitMaxCus) * 2 * 4 * 4 * 4096;
 // What the matrix-core kernels run for m >= 1 tokens on an n x k matrix
 // over `cus` compute units.
 GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus);

@@ -16,6 +16,9 @@
 #ifndef HYB_GEMM_SPLIT_COST
 #define HYB_GEMM_SPLIT_COST 30.0
 #endif
+#ifndef HYB_GEMM_LDS_SPLIT_ROUND
+#define HYB_GEMM_LDS_SPLIT_ROUND 0.39
+#endif
 
 namespace hyb {
 
@@ -75,6 +78,14 @@ bool gemv_preferred(const hyb_layout& L, int m) {
 namespace {
 
 constexpr double kSplitCost = HYB_GEMM_SPLIT_COST;
+// Cost of one round of the split LDS-fed 64-token shape on the scale of
+// kRound (register-fed 64 tokens x 128 rows: 0.29), for S K steps per tile.
+// Against the split register-fed shapes it grows with K: measured 0.37-0.44
+// at 64-80 K steps, 0.44-0.49 at 128, 0.46-0.56 at 224-448.
+double lds_split_round(int64_t steps) {
+  const double c = HYB_GEMM_LDS_SPLIT_ROUND + 0.0007 * double(steps - 64);
+  return c < HYB_GEMM_LDS_SPLIT_ROUND ? HYB_GEMM_LDS_SPLIT_ROUND : (c > 0.6 ? 0.6 : c);
+}
 
 struct Priced {
   GemmRoute r;
@@ -137,7 +148,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   };
   // The cheapest split launch of any register-fed shape (cost relative to
   // the 256-token LDS round, as kRound).
-  auto best_split = [&](double& cost) {
+  auto best_split = [&](double& cost, bool lds) {
     GemmRoute best{0, 0, 0, 0, 0};
     for (int i = 0; i < kNumShapes; ++i) {
       if ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
@@ -146,6 +157,19 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
         best = p.r;
         cost = p.rounds * kSplitRound[i];
       }
+    }
+    // Up to 128 tokens, the LDS-fed 64-token shape (256 rows on eight
+    // wavefronts) split the same way: per unit of work it is the cheaper
+    // kernel where its tiles fill the CUs (65536 x 4096 at 64 tokens: one
+    // round of it 83 us, against 105 us for two rounds of 64 tokens x 128
+    // rows; 17408 x 5120 at 64 and 128 tokens: 37 and 53 us against 41 and
+    // 57 us for the split register-fed shape).  Above 128 tokens it lost to
+    // the shapes priced here in every case measured (8192 x 28672 and 4096 x
+    // 14336 at 256 tokens by 9-10%, 14336 x 4096 at 256 by 13%).
+    const Priced lp = rx_priced(n, steps, m64, 4, 8, 4, cus);
+    if (lds && lp.r.kernel == kRouteSplit && (best.kernel == 0 || lp.rounds * lds_split_round(steps) < cost)) {
+      best = lp.r;
+      cost = lp.rounds * lds_split_round(steps);
     }
     return best;
   };
@@ -177,7 +201,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
       plain = 0.57;
     }
     double split = 0.0;
-    const GemmRoute s = best_split(split);
+    const GemmRoute s = best_split(split, true);
     return (s.kernel == kRouteSplit && split < plain) ? s : pick;
   }
   const int64_t gn = (n + 255) / 256;
@@ -204,7 +228,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
     }
   }
   double split = 0.0;
-  const GemmRoute s = best_split(split);
+  const GemmRoute s = best_split(split, false);
   if (s.kernel == kRouteSplit && split < rx_cost && split < best) return s;
   if (rx_best >= 0 && rx_cost < 0.9 * best) return rx(rx_best);
   if (c256 == best) return GemmRoute{kRouteLds, 16, 8, 4, 0};

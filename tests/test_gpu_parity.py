@@ -623,7 +623,7 @@ def test_gemm_small_matrices_above_128(config, index, m, route):
     assert_close(y, yref, s, what=f"gemm {mat.name} m={m}")
 
 
-@pytest.mark.parametrize("m", [8, 16, 64, 256, 2048])
+@pytest.mark.parametrize("m", [8, 16, 64, 128, 256, 2048])
 def test_gemm_qwen14b_full(m):
     """17408x5120, 64x64 tiles, 60% sparse tiles; M from 8 to 2048 through
     hyb_gemm and through the matrix-core entry point, every output against

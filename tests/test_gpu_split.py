@@ -1,9 +1,10 @@
-"""GPU parity of the split-K register-fed launch (k_gemm_split + the kernel
-that adds the partial tiles): every split shape the launcher uses, in every
-dtype, metadata kind and tile size, with ragged row and token blocks, the
-low-rank epilogue, corrupt tile indices, 16-bit outputs, the caller-held
-workspace of hyb_gemm_ws, and replays of a captured graph.  Every output
-against the oracle (same acceptance rule as test_gpu_parity)."""
+"""GPU parity of the split-K launches (k_gemm_split, the register-fed
+shapes, and k_gemm_lds_split, the LDS-fed 64-token shape, each followed by
+the kernel that adds its partial tiles): every split shape the launcher
+uses, in every dtype, metadata kind and tile size, with ragged row and token
+blocks, the low-rank epilogue, corrupt tile indices, 16-bit outputs, the
+caller-held workspace of hyb_gemm_ws, and replays of a captured graph.
+Every output against the oracle (same acceptance rule as test_gpu_parity)."""
 import numpy as np
 import pytest
 
@@ -16,8 +17,10 @@ from test_gpu_parity import (_torch, assert_close, dev, expect_route, note, orac
 pytestmark = pytest.mark.gpu
 
 # (n, k, b1, b2, m, dtype, meta) -> split shape (token blocks, wavefronts,
-# row groups) on a 256-CU device.  2112 rows leave the last 128-row block
-# half outside the matrix; 100, 90 and 70 tokens leave a ragged token block.
+# row groups) on a 256-CU device; row groups 4 is the LDS-fed shape.  2112
+# rows leave the last 128-row block half outside the matrix, 8256, 8320,
+# 16448 and 32832 the last 256-row block; 100, 90, 70, 60 and 49 tokens
+# leave a ragged token block.
 CASES = [
     ((256, 4096, 128, 128, 33, "bf16", "idx2"), (1, 8, 1)),
     ((192, 8192, 64, 128, 17, "f16", "mask8"), (1, 8, 1)),
@@ -30,7 +33,18 @@ CASES = [
     ((1088, 8192, 64, 128, 100, "f16", "idx2"), (4, 8, 1)),
     ((2048, 16384, 128, 128, 100, "f16", "idx2"), (4, 4, 2)),
     ((2112, 16384, 64, 128, 100, "bf16", "idx2"), (4, 4, 2)),
+    ((8256, 5120, 64, 64, 100, "bf16", "idx2"), (4, 8, 4)),
+    ((8320, 5120, 128, 128, 120, "f16", "mask8"), (4, 8, 4)),
+    ((8448, 6144, 256, 64, 100, "bf16", "mask8"), (4, 8, 4)),
+    ((16448, 4096, 64, 256, 64, "f16", "idx2"), (4, 8, 4)),
+    ((16512, 4096, 128, 128, 49, "bf16", "mask4"), (4, 8, 4)),
+    ((32832, 2048, 64, 128, 100, "bf16", "idx2"), (4, 8, 4)),
+    ((7616, 8192, 64, 64, 128, "f16", "mask4"), (4, 8, 4)),
+    ((15296, 8192, 64, 64, 60, "f16", "mask8"), (4, 8, 4)),
 ]
+
+# One product per split kernel for the checks below: (n, k, b, m) -> shape.
+KERNELS = [((2048, 16384, 128, 100), (4, 4, 2)), ((8320, 5120, 128, 100), (4, 8, 4))]
 
 
 def _case(n, k, b1, b2, m, dtype, meta):
@@ -52,7 +66,7 @@ def test_split_shapes_every_output(case, shape):
     P = pack_gpu(w, tmap, b1, b2, dtype, meta)
     expect_route(P, m, "split", *shape)
     need = hb.workspace_bytes(P, m)
-    assert 0 < need <= 16 << 20
+    assert 0 < need <= 32 << 20
     xt = upload(x, dtype)
     y = hb.gemm(P, xt)
     y_again = hb.gemm(P, xt)
@@ -68,18 +82,20 @@ def test_split_shapes_every_output(case, shape):
     assert_close(y_plain.cpu().numpy(), yref, s, what=f"unsplit {case}")
 
 
-def test_split_lowrank_and_bf16_out():
+@pytest.mark.parametrize("case,shape", [((2112, 16384, 64, 128, 100), (4, 4, 2)), ((8256, 5120, 64, 64, 100), (4, 8, 4))])
+def test_split_lowrank_and_bf16_out(case, shape):
     """The low-rank term is added by the piece that starts at K step 0, and
     the split tiles' sums are rounded once to a bf16 y."""
     torch = _torch()
-    n, k, b1, b2, m, rank = 2112, 16384, 64, 128, 100, 64
-    note("split lowrank + bf16 y")
+    n, k, b1, b2, m = case
+    rank = 64
+    note(f"split lowrank + bf16 y {case}")
     w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
     rng = np.random.default_rng(99)
     t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
     u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, "bf16")
     P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
-    expect_route(P, m, "split", 4, 4, 2)
+    expect_route(P, m, "split", *shape)
     xt, tt = upload(x, "bf16"), torch.from_numpy(t).to(dev())
     y = hb.gemm_lowrank(P, xt, tt, upload(u, "bf16"))
     y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=torch.bfloat16)), "bf16")
@@ -90,38 +106,43 @@ def test_split_lowrank_and_bf16_out():
     assert_close(y16, y0ref, s0, extra=np.abs(y0ref) * 2.0 ** -8 + 2.0 ** -133, what="split bf16 y")
 
 
-def test_split_skips_corrupt_tile_index():
+@pytest.mark.parametrize("case,shape", KERNELS)
+def test_split_skips_corrupt_tile_index(case, shape):
     """tidx entries naming slots outside the streams are skipped inside the
     split pieces too (the kernels' own bounds checks)."""
     torch = _torch()
-    n, k, b1, b2, m = 2048, 16384, 128, 128, 100
-    note("split corrupt tidx")
+    n, k, b, m = case
+    b1 = b2 = b
+    note(f"split corrupt tidx {case}")
     w, tmap, x = _case(n, k, b1, b2, m, "f16", "idx2")
     P = pack_gpu(w, tmap, b1, b2, "f16", "idx2")
-    expect_route(P, m, "split", 4, 4, 2)
+    expect_route(P, m, "split", *shape)
     tk = k // b2
     bad = P.tidx.cpu().numpy().copy()
-    t0, t1 = 3 * tk + 50, 9 * tk + tk - 1      # tile (3, 50) and tile (9, last)
+    c0 = tk // 3
+    t0, t1 = 3 * tk + c0, 9 * tk + tk - 1      # tile (3, tk / 3) and tile (9, last)
     bad[t0] = 1 << 30
     bad[t1] = -(1 << 30)
     P.tidx.copy_(torch.from_numpy(bad))
     y = hb.gemm(P, upload(x, "f16")).cpu().numpy()
     wp = oracle.prune(w, tmap, b1, b2)
-    wp[3 * b1:4 * b1, 50 * b2:51 * b2] = 0
+    wp[3 * b1:4 * b1, c0 * b2:(c0 + 1) * b2] = 0
     wp[9 * b1:10 * b1, (tk - 1) * b2:tk * b2] = 0
     yref, s = oracle.ref_matmul(wp, x, "f16")
     assert_close(y, yref, s, what="split corrupt tidx")
 
 
-def test_split_in_a_captured_graph():
+@pytest.mark.parametrize("case,shape", KERNELS)
+def test_split_in_a_captured_graph(case, shape):
     """A split product captured into a graph: each of three replays, with
     eager work and synchronisations between them, gives the eager bits."""
     torch = _torch()
-    n, k, b1, b2, m = 2048, 16384, 128, 128, 100
-    note("split graph replays")
+    n, k, b, m = case
+    b1 = b2 = b
+    note(f"split graph replays {case}")
     w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
     P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
-    expect_route(P, m, "split", 4, 4, 2)
+    expect_route(P, m, "split", *shape)
     xt = upload(x, "bf16")
     eager = hb.gemm(P, xt)
     y = torch.empty_like(eager)
