@@ -262,7 +262,7 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
  * the matrix has fewer than two 16-row slabs per compute unit), larger m
  * the matrix-core kernels.  Where those split K over workgroups
  * (HYB_KERNEL_SPLIT of hyb_gemm_shape) they keep partial sums in a
- * workspace that the library allocates (hipMalloc, 32 MiB) at the first
+ * workspace that the library allocates (hipMalloc, 64 MiB) at the first
  * such launch on a (device, stream) pair and holds until the process ends;
  * launches on one stream share it, so concurrent calls on different
  * streams stay safe.  Nothing is allocated on a stream that is being
@@ -290,7 +290,7 @@ hyb_status hyb_gemm_ws(const hyb_layout* layout, const hyb_packed* w, const void
 /* For callers that cannot allocate device memory (code under graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): hyb_gemm with no
  * allocation at all.  Where hyb_gemm would split K it uses a scratch array
- * that the library holds in static device memory, 32 MiB per GPU from the
+ * that the library holds in static device memory, 64 MiB per GPU from the
  * library's load until the process ends, instead of a workspace (its
  * address is looked up once per device, at the first call there).  The
  * array keeps the last call's contents and needs no clearing; all calls on
@@ -319,7 +319,7 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
  * HYB_KERNEL_REGISTER (k_gemm_rx, wavefronts splitting K), HYB_KERNEL_LDS
  * (k_gemm_lds, 4 row groups) or HYB_KERNEL_SPLIT (k_gemm_split with 1-2
  * row groups, the register-fed shape, or k_gemm_lds_split with 4, the
- * LDS-fed 64-token shape: the (tile, K step) units dealt out evenly over a
+ * LDS-fed 64- or 128-token shape: the (tile, K step) units dealt out evenly over a
  * fixed number of workgroups, partial tiles added by a second kernel in a
  * fixed order; it needs a workspace, which hyb_gemm holds per device and
  * stream).  Errors: as the layout checks of hyb_gemm; out NULL ->

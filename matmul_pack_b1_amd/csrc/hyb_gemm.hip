@@ -1004,7 +1004,7 @@ hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const Gemm
   const int64_t gm = (int64_t(m) + 16 * MB - 1) / (16 * MB);
   const int64_t gn = (L.n + 255) / 256;
   if (gn * gm >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
-  if constexpr (MB == 4) {
+  if constexpr (MB == 4 || MB == 8) {
     if (sp.groups > 0) {
       // K split over sp.groups workgroups in all, sp.groups / gm per token
       // block (workspace checked by the caller, as for gemm_rx_go)

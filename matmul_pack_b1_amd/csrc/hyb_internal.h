@@ -72,8 +72,8 @@ constexpr int64_t kSplitMaxCus = 256;
 // ... and gives each wavefront at least this many K steps.
 constexpr int64_t kSplitMinSteps = 2;
 // Largest split_workspace_bytes of any route: 256 workgroups x 2 pieces x
-// (256 rows x 64 tokens x 4 bytes), the LDS-fed shape.
-constexpr size_t kSplitMaxBytes = size_t(kSplitMaxCus) * 2 * 4 * 4 * 4096;
+// (256 rows x 128 tokens x 4 bytes), the LDS-fed 128-token shape.
+constexpr size_t kSplitMaxBytes = size_t(kSplitMaxCus) * 2 * 4 * 8 * 4096;
 // What the matrix-core kernels run for m >= 1 tokens on an n x k matrix
 // over `cus` compute units.
 GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus);

@@ -86,6 +86,18 @@ double lds_split_round(int64_t steps) {
   const double c = HYB_GEMM_LDS_SPLIT_ROUND + 0.0007 * double(steps - 64);
   return c < HYB_GEMM_LDS_SPLIT_ROUND ? HYB_GEMM_LDS_SPLIT_ROUND : (c > 0.6 ? 0.6 : c);
 }
+// The same for the split LDS-fed 128-token shape.  Up to 128 tokens it is
+// priced against the split register-fed shapes (0.47: 8192 x 28672 at 128
+// tokens 103 us against 119, 28672 x 8192 at 128 112 against 124 for the
+// LDS 64-token round); above 128 against the LDS rounds, growing with K
+// (0.63 at 64 K steps to 0.78 at 448: 17408 x 5120 at 256 tokens 79 us
+// against 93 for the 128-token round, 8192 x 28672 at 256 and 512 tokens
+// 167 and 291 us against 187 and 367).
+double lds8_split_round(int64_t steps, bool up_to_128) {
+  if (up_to_128) return 0.47;
+  const double c = 0.63 + 0.0004 * double(steps - 64);
+  return c < 0.63 ? 0.63 : (c > 0.8 ? 0.8 : c);
+}
 
 struct Priced {
   GemmRoute r;
@@ -148,7 +160,7 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
   };
   // The cheapest split launch of any register-fed shape (cost relative to
   // the 256-token LDS round, as kRound).
-  auto best_split = [&](double& cost, bool lds) {
+  auto best_split = [&](double& cost, bool up_to_128) {
     GemmRoute best{0, 0, 0, 0, 0};
     for (int i = 0; i < kNumShapes; ++i) {
       if ((m64 + 16 * kShapes[i][0] - 1) / (16 * kShapes[i][0]) > 65535) continue;
@@ -167,9 +179,20 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
     // the shapes priced here in every case measured (8192 x 28672 and 4096 x
     // 14336 at 256 tokens by 9-10%, 14336 x 4096 at 256 by 13%).
     const Priced lp = rx_priced(n, steps, m64, 4, 8, 4, cus);
-    if (lds && lp.r.kernel == kRouteSplit && (best.kernel == 0 || lp.rounds * lds_split_round(steps) < cost)) {
+    if (up_to_128 && lp.r.kernel == kRouteSplit && (best.kernel == 0 || lp.rounds * lds_split_round(steps) < cost)) {
       best = lp.r;
       cost = lp.rounds * lds_split_round(steps);
+    }
+    // From 97 tokens (a 128-token block at least 3/4 full), the LDS-fed
+    // 128-token shape split the same way: per K step it does twice the
+    // 64-token shape's products for 1.3x its loads.
+    if (m64 > 96) {
+      const Priced lp8 = rx_priced(n, steps, m64, 8, 8, 4, cus);
+      const double c8 = lp8.rounds * lds8_split_round(steps, up_to_128);
+      if (lp8.r.kernel == kRouteSplit && (best.kernel == 0 || c8 < cost)) {
+        best = lp8.r;
+        cost = c8;
+      }
     }
     return best;
   };

@@ -603,15 +603,16 @@ def test_gemm_lds_shapes_random(n, m, b1, b2, dtype, meta):
 
 @pytest.mark.parametrize("config,index,m,route", [(3, 1, 384, ("register", 2, 8, 1)),
                                                   (3, 0, 160, ("register", 2, 4, 2)),
-                                                  (3, 6, 256, ("split", 4, 4, 2))])
+                                                  (3, 6, 256, ("split", 8, 8, 4))])
 def test_gemm_small_matrices_above_128(config, index, m, route):
     """Few 256-row blocks above 128 tokens: the launcher prices every
     register-fed shape, plain and split, against the LDS shapes and, on a
     256-CU device, runs 32 tokens x 64 rows on eight wavefronts for the 1024
     x 4096 k projection at 384 tokens, 32 tokens x 128 rows on four
-    wavefronts for the 4096-row q projection at 160 tokens (ragged), and 64
-    tokens x 128 rows split over 256 workgroups for the 4096 x 14336 down
-    projection at 256 tokens.  Every output against the oracle."""
+    wavefronts for the 4096-row q projection at 160 tokens (ragged), and the
+    LDS-fed 128-token x 256-row shape split over 256 workgroups for the 4096
+    x 14336 down projection at 256 tokens.  Every output against the
+    oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(config, index)
     note(f"gemm small matrix {mat.name} m={m}")
@@ -663,15 +664,15 @@ def test_gemm_8b_up_shapes(m, tb):
 
 
 @pytest.mark.parametrize("m,route", [(64, ("split", 4, 4, 2)), (160, ("split", 4, 4, 2)),
-                                     (256, ("register", 4, 4, 2)), (512, ("lds", 4, 8, 4))])
+                                     (256, ("split", 8, 8, 4)), (512, ("split", 8, 8, 4))])
 def test_gemm_tall_70b(m, route):
     """8192x28672 (32 blocks of 256 rows), 128x128 tiles in a checkerboard:
-    up to a few hundred tokens every LDS shape leaves most CUs of a 256-CU
-    device idle and the launcher runs the register-fed shape (128 rows by 64
-    tokens, K split over four wavefronts): at 64 and 160 tokens (ragged)
-    with K also split across 256 workgroups, at 256 tokens (256 tiles, one
-    per CU) plain; at 512 it runs the 64-token LDS shape.  Every output
-    against the oracle."""
+    up to a few hundred tokens every plain LDS shape leaves most CUs of a
+    256-CU device idle.  At 64 and 160 tokens (ragged) the launcher runs the
+    register-fed shape (128 rows by 64 tokens, K split over four wavefronts
+    and across 256 workgroups); at 256 and 512 tokens the LDS-fed 128-token
+    shape with K split across 256 workgroups (2 and 4 token blocks).  Every
+    output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 5)
     note(f"gemm 70b tall m={m}")
@@ -683,13 +684,12 @@ def test_gemm_tall_70b(m, route):
     assert_close(y, yref, s, what=f"gemm tall m={m}")
 
 
-@pytest.mark.parametrize("m,route", [(80, ("split", 3, 4, 2)), (128, ("lds", 4, 8, 4))])
+@pytest.mark.parametrize("m,route", [(80, ("split", 3, 4, 2)), (128, ("split", 8, 8, 4))])
 def test_gemm_wide_70b(m, route):
     """28672x8192 (128x128 tiles, checkerboard): at 80 tokens (ragged) the
-    launcher splits 48-token x 128-row tiles over 256 workgroups; at 128 the
-    register-fed shapes would need two rounds on a 256-CU device and the
-    64-token LDS shape, 224 workgroups, fits in one.  Every output against
-    the oracle."""
+    launcher splits 48-token x 128-row tiles over 256 workgroups; at 128 it
+    splits the 112 tiles of the LDS-fed 128-token x 256-row shape over 256
+    workgroups.  Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 2)
     note(f"gemm 70b wide m={m}")
