@@ -546,10 +546,13 @@ def kernel_text(hb, layout, m):
     if sh["kernel"] == "decode":
         return f"k_gemv ({sh['waves']} wavefronts per 16-row slab)"
     lds_split = sh["kernel"] == "split" and sh["row_groups"] == 4
-    name = {"register": "k_gemm_rx", "lds": "k_gemm_lds",
-            "split": "k_gemm_lds_split + k_gemm_lds_split_sum" if lds_split else "k_gemm_split + k_gemm_split_sum"}[sh["kernel"]]
+    lds_parts = lds_split and sh["token_blocks"] >= 12
+    split_name = ("k_gemm_lds_parts + k_gemm_lds_parts_sum" if lds_parts else
+                  "k_gemm_lds_split + k_gemm_lds_split_sum" if lds_split else "k_gemm_split + k_gemm_split_sum")
+    name = {"register": "k_gemm_rx", "lds": "k_gemm_lds", "split": split_name}[sh["kernel"]]
     split = {"register": ", wavefronts splitting K",
-             "split": (", K split across one workgroup per CU" if lds_split
+             "split": (", K cut into equal parts, one per workgroup" if lds_parts else
+                       ", K split across one workgroup per CU" if lds_split
                        else ", wavefronts splitting K, K also split across one workgroup per CU"),
              "lds": ""}[sh["kernel"]]
     return (f"{name} ({64 * sh['row_groups']}-row x {16 * sh['token_blocks']}-token workgroups on "

@@ -318,11 +318,13 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
  * out[1] = out[3] = 0, out[2] its wavefronts per 16-row slab),
  * HYB_KERNEL_REGISTER (k_gemm_rx, wavefronts splitting K), HYB_KERNEL_LDS
  * (k_gemm_lds, 4 row groups) or HYB_KERNEL_SPLIT (k_gemm_split with 1-2
- * row groups, the register-fed shape, or k_gemm_lds_split with 4, the
- * LDS-fed 64- or 128-token shape: the (tile, K step) units dealt out evenly over a
- * fixed number of workgroups, partial tiles added by a second kernel in a
- * fixed order; it needs a workspace, which hyb_gemm holds per device and
- * stream).  Errors: as the layout checks of hyb_gemm; out NULL ->
+ * row groups, the register-fed shape, or k_gemm_lds_split with 4 and 4 or
+ * 8 token blocks, the LDS-fed 64- or 128-token shape: the (tile, K step)
+ * units dealt out evenly over a fixed number of workgroups; or
+ * k_gemm_lds_parts with 4 row groups and 12 or 16 token blocks, the 192- or
+ * 256-token LDS tile with K cut into equal parts, one per workgroup; partial
+ * tiles added by a second kernel in a fixed order; it needs a workspace,
+ * which hyb_gemm holds per device and stream).  Errors: as the layout checks of hyb_gemm; out NULL ->
  * HYB_ERR_INVALID_ARG; m < 1 -> HYB_ERR_SHAPE. */
 enum { HYB_KERNEL_DECODE = 1, HYB_KERNEL_REGISTER = 2, HYB_KERNEL_LDS = 3, HYB_KERNEL_SPLIT = 4 };
 hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out);

@@ -989,6 +989,70 @@ __global__ __launch_bounds__(256) void k_gemm_lds_split_sum(const float* __restr
   store_row4(y, d, m, int64_t(n0) + sl * 16 + (lane >> 4) * 4, s, y_vec_ok(y, d));
 }
 
+
+// The 256-row LDS tile with K cut into `parts` equal parts, one workgroup
+// per (tile, part): part p of tile (nb, mbk) covers K steps
+// [p S / parts, (p + 1) S / parts) and writes its partial outputs to
+// workspace slot w = (nb * parts + p) * gm + mbk, each wavefront its own.
+// With one piece per workgroup no state lives across pieces, so the larger
+// tiles keep the plain kernel's registers.  Logical ids are XCD-major (as in
+// k_gemm_split): the gm token blocks of one (row block, part) read the same
+// weights at the same K steps on one XCD.
+template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_lds_parts(const uint4* __restrict__ dense,
+                                                        const uint4* __restrict__ val,
+                                                        const uint16_t* __restrict__ meta,
+                                                        const int32_t* __restrict__ tidx,
+                                                        const uint16_t* __restrict__ x, GemmDims d, int32_t gm,
+                                                        int32_t steps, int32_t parts, float* __restrict__ ws) {
+  using Cfg = GemmLdsCfg<B2, MB, STAGES, WAVES>;
+  constexpr int MBW = Cfg::kMBW;
+  constexpr int kWave = 4 * MBW * 64 * 4;     // floats of one wavefront's outputs
+  constexpr int kPart = WAVES * kWave;        // floats of one piece (256 rows x 16 MB tokens)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t G = int32_t(gridDim.x), L = int32_t(blockIdx.x);
+  const int32_t xcd = L % kSplitXcds, per = G / kSplitXcds, extra = G % kSplitXcds;
+  const int32_t w = xcd * per + (xcd < extra ? xcd : extra) + L / kSplitXcds;
+  const int32_t r = w / gm, mbk = w - r * gm;
+  const int32_t nb = r / parts, part = r - nb * parts;
+  const int32_t k0 = int32_t(int64_t(part) * steps / parts), k1 = int32_t(int64_t(part + 1) * steps / parts);
+  f32x4_t acc[4][MBW];
+  lds_piece<B2, DT, META, MB, STAGES, WAVES>(dense, val, meta, tidx, x, d, nb, mbk, k0, k1, acc);
+  const int32_t n0 = nb * 256 + (wave % 4) * 64;
+  if (k0 == 0 && d.rank > 0 && n0 < d.n) lr_block<DT, 4, MBW>(acc, d, n0, mbk * 16 * MB + (wave / 4) * MBW * 16, lane);
+  float* out = ws + int64_t(w) * kPart + wave * kWave;
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+      *reinterpret_cast<f32x4_t*>(out + ((sl * MBW + mb) * 64 + lane) * 4) = acc[sl][mb];
+}
+
+// Adds the `parts` partial tiles of k_gemm_lds_parts in part order and
+// stores the outputs; float4 f of a piece as in k_gemm_lds_split_sum.
+template <int MB, int WAVES>
+__global__ __launch_bounds__(256) void k_gemm_lds_parts_sum(const float* __restrict__ ws, void* __restrict__ y,
+                                                            GemmDims d, int32_t gm, int32_t parts) {
+  constexpr int MBW = MB / (WAVES / 4);
+  constexpr int kVec = WAVES * 4 * MBW * 64;  // float4 per piece
+  constexpr int kBlocks = kVec / 256;
+  const int32_t t = int32_t(blockIdx.x) / kBlocks;
+  const int32_t nb = t / gm, mt = t - nb * gm;
+  const int f = (int(blockIdx.x) % kBlocks) * 256 + int(threadIdx.x);
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(ws) + (int64_t(nb) * parts * gm + mt) * kVec + f;
+  f32x4_t s = __builtin_nontemporal_load(src);
+  for (int32_t p = 1; p < parts; ++p) s += __builtin_nontemporal_load(src + int64_t(p) * gm * kVec);
+  const int lane = f & 63;
+  const int mb = (f >> 6) % MBW;
+  const int sl = ((f >> 6) / MBW) & 3;
+  const int wave = (f >> 6) / (4 * MBW);
+  const int32_t n0 = nb * 256 + (wave % 4) * 64;
+  const int64_t m = int64_t(mt) * 16 * MB + ((wave / 4) * MBW + mb) * 16 + (lane & 15);
+  if (m >= d.m || n0 >= d.n) return;
+  store_row4(y, d, m, int64_t(n0) + sl * 16 + (lane >> 4) * 4, s, y_vec_ok(y, d));
+}
+
 }  // namespace
 
 
@@ -1025,6 +1089,24 @@ hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const Gemm
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((k_gemm_lds_split_sum<MB, WAVES>), dim3(unsigned(gn * gm * (4 * MB))), dim3(256), 0, s,
                          static_cast<const float*>(sp.ws), q.y, d, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (MB == 12 || MB == 16) {
+    if (sp.groups > 0) {
+      // K cut into sp.groups / (gn gm) equal parts per tile (the route gives
+      // a multiple of the tile count; workspace checked by the caller)
+      const int64_t steps = int64_t(d.tiles_k) * (B2 / 64), tiles = gn * gm;
+      const int64_t parts = sp.groups / tiles;
+      if (parts < 2 || parts * tiles != sp.groups || steps < parts || tiles * parts >= (int64_t(1) << 31))
+        return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((k_gemm_lds_parts<B2, DT, META, MB, STAGES, WAVES>), dim3(unsigned(tiles * parts)),
+                         dim3(64 * WAVES), size_t(Cfg::kBytes), s, q.dense, q.val, q.meta, q.tidx, q.x, d,
+                         int32_t(gm), int32_t(steps), int32_t(parts), sp.ws);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((k_gemm_lds_parts_sum<MB, WAVES>), dim3(unsigned(tiles * (4 * MB))), dim3(256), 0, s,
+                         static_cast<const float*>(sp.ws), q.y, d, int32_t(gm), int32_t(parts));
       return hipGetLastError();
     }
   }

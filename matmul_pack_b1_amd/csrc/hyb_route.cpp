@@ -130,7 +130,11 @@ Priced rx_priced(int64_t n, int64_t steps, int64_t m, int mb, int waves, int rg,
 }  // namespace
 
 size_t split_workspace_bytes(const GemmRoute& r) {
-  return r.kernel == kRouteSplit ? size_t(r.groups) * 2 * size_t(r.rg) * size_t(r.mb) * 4096 : 0;
+  if (r.kernel != kRouteSplit) return 0;
+  // two partial tiles per workgroup of a stream-K range; one per workgroup
+  // of the 192- and 256-token LDS tiles, whose K is cut into equal parts
+  const size_t pieces = (r.rg == 4 && r.mb >= 12) ? 1 : 2;
+  return size_t(r.groups) * pieces * size_t(r.rg) * size_t(r.mb) * 4096;
 }
 
 GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
@@ -192,6 +196,27 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
       if (lp8.r.kernel == kRouteSplit && (best.kernel == 0 || c8 < cost)) {
         best = lp8.r;
         cost = c8;
+      }
+    }
+    // Above 128 tokens, the 192- and 256-token LDS tiles with K cut into
+    // equal parts (k_gemm_lds_parts), when their tiles fill at most half the
+    // CUs.  Priced by time: each workgroup walks S / parts K steps at 1.45 or
+    // 1.75 us a step (measured at full occupancy), plus a fixed 25 us and
+    // 0.05 us per K step of the tile (the sum kernel, the pieces' pipeline
+    // starts); one round of the 256-token LDS tile costs about 1.75 us per K
+    // step, which converts the time to this scale.
+    if (!up_to_128) {
+      for (const int mb : {12, 16}) {
+        const int64_t gm = (m64 + 16 * mb - 1) / (16 * mb), tiles = ((n + 255) / 256) * gm;
+        int64_t parts = cus / tiles;
+        if (parts > steps / 16) parts = steps / 16;
+        if (parts < 2 || tiles * parts > kSplitMaxCus) continue;
+        const double t_us = (mb == 12 ? 1.45 : 1.75) * double(steps) / double(parts) + 25.0 + 0.05 * double(steps);
+        const double c = t_us / (1.75 * double(steps));
+        if (best.kernel == 0 || c < cost) {
+          best = GemmRoute{kRouteSplit, mb, 8, 4, int32_t(tiles * parts)};
+          cost = c;
+        }
       }
     }
     return best;

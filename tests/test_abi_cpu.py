@@ -333,7 +333,7 @@ ROUTES = [
     ((17408, 5120, 64, 128), ("split", 8, 8, 4)),
     ((8256, 5120, 64, 100), ("split", 4, 8, 4)),         # last 256-row block a quarter full
     ((28672, 8192, 128, 64), ("register", 4, 4, 2)),     # one round of 224 tiles: no split
-    ((4096, 14336, 128, 256), ("split", 8, 8, 4)),       # 32 LDS 128-token tiles, K split 8 ways
+    ((4096, 14336, 128, 256), ("split", 16, 8, 4)),      # 16 LDS 256-token tiles, K cut in 14 parts
     ((4096, 14336, 128, 160), ("split", 3, 4, 2)),       # register-fed split
     ((14336, 4096, 128, 64), ("register", 2, 4, 2)),
     ((14336, 4096, 128, 128), ("register", 4, 4, 2)),    # 224 tiles fill the CUs well enough
@@ -345,14 +345,17 @@ ROUTES = [
     ((8192, 28672, 128, 128), ("split", 8, 8, 4)),
     ((1024, 4096, 128, 32), ("split", 1, 8, 1)),
     ((17408, 5120, 64, 2048), ("lds", 12, 8, 4)),
-    ((14336, 4096, 128, 200), ("lds", 4, 8, 4)),
+    ((14336, 4096, 128, 200), ("split", 16, 8, 4)),
+    ((14336, 4096, 128, 160), ("split", 12, 8, 4)),      # 192-token tiles, K cut in 4 parts
     ((14336, 4096, 128, 300), ("lds", 8, 8, 4)),
     ((14336, 4096, 128, 700), ("lds", 12, 8, 4)),
     ((14336, 4096, 128, 1024), ("lds", 16, 8, 4)),
     ((14336, 4096, 128, 2048), ("lds", 16, 8, 4)),
-    ((8192, 28672, 128, 256), ("split", 8, 8, 4)),       # few 256-row blocks
-    ((8192, 28672, 128, 512), ("split", 8, 8, 4)),
-    ((8192, 28672, 128, 1024), ("lds", 8, 8, 4)),        # 256 tiles of 128 tokens: one full round
+    ((8192, 28672, 128, 256), ("split", 16, 8, 4)),      # few 256-row blocks
+    ((8192, 28672, 128, 384), ("split", 12, 8, 4)),
+    ((8192, 28672, 128, 512), ("split", 16, 8, 4)),
+    ((8192, 28672, 128, 1024), ("split", 16, 8, 4)),     # 128 256-token tiles, K cut in halves
+    ((8192, 28672, 128, 2048), ("lds", 16, 8, 4)),       # 256 tiles of 256 tokens: one full round
     ((4096, 4096, 128, 160), ("register", 2, 4, 2)),
     ((1024, 4096, 128, 384), ("register", 2, 8, 1)),
     ((8192, 256, 64, 1024), ("lds", 8, 8, 4)),
@@ -370,8 +373,8 @@ def test_gemm_routes(case, expect):
 
 
 def test_split_workspace_sizes(L):
-    """hyb_gemm_workspace_size: 2 pieces x (rows x tokens x 4 bytes) per
-    workgroup of a split route, 0 for every other route and for m = 0;
+    """hyb_gemm_workspace_size: 2 pieces (1 for the K-parts routes) x (rows x
+    tokens x 4 bytes) per workgroup of a split route, 0 for every other route and for m = 0;
     never above the 64 MiB the library holds per stream."""
     for (n, k, b, m), expect in ROUTES:
         lay = _layout(n, k, b)
@@ -379,7 +382,10 @@ def test_split_workspace_sizes(L):
         assert L.hyb_gemm_workspace_size(ctypes.byref(lay), m, ctypes.byref(size)) == 0
         if expect[0] == "split":
             _, mb, _, rg = expect
-            tiles_per_group = 2 * (64 * rg) * (16 * mb) * 4
+            # two partial tiles per stream-K workgroup, one per workgroup of
+            # the 192- and 256-token LDS tiles (K cut into equal parts)
+            pieces = 1 if (rg == 4 and mb >= 12) else 2
+            tiles_per_group = pieces * (64 * rg) * (16 * mb) * 4
             assert size.value > 0 and size.value % tiles_per_group == 0, (n, k, m, size.value)
             assert size.value // tiles_per_group <= 256
             assert size.value <= 64 << 20

@@ -603,15 +603,15 @@ def test_gemm_lds_shapes_random(n, m, b1, b2, dtype, meta):
 
 @pytest.mark.parametrize("config,index,m,route", [(3, 1, 384, ("register", 2, 8, 1)),
                                                   (3, 0, 160, ("register", 2, 4, 2)),
-                                                  (3, 6, 256, ("split", 8, 8, 4))])
+                                                  (3, 6, 256, ("split", 16, 8, 4))])
 def test_gemm_small_matrices_above_128(config, index, m, route):
     """Few 256-row blocks above 128 tokens: the launcher prices every
     register-fed shape, plain and split, against the LDS shapes and, on a
     256-CU device, runs 32 tokens x 64 rows on eight wavefronts for the 1024
     x 4096 k projection at 384 tokens, 32 tokens x 128 rows on four
     wavefronts for the 4096-row q projection at 160 tokens (ragged), and the
-    LDS-fed 128-token x 256-row shape split over 256 workgroups for the 4096
-    x 14336 down projection at 256 tokens.  Every output against the
+    LDS-fed 256-token x 256-row tile with K cut into 14 parts for the 4096 x
+    14336 down projection at 256 tokens.  Every output against the
     oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(config, index)
@@ -642,37 +642,39 @@ def test_gemm_qwen14b_full(m):
     assert_close(y2, yref, s, what=f"gemm_mfma m={m}")
 
 
-@pytest.mark.parametrize("m,tb", [(200, 4), (256, 4), (300, 8), (512, 8), (700, 12), (1024, 16)])
-def test_gemm_8b_up_shapes(m, tb):
+@pytest.mark.parametrize("m,route", [(160, ("split", 12, 8, 4)), (200, ("split", 16, 8, 4)), (256, ("split", 16, 8, 4)),
+                                     (300, ("lds", 8, 8, 4)), (512, ("lds", 8, 8, 4)), (700, ("lds", 12, 8, 4)),
+                                     (1024, ("lds", 16, 8, 4))])
+def test_gemm_8b_up_shapes(m, route):
     """14336x4096, 128x128 tiles, 70% sparse tiles.  From 129 tokens the
-    launcher picks one of four workgroup shapes (256, 192, 128 or 64 tokens
-    per workgroup) by the number of workgroup rounds on the device; on a
-    256-CU device these token counts select the 64-token shape (200 with a
-    ragged last block, 256), the 128-token shape (300 ragged, 512), the
-    192-token shape (700 ragged) and the 256-token shape (1024).  The
-    17408-row matrix at 2048 tokens (test_gemm_qwen14b_full) also runs
-    the 192-token shape.  Every output against the oracle."""
+    launcher picks among the 256-row LDS tiles (256, 192, 128 or 64 tokens
+    per workgroup); on a 256-CU device these token counts select the
+    192-token tile with K cut into 4 parts (160, ragged), the 256-token tile
+    with K cut into 2 parts (200 ragged, 256), and one round of plain tiles:
+    128 tokens (300 ragged, 512), 192 (700 ragged) and 256 (1024).  The
+    17408-row matrix at 2048 tokens (test_gemm_qwen14b_full) also runs the
+    192-token tile.  Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(2, 0)
     note(f"gemm 8b up m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
-    expect_route(P, m, "lds", token_blocks=tb)
+    expect_route(P, m, *route)
     yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, upload(x, mat.dtype)).cpu().numpy()
     assert_close(y, yref, s, what=f"gemm m={m}")
 
 
-@pytest.mark.parametrize("m,route", [(64, ("split", 4, 4, 2)), (160, ("split", 4, 4, 2)),
-                                     (256, ("split", 8, 8, 4)), (512, ("split", 8, 8, 4))])
+@pytest.mark.parametrize("m,route", [(64, ("split", 4, 4, 2)), (160, ("split", 12, 8, 4)),
+                                     (256, ("split", 16, 8, 4)), (512, ("split", 16, 8, 4))])
 def test_gemm_tall_70b(m, route):
     """8192x28672 (32 blocks of 256 rows), 128x128 tiles in a checkerboard:
     up to a few hundred tokens every plain LDS shape leaves most CUs of a
-    256-CU device idle.  At 64 and 160 tokens (ragged) the launcher runs the
-    register-fed shape (128 rows by 64 tokens, K split over four wavefronts
-    and across 256 workgroups); at 256 and 512 tokens the LDS-fed 128-token
-    shape with K split across 256 workgroups (2 and 4 token blocks).  Every
-    output against the oracle."""
+    256-CU device idle.  At 64 tokens the launcher runs the register-fed
+    shape (128 rows by 64 tokens, K split over four wavefronts and across
+    256 workgroups); at 160 (ragged) the 192-token LDS tile, at 256 and 512
+    the 256-token one (1 and 2 token blocks), each with K cut into 8 or 4
+    equal parts over 256 workgroups.  Every output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(4, 5)
     note(f"gemm 70b tall m={m}")

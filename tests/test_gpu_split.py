@@ -1,5 +1,7 @@
 """GPU parity of the split-K launches (k_gemm_split, the register-fed
-shapes, and k_gemm_lds_split, the LDS-fed 64- and 128-token shapes, each followed by
+shapes; k_gemm_lds_split, the LDS-fed 64- and 128-token shapes; and
+k_gemm_lds_parts, the 192- and 256-token LDS tiles with K cut into equal
+parts; each followed by
 the kernel that adds its partial tiles): every split shape the launcher
 uses, in every dtype, metadata kind and tile size, with ragged row and token
 blocks, the low-rank epilogue, corrupt tile indices, 16-bit outputs, the
@@ -19,9 +21,10 @@ pytestmark = pytest.mark.gpu
 # (n, k, b1, b2, m, dtype, meta) -> split shape (token blocks, wavefronts,
 # row groups) on a 256-CU device; row groups 4 is the LDS-fed shape.  2112
 # rows leave the last 128-row block half outside the matrix, 8256, 8320,
-# 16448, 32832, 2880, 3008, 3200, 4288, 4416, 2176 and 2496 the last 256-row
-# block; 100, 90, 70, 60, 49, 120, 200, 300 and 450 tokens leave a ragged
-# token block (128-token shape: 2, 3 and 4 token blocks at 200-450).
+# 16448, 32832, 2880, 3008, 3200, 8256, 10816, 11136, 2496, 3392, 3136,
+# 2112, 2432, 3904, 4032 and 1984 the last 256-row block; 100, 90, 70, 60,
+# 49, 120, 150, 180, 200, 300, 400, 450 and 500 tokens leave a ragged token
+# block (2 to 4 token blocks at 300-500).
 CASES = [
     ((256, 4096, 128, 128, 33, "bf16", "idx2"), (1, 8, 1)),
     ((192, 8192, 64, 128, 17, "f16", "mask8"), (1, 8, 1)),
@@ -46,15 +49,25 @@ CASES = [
     ((3008, 16384, 64, 128, 120, "f16", "mask4"), (8, 8, 4)),
     ((3200, 16384, 128, 128, 128, "bf16", "mask8"), (8, 8, 4)),
     ((3840, 12288, 256, 64, 128, "bf16", "idx2"), (8, 8, 4)),
-    ((4288, 16384, 64, 256, 200, "f16", "idx2"), (8, 8, 4)),
-    ((4416, 16384, 64, 64, 300, "bf16", "mask4"), (8, 8, 4)),
-    ((2176, 16384, 64, 128, 450, "bf16", "idx2"), (8, 8, 4)),
-    ((2496, 12288, 64, 64, 450, "f16", "mask8"), (8, 8, 4)),
+    ((8256, 8192, 64, 256, 300, "f16", "idx2"), (8, 8, 4)),
+    ((10816, 5120, 64, 64, 300, "bf16", "mask4"), (8, 8, 4)),
+    ((11136, 8192, 64, 128, 400, "bf16", "idx2"), (8, 8, 4)),
+    ((2496, 12288, 64, 64, 450, "f16", "mask8"), (16, 8, 4)),
+    ((3392, 16384, 64, 64, 200, "bf16", "idx2"), (16, 8, 4)),
+    ((3136, 16384, 64, 128, 256, "f16", "mask4"), (16, 8, 4)),
+    ((2112, 16384, 64, 256, 500, "bf16", "mask8"), (16, 8, 4)),
+    ((2432, 12288, 128, 64, 400, "f16", "idx2"), (16, 8, 4)),
+    ((3072, 16384, 256, 256, 400, "bf16", "mask4"), (16, 8, 4)),
+    ((3904, 16384, 64, 64, 150, "bf16", "idx2"), (12, 8, 4)),
+    ((4032, 16384, 64, 128, 180, "f16", "mask8"), (12, 8, 4)),
+    ((3008, 16384, 64, 64, 300, "bf16", "mask4"), (12, 8, 4)),
+    ((1984, 12288, 64, 128, 500, "f16", "idx2"), (12, 8, 4)),
+    ((4096, 16384, 256, 128, 300, "bf16", "mask8"), (12, 8, 4)),
 ]
 
 # One product per split kernel for the checks below: (n, k, b, m) -> shape.
 KERNELS = [((2048, 16384, 128, 100), (4, 4, 2)), ((8320, 5120, 128, 100), (4, 8, 4)),
-           ((3200, 16384, 128, 120), (8, 8, 4))]
+           ((3200, 16384, 128, 120), (8, 8, 4)), ((3136, 16384, 64, 256), (16, 8, 4))]
 
 
 def _case(n, k, b1, b2, m, dtype, meta):
@@ -93,7 +106,9 @@ def test_split_shapes_every_output(case, shape):
 
 
 @pytest.mark.parametrize("case,shape", [((2112, 16384, 64, 128, 100), (4, 4, 2)), ((8256, 5120, 64, 64, 100), (4, 8, 4)),
-                                        ((4288, 16384, 64, 128, 200), (8, 8, 4))])
+                                        ((8256, 8192, 64, 128, 300), (8, 8, 4)),
+                                        ((3904, 16384, 64, 128, 150), (12, 8, 4)),
+                                        ((3392, 16384, 64, 128, 200), (16, 8, 4))])
 def test_split_lowrank_and_bf16_out(case, shape):
     """The low-rank term is added by the piece that starts at K step 0, and
     the split tiles' sums are rounded once to a bf16 y."""

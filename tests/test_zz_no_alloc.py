@@ -23,7 +23,8 @@ def _product(n, k, b1, b2, m, dtype, meta, seed):
 def test_noalloc_matches_gemm(order):
     torch = _torch()
     cases = [
-        ((2176, 16384, 64, 128, 450, "bf16", "idx2"), ("split", 8, 8, 4)),    # all 64 MiB of scratch in use
+        ((11136, 8192, 64, 128, 400, "bf16", "idx2"), ("split", 8, 8, 4)),    # all 64 MiB of scratch in use
+        ((3136, 16384, 64, 128, 256, "f16", "mask4"), ("split", 16, 8, 4)),   # K cut in parts: 52 MiB
         ((8256, 5120, 64, 64, 100, "bf16", "idx2"), ("split", 4, 8, 4)),      # 32 MiB
         ((2048, 16384, 128, 128, 100, "bf16", "idx2"), ("split", 4, 4, 2)),   # 16 MiB
         ((256, 4096, 128, 128, 33, "f16", "mask4"), ("split", 1, 8, 1)),      # smaller: reuses the array
