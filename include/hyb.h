@@ -164,10 +164,10 @@ hyb_status hyb_unpack(const hyb_layout* layout, const hyb_packed* src, void* w_o
 
 /* Decode product, 0 <= m <= 16 tokens: Y[i, :] = W' X[i, :] for i < m
  * (SparseDecoding abstract: the decode-phase sparse matrix x vector product
- * over the compressed matrix).  Up to 8 tokens (16 on a matrix with fewer
- * than two 16-row slabs per compute unit) the decode kernel runs; 9-16
- * tokens otherwise run the matrix-core kernel, exactly as hyb_gemm routes
- * them (the decode kernel is bound by its vector arithmetic there).
+ * over the compressed matrix).  Up to 4 tokens (16 on a matrix of at most
+ * one 16-row slab per compute unit) the decode kernel runs; 5-16 tokens
+ * otherwise run the matrix-core kernel, exactly as hyb_gemm routes them
+ * (the decode kernel is bound by its vector arithmetic there).
  *   x       device, m x k of layout->dtype, row stride ldx >= k (elements),
  *           16-byte aligned, ldx % 8 == 0
  *   y       device, m x n, row stride ldy >= n, element type y_dtype in
@@ -247,7 +247,7 @@ hyb_status hyb_gemv_lowrank(const hyb_layout* layout, const hyb_packed* w, const
 /* Sparse + low-rank product for any m >= 0: Y = X W'^T + T U^T as for
  * hyb_gemv_lowrank (3BASiL sections 1 and 4), with the same arguments and
  * checks.  The fused decode kernel runs where hyb_gemm would run the decode
- * kernel (m <= 8, or m <= 16 on short matrices); larger m the matrix-core
+ * kernel (m <= 4, or m <= 16 on short matrices); larger m the matrix-core
  * kernels, which add T U^T to each output tile before it is stored (fp32
  * products and sums, rank walked in order), so 16-bit outputs are rounded
  * once.  rank 0 is plain hyb_gemm. */
@@ -258,8 +258,8 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
 
 /* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same
- * arguments as hyb_gemv; m <= 8 runs the decode kernel (also m <= 16 when
- * the matrix has fewer than two 16-row slabs per compute unit), larger m
+ * arguments as hyb_gemv; m <= 4 runs the decode kernel (also m <= 16 when
+ * the matrix has at most one 16-row slab per compute unit), larger m
  * the matrix-core kernels.  Where those split K over workgroups
  * (HYB_KERNEL_SPLIT of hyb_gemm_shape) they keep partial sums in a
  * workspace that the library allocates (hipMalloc, 64 MiB) at the first

@@ -17,11 +17,12 @@ namespace hyb {
 constexpr int kGemvWaves = HYB_GEMV_WAVES;
 // Decode kernel handles up to this many tokens per launch.
 constexpr int kMaxGemvM = 16;
-// hyb_gemm runs the decode kernel up to this many tokens and the
-// matrix-core kernels above (measured: from 9 tokens the register-fed
-// matrix-core kernel is 1.4-1.9x faster on every workload shape; up to 4
-// the decode kernel is faster; between they are even).
-constexpr int kGemvCrossoverM = 8;
+// hyb_gemm runs the decode kernel up to this many tokens on every matrix
+// (it is the faster kernel there, up to 1.9x); from 5 tokens the decode
+// kernel's cost steps up (14336 x 4096: 17.7 us at 4 tokens, 22 at 5) and
+// the matrix cores take the product except on short matrices
+// (gemv_preferred).
+constexpr int kGemvCrossoverM = 4;
 // Matrices per grouped decode launch (HYB_MAX_GROUP in hyb.h).
 constexpr int kMaxGroup = HYB_MAX_GROUP;
 
@@ -34,9 +35,8 @@ hipError_t launch_gemv(const hyb_layout& L, const hyb_packed& P, const void* x, 
 // Decode product plus the low-rank term T U^T (hyb_gemv_lowrank).
 hipError_t launch_lr_project(const void* v, int64_t ldv, int rank, int64_t k, int dtype, const void* x, int m,
                              int64_t ldx, float* t, int64_t ldt, hipStream_t s);
-// Whether hyb_gemm should run m tokens on the decode kernel (m <= 8, or
-// m <= 16 on a matrix short enough that the decode kernel splits each tile
-// row sixteen ways).
+// Whether hyb_gemm should run m tokens on the decode kernel (m <= 4, or
+// m <= 16 on a matrix of at most one 16-row slab per compute unit).
 bool gemv_preferred(const hyb_layout& L, int m);
 hipError_t launch_gemv_lowrank(const hyb_layout& L, const hyb_packed& P, const void* x, int m, int64_t ldx,
                                const float* t, int64_t ldt, const void* u, int64_t ldu, int rank, void* y,

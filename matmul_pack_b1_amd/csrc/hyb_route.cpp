@@ -49,10 +49,14 @@ int gemv_waves(int64_t slabs, int m) {
 
 bool gemv_preferred(const hyb_layout& L, int m) {
   if (m <= kGemvCrossoverM) return true;
-  // 9-16 tokens on a matrix short enough for 16 wavefronts per slab: the
-  // decode kernel beats the register-fed product there (1024 and 4096 rows
-  // at 16 tokens: 11-12 us against 15-16 us)
-  return m <= kMaxGemvM && gemv_waves(L.n / 16, m) == 16;
+  // 5-16 tokens on a matrix of at most one 16-row slab per CU: the decode
+  // kernel's 8 or 16 wavefronts per slab match or beat the matrix-core
+  // product there (1024-4096 rows: K = 8192-28672 1.0-1.5x faster, K = 4096
+  // within 8%).  With more slabs the matrix cores win: at 5-8 tokens 14336 x
+  // 4096, 6144 x 4096 and 5120 x 17408 take 16.7, 11.7 and 37-39 us against
+  // 22, 16 and 41-42 us (8192 x 28672 even); at 9-16 tokens 5120 x 17408 and
+  // 6144 x 4096 take 41-45 and 12-13 us against 64-69 and 22 us.
+  return m <= kMaxGemvM && L.n / 16 <= int64_t(device_cus());
 }
 
 // Workgroup shape by token count.  Up to 16 tokens the register-fed kernel

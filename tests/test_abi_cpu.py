@@ -254,7 +254,7 @@ def test_gemm_lowrank_rejects(L):
     assert call(u=FAKE + 2) == 1
     assert call(ldu=60) == 1
     assert call(m=-1) == 2
-    assert call(m=4, t=None) == 1                   # 8 tokens or fewer: the decode entry point's checks
+    assert call(m=4, t=None) == 1                   # 4 tokens or fewer: the decode entry point's checks
     assert call(m=0) == 0
     assert call(m=4, ydt=2, t=None) == 1
     assert "t is NULL" in hb.last_error()
@@ -323,6 +323,10 @@ def _layout(n, k, b):
 ROUTES = [
     ((14336, 4096, 128, 1), ("decode", 0, 4, 0)),
     ((1024, 4096, 128, 16), ("decode", 0, 16, 0)),       # short matrix: decode kernel up to 16 tokens
+    ((4096, 14336, 128, 8), ("decode", 0, 16, 0)),       # one 16-row slab per CU
+    ((14336, 4096, 128, 4), ("decode", 0, 4, 0)),
+    ((14336, 4096, 128, 5), ("register", 1, 8, 1)),      # 5-16 tokens on the matrix cores
+    ((5120, 17408, 64, 12), ("split", 1, 8, 1)),         # 320 slabs: matrix cores from 5 tokens
     ((14336, 4096, 128, 12), ("register", 1, 8, 1)),
     ((17408, 5120, 64, 12), ("split", 1, 4, 1)),         # 272 64-row groups: K split over 256 workgroups
     ((17408, 5120, 64, 16), ("split", 1, 4, 1)),

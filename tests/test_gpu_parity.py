@@ -425,9 +425,9 @@ def test_gemm_lowrank_lds_shape(dtype):
 
 
 def test_gemm_lowrank_small_m_and_strides():
-    """8 tokens or fewer run the fused decode kernel (bitwise the decode
-    entry point); above, a y with a row stride larger than n keeps its
-    padding."""
+    """Up to the crossover (8 tokens on this 256-row matrix) the fused decode
+    kernel runs (bitwise the decode entry point); above, a y with a row
+    stride larger than n keeps its padding."""
     torch = _torch()
     note("gemm lowrank m <= 8 and strided y")
     b1, b2, n, k, rank = 128, 128, 256, 512, 32

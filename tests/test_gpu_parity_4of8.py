@@ -2,7 +2,7 @@
 bit-exact against the oracle, every product path within the same bound as
 the 2:4 tiles (|y - y_ref| <= 2e-3 * s), bitwise closed forms, and the
 grouped and low-rank decode entry points.  The matrix-core tests pick token
-counts and shapes that reach each kernel variant: the decode kernel (m <= 8
+counts and shapes that reach each kernel variant: the decode kernel (m <= 4
 through hyb_gemm), the register-fed kernel with eight and four wavefronts,
 two row groups per workgroup (17408 rows: more 64-row groups than compute
 units), 65-128 tokens, and the four LDS-fed shapes (17408 rows at 256 and
