@@ -547,6 +547,15 @@ def kernel_text(hb, layout, m):
         return f"k_gemv ({sh['waves']} wavefronts per 16-row slab)"
     lds_split = sh["kernel"] == "split" and sh["row_groups"] == 4
     lds_parts = lds_split and sh["token_blocks"] >= 12
+    # K parts after whole rounds of plain tiles: the tiles outnumber the CUs
+    # (the parts alone run only where they fill at most half of them)
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-layout.n // 256) * -(-m // (16 * sh["token_blocks"]))
+    if lds_parts and tiles > cus:
+        return (f"k_gemm_lds over whole rounds, then k_gemm_lds_parts + k_gemm_lds_parts_sum on the last row "
+                f"blocks (256-row x {16 * sh['token_blocks']}-token workgroups on {sh['waves']} wavefronts, "
+                f"K cut into equal parts in the parts launch)")
     split_name = ("k_gemm_lds_parts + k_gemm_lds_parts_sum" if lds_parts else
                   "k_gemm_lds_split + k_gemm_lds_split_sum" if lds_split else "k_gemm_split + k_gemm_split_sum")
     name = {"register": "k_gemm_rx", "lds": "k_gemm_lds", "split": split_name}[sh["kernel"]]

@@ -322,9 +322,12 @@ hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const vo
  * 8 token blocks, the LDS-fed 64- or 128-token shape: the (tile, K step)
  * units dealt out evenly over a fixed number of workgroups; or
  * k_gemm_lds_parts with 4 row groups and 12 or 16 token blocks, the 192- or
- * 256-token LDS tile with K cut into equal parts, one per workgroup; partial
- * tiles added by a second kernel in a fixed order; it needs a workspace,
- * which hyb_gemm holds per device and stream).  Errors: as the layout checks of hyb_gemm; out NULL ->
+ * 256-token LDS tile with K cut into equal parts, one per workgroup; with
+ * 16 token blocks and more tiles than CUs, a plain k_gemm_lds launch first
+ * runs the leading 256-row blocks whose tiles fill whole rounds of the CUs,
+ * and the parts cover the remaining blocks; partial tiles added by a second
+ * kernel in a fixed order; it needs a workspace, which hyb_gemm holds per
+ * device and stream).  Errors: as the layout checks of hyb_gemm; out NULL ->
  * HYB_ERR_INVALID_ARG; m < 1 -> HYB_ERR_SHAPE. */
 enum { HYB_KERNEL_DECODE = 1, HYB_KERNEL_REGISTER = 2, HYB_KERNEL_LDS = 3, HYB_KERNEL_SPLIT = 4 };
 hyb_status hyb_gemm_shape(const hyb_layout* layout, int32_t m, int32_t* out);

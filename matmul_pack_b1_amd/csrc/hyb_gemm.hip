@@ -462,6 +462,7 @@ constexpr int32_t kSplitXcds = 8;
 struct SplitArgs {
   int32_t groups;
   float* ws;
+  int32_t rows0;  // GemmRoute::rows0
 };
 
 __device__ __forceinline__ int32_t split_begin(int32_t j, const SplitPlan& p) {
@@ -1094,19 +1095,41 @@ hipError_t gemm_lds_go(const hyb_layout& L, const GemvPtrs& q, int m, const Gemm
   }
   if constexpr (MB == 12 || MB == 16) {
     if (sp.groups > 0) {
-      // K cut into sp.groups / (gn gm) equal parts per tile (the route gives
-      // a multiple of the tile count; workspace checked by the caller)
-      const int64_t steps = int64_t(d.tiles_k) * (B2 / 64), tiles = gn * gm;
+      // The first rows0 row blocks whole, in one plain launch over whole
+      // rounds of the CUs; the blocks after them with K cut into
+      // sp.groups / (tail gm) equal parts per tile (the route gives a
+      // multiple of the tail's tile count; workspace checked by the caller).
+      // The tail runs on a view of the matrix that starts at row rows0 * 256:
+      // the tile-index rows, the output columns and the low-rank rows move
+      // there; the weight streams are addressed through the tile index.
+      const int64_t rows0 = sp.rows0;
+      if (rows0 < 0 || rows0 >= gn) return hipErrorInvalidConfiguration;
+      GemvPtrs qt = q;
+      GemmDims dt = d;
+      if (rows0 > 0) {
+        GemmDims dp = d;
+        dp.n = int32_t(rows0 * 256);
+        hipLaunchKernelGGL((k_gemm_lds<B2, DT, META, MB, STAGES, WAVES>), dim3(unsigned(rows0 * gm)),
+                           dim3(64 * WAVES), size_t(Cfg::kBytes), s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, dp);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t row0 = rows0 * 256;
+        qt.tidx = q.tidx + (row0 / d.b1) * d.tiles_k;
+        qt.y = static_cast<char*>(q.y) + row0 * (d.ydt == HYB_F32 ? 4 : 2);
+        dt.n = int32_t(d.n - row0);
+        if (d.rank > 0) dt.u = d.u + row0 * d.ldu;
+      }
+      const int64_t steps = int64_t(d.tiles_k) * (B2 / 64), tiles = (gn - rows0) * gm;
       const int64_t parts = sp.groups / tiles;
       if (parts < 2 || parts * tiles != sp.groups || steps < parts || tiles * parts >= (int64_t(1) << 31))
         return hipErrorInvalidConfiguration;
       hipLaunchKernelGGL((k_gemm_lds_parts<B2, DT, META, MB, STAGES, WAVES>), dim3(unsigned(tiles * parts)),
-                         dim3(64 * WAVES), size_t(Cfg::kBytes), s, q.dense, q.val, q.meta, q.tidx, q.x, d,
+                         dim3(64 * WAVES), size_t(Cfg::kBytes), s, q.dense, q.val, q.meta, qt.tidx, q.x, dt,
                          int32_t(gm), int32_t(steps), int32_t(parts), sp.ws);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((k_gemm_lds_parts_sum<MB, WAVES>), dim3(unsigned(tiles * (4 * MB))), dim3(256), 0, s,
-                         static_cast<const float*>(sp.ws), q.y, d, int32_t(gm), int32_t(parts));
+                         static_cast<const float*>(sp.ws), qt.y, dt, int32_t(gm), int32_t(parts));
       return hipGetLastError();
     }
   }
@@ -1248,8 +1271,9 @@ hipError_t launch_gemm(const hyb_layout& L, const hyb_packed& P, const void* x, 
   d.rank = rank;
   const GemmRoute r = gemm_route(L, m, device_cus());
   // Without a large enough workspace a split route runs its shape unsplit.
-  SplitArgs sp{0, nullptr};
-  if (r.kernel == kRouteSplit && ws && ws_bytes >= split_workspace_bytes(r)) sp = SplitArgs{r.groups, static_cast<float*>(ws)};
+  SplitArgs sp{0, nullptr, 0};
+  if (r.kernel == kRouteSplit && ws && ws_bytes >= split_workspace_bytes(r))
+    sp = SplitArgs{r.groups, static_cast<float*>(ws), r.rows0};
   if (L.dtype == HYB_BF16) {
     if (L.meta == HYB_META_IDX2) return gemm_b2<HYB_BF16, HYB_META_IDX2>(L, q, m, d, r, sp, s);
     if (L.meta == HYB_META_MASK4) return gemm_b2<HYB_BF16, HYB_META_MASK4>(L, q, m, d, r, sp, s);

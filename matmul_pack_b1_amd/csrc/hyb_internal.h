@@ -65,6 +65,9 @@ struct GemmRoute {
   int rg;      // 64-row groups per workgroup (0: the decode kernel's 16-row slabs;
                // 4: the LDS-fed kernel, also when split)
   int groups;  // workgroups of a split launch (0 otherwise)
+  int rows0;   // 192- and 256-token tiles cut into K parts: the first rows0
+               // 256-row blocks run whole in a plain launch first, the K
+               // parts cover the blocks after them (0: all blocks in parts)
 };
 // A split launch runs one workgroup per CU on at most this many CUs (its
 // workgroups hold partial sums in a workspace of at most kSplitMaxBytes) ...

@@ -19,6 +19,19 @@
 #ifndef HYB_GEMM_LDS_SPLIT_ROUND
 #define HYB_GEMM_LDS_SPLIT_ROUND 0.39
 #endif
+// K parts of the 192- and 256-token LDS tiles: the fewest K steps a part
+// walks; and, for parts that follow whole rounds of a plain launch, a fixed
+// time (us) plus a time per parts workgroup (its 256 KiB partial tile
+// written and read back, about 0.08 us at 6.7 TB/s)
+#ifndef HYB_GEMM_PART_MIN_STEPS
+#define HYB_GEMM_PART_MIN_STEPS 16
+#endif
+#ifndef HYB_GEMM_TAIL_FIXED_US
+#define HYB_GEMM_TAIL_FIXED_US 10.0
+#endif
+#ifndef HYB_GEMM_TAIL_WG_US
+#define HYB_GEMM_TAIL_WG_US 0.078
+#endif
 
 namespace hyb {
 
@@ -209,16 +222,46 @@ GemmRoute gemm_route(int64_t n, int64_t k, int m, int64_t cus) {
     // 0.05 us per K step of the tile (the sum kernel, the pieces' pipeline
     // starts); one round of the 256-token LDS tile costs about 1.75 us per K
     // step, which converts the time to this scale.
+    //
+    // With more tiles than CUs, the 256-token tiles can end a launch instead:
+    // the row blocks whose tiles fill whole rounds of the CUs run in one
+    // plain launch (a round costs 1), and the blocks after them, which would
+    // leave most CUs idle in a last round, run with K cut into parts over
+    // the CUs.  Measured against the previous route (graph bursts, 25
+    // products of 4096-28672 rows at 1024-4096 tokens): 17408 x 5120 at
+    // 1024 / 2048 / 3072 / 4096 tokens 255 / 367 / 546 / 691 us -> 212 /
+    // 343 / 486 / 623; 28672 x 8192 at 2048 and 3072 884 and 1307 -> 837 and
+    // 1275; 14336 x 4096 at 4096 432 -> 426.  The same with the 192-token
+    // tile lost more often than it won (28672 x 8192 at 1536 tokens 3% slower,
+    // 14336 x 4096 and 8192 x 28672 at 2048 10-20% slower), so it is not
+    // offered.
     if (!up_to_128) {
       for (const int mb : {12, 16}) {
-        const int64_t gm = (m64 + 16 * mb - 1) / (16 * mb), tiles = ((n + 255) / 256) * gm;
+        const int64_t gn = (n + 255) / 256, gm = (m64 + 16 * mb - 1) / (16 * mb), tiles = gn * gm;
+        const double step_us = mb == 12 ? 1.45 : 1.75;
         int64_t parts = cus / tiles;
-        if (parts > steps / 16) parts = steps / 16;
-        if (parts < 2 || tiles * parts > kSplitMaxCus) continue;
-        const double t_us = (mb == 12 ? 1.45 : 1.75) * double(steps) / double(parts) + 25.0 + 0.05 * double(steps);
-        const double c = t_us / (1.75 * double(steps));
+        if (parts > steps / HYB_GEMM_PART_MIN_STEPS) parts = steps / HYB_GEMM_PART_MIN_STEPS;
+        if (parts >= 2 && tiles * parts <= kSplitMaxCus) {
+          const double t_us = step_us * double(steps) / double(parts) + 25.0 + 0.05 * double(steps);
+          const double c = t_us / (1.75 * double(steps));
+          if (best.kernel == 0 || c < cost) {
+            best = GemmRoute{kRouteSplit, mb, 8, 4, int32_t(tiles * parts), 0};
+            cost = c;
+          }
+          continue;
+        }
+        if (mb != 16) continue;
+        const int64_t rows0 = (tiles / cus) * cus / gm;  // whole row blocks in whole rounds
+        if (rows0 < 1 || rows0 >= gn) continue;
+        const int64_t tail = (gn - rows0) * gm;
+        int64_t tparts = cus / tail;
+        if (tparts > steps / HYB_GEMM_PART_MIN_STEPS) tparts = steps / HYB_GEMM_PART_MIN_STEPS;
+        if (tparts < 2 || tail * tparts > kSplitMaxCus) continue;
+        const double t_us = step_us * double(steps) / double(tparts) + HYB_GEMM_TAIL_FIXED_US +
+                            HYB_GEMM_TAIL_WG_US * double(tail * tparts) + 0.05 * double(steps);
+        const double c = double((rows0 * gm + cus - 1) / cus) + t_us / (1.75 * double(steps));
         if (best.kernel == 0 || c < cost) {
-          best = GemmRoute{kRouteSplit, mb, 8, 4, int32_t(tiles * parts)};
+          best = GemmRoute{kRouteSplit, mb, 8, 4, int32_t(tail * tparts), int32_t(rows0)};
           cost = c;
         }
       }

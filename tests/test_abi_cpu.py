@@ -348,7 +348,14 @@ ROUTES = [
     ((8192, 28672, 128, 64), ("split", 4, 4, 2)),
     ((8192, 28672, 128, 128), ("split", 8, 8, 4)),
     ((1024, 4096, 128, 32), ("split", 1, 8, 1)),
-    ((17408, 5120, 64, 2048), ("lds", 12, 8, 4)),
+    ((17408, 5120, 64, 2048), ("split", 16, 8, 4)),      # 2 rounds of 256-token tiles, then 32 tiles in 5 K parts
+    ((17408, 5120, 64, 1024), ("split", 16, 8, 4)),      # 1 round, then 16 tiles in 5 K parts
+    ((17408, 5120, 64, 1536), ("lds", 16, 8, 4)),        # a tail of 156 tiles has no room for 2 parts
+    ((17408, 5120, 64, 3072), ("split", 16, 8, 4)),
+    ((28672, 8192, 128, 2048), ("split", 16, 8, 4)),
+    ((28672, 8192, 128, 1536), ("lds", 16, 8, 4)),
+    ((14336, 4096, 128, 4096), ("split", 16, 8, 4)),
+    ((16640, 4096, 128, 1024), ("split", 16, 8, 4)),     # 1 round, then 4 tiles in 4 K parts
     ((14336, 4096, 128, 200), ("split", 16, 8, 4)),
     ((14336, 4096, 128, 160), ("split", 12, 8, 4)),      # 192-token tiles, K cut in 4 parts
     ((14336, 4096, 128, 300), ("lds", 8, 8, 4)),
@@ -398,6 +405,13 @@ def test_split_workspace_sizes(L):
     lay = _layout(17408, 5120, 64)
     size = ctypes.c_size_t(7)
     assert L.hyb_gemm_workspace_size(ctypes.byref(lay), 0, ctypes.byref(size)) == 0 and size.value == 0
+    # whole rounds of 256-token tiles, then the last row blocks in K parts:
+    # only the parts hold partial tiles (256 rows x 256 tokens x 4 bytes each)
+    for (n, k, b, m), tail_wgs in [((17408, 5120, 64, 2048), 32 * 5), ((17408, 5120, 64, 1024), 16 * 5),
+                                   ((17408, 5120, 64, 4096), 64 * 4), ((28672, 8192, 128, 2048), 128 * 2),
+                                   ((16640, 4096, 128, 1024), 4 * 4)]:
+        assert L.hyb_gemm_workspace_size(ctypes.byref(_layout(n, k, b)), m, ctypes.byref(size)) == 0
+        assert size.value == tail_wgs * 256 * 256 * 4, (n, k, m, size.value)
     assert L.hyb_gemm_workspace_size(ctypes.byref(lay), -1, ctypes.byref(size)) == 2
     assert L.hyb_gemm_workspace_size(ctypes.byref(lay), 100, None) == 1
     assert L.hyb_gemm_workspace_size(None, 100, ctypes.byref(size)) == 1

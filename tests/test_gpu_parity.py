@@ -628,12 +628,17 @@ def test_gemm_small_matrices_above_128(config, index, m, route):
 def test_gemm_qwen14b_full(m):
     """17408x5120, 64x64 tiles, 60% sparse tiles; M from 8 to 2048 through
     hyb_gemm and through the matrix-core entry point, every output against
-    the oracle."""
+    the oracle.  At 2048 tokens a 256-CU device runs two whole rounds of
+    256-token tiles (the first 64 of 68 row blocks) and the last 4 row
+    blocks' 32 tiles with K cut into 5 parts."""
     torch = _torch()
     mat, w, tmap = workload_matrix(5, 0)
     note(f"gemm qwen14b m={m}")
     x = mat.activation_bits(m)
     P = pack_gpu(w, tmap, mat.b1, mat.b2, mat.dtype, "idx2")
+    if m == 2048:
+        expect_route(P, m, "split", 16, 8, 4)
+        assert hb.workspace_bytes(P, m) == 32 * 5 * 256 * 256 * 4
     xt = upload(x, mat.dtype)
     yref, s = oracle_full(w, tmap, mat.b1, mat.b2, x, mat.dtype)
     y = hb.gemm(P, xt).cpu().numpy()
@@ -651,9 +656,8 @@ def test_gemm_8b_up_shapes(m, route):
     per workgroup); on a 256-CU device these token counts select the
     192-token tile with K cut into 4 parts (160, ragged), the 256-token tile
     with K cut into 2 parts (200 ragged, 256), and one round of plain tiles:
-    128 tokens (300 ragged, 512), 192 (700 ragged) and 256 (1024).  The
-    17408-row matrix at 2048 tokens (test_gemm_qwen14b_full) also runs the
-    192-token tile.  Every output against the oracle."""
+    128 tokens (300 ragged, 512), 192 (700 ragged) and 256 (1024).  Every
+    output against the oracle."""
     torch = _torch()
     mat, w, tmap = workload_matrix(2, 0)
     note(f"gemm 8b up m={m}")

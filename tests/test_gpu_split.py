@@ -233,3 +233,69 @@ def test_split_two_streams_held_workspaces():
         torch.cuda.synchronize()
         for y, out in zip(serial, outs):
             assert torch.equal(y.view(torch.int32), out.view(torch.int32)), f"repeat {rep}"
+
+
+# Whole rounds of plain 256-token tiles, then the last 256-row blocks with K
+# cut into parts (k_gemm_lds over the first blocks, k_gemm_lds_parts and its
+# sum over the rest): (n, k, b1, b2, m, dtype, meta) -> workgroups of the
+# parts launch on a 256-CU device.  16640 rows are 65 blocks of 256: at 4
+# token blocks 64 blocks fill one round, and the 65th block's 4 tiles run in
+# 4 K parts; 16704 rows add a 66th block a quarter full; 900 and 1000 tokens
+# leave a ragged token block.
+TAIL_CASES = [
+    ((16640, 4096, 128, 128, 1000, "bf16", "idx2"), 16),
+    ((16640, 4096, 64, 64, 1024, "f16", "mask4"), 16),
+    ((16640, 4096, 256, 256, 900, "bf16", "mask8"), 16),
+    ((16704, 4096, 64, 128, 1000, "bf16", "idx2"), 32),
+]
+
+
+@pytest.mark.parametrize("case,tail_wgs", TAIL_CASES)
+def test_lds_tail_every_output(case, tail_wgs):
+    """The route and its workspace (one 256-row x 256-token partial tile per
+    parts workgroup); hyb_gemm, hyb_gemm_noalloc and a second call give the
+    same bits; hyb_gemm_ws without a workspace runs every tile plain.  Both
+    against the oracle on every output, so the rows on either side of the
+    boundary between the two launches are covered."""
+    torch = _torch()
+    n, k, b1, b2, m, dtype, meta = case
+    note(f"lds tail {case}")
+    w, tmap, x = _case(*case)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    expect_route(P, m, "split", 16, 8, 4)
+    assert hb.workspace_bytes(P, m) == tail_wgs * 256 * 256 * 4
+    xt = upload(x, dtype)
+    y = hb.gemm(P, xt)
+    y_again = hb.gemm(P, xt)
+    y_static = hb.gemm_noalloc(P, xt)
+    y_plain = hb.gemm(P, xt, workspace=torch.empty(0, dtype=torch.uint8, device=dev()))
+    torch.cuda.synchronize()
+    for other in (y_again, y_static):
+        assert torch.equal(y.view(torch.int32), other.view(torch.int32))
+    yref, s = oracle_full(w, tmap, b1, b2, x, dtype, meta)
+    assert_close(y.cpu().numpy(), yref, s, what=f"lds tail {case}")
+    assert_close(y_plain.cpu().numpy(), yref, s, what=f"plain {case}")
+
+
+def test_lds_tail_lowrank_and_bf16_out():
+    """On the same route the low-rank rows of the parts launch are those of
+    its row blocks (U moves with the view), T U^T is added once, and a bf16
+    y is rounded once."""
+    torch = _torch()
+    n, k, b1, b2, m = 16704, 4096, 64, 128, 1000
+    rank = 32
+    note("lds tail lowrank + bf16 y")
+    w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
+    rng = np.random.default_rng(1000)
+    t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, "bf16")
+    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    expect_route(P, m, "split", 16, 8, 4)
+    xt, tt = upload(x, "bf16"), torch.from_numpy(t).to(dev())
+    y = hb.gemm_lowrank(P, xt, tt, upload(u, "bf16"))
+    y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=torch.bfloat16)), "bf16")
+    torch.cuda.synchronize()
+    yref, s = oracle_full_lowrank(w, tmap, b1, b2, x, t, u, "bf16")
+    assert_close(y.cpu().numpy(), yref, s, what="lds tail lowrank")
+    y0ref, s0 = oracle_full(w, tmap, b1, b2, x, "bf16")
+    assert_close(y16, y0ref, s0, extra=np.abs(y0ref) * 2.0 ** -8 + 2.0 ** -133, what="lds tail bf16 y")
