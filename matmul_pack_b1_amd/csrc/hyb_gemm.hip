@@ -994,11 +994,14 @@ __global__ __launch_bounds__(256) void k_gemm_lds_split_sum(const float* __restr
 // The 256-row LDS tile with K cut into `parts` equal parts, one workgroup
 // per (tile, part): part p of tile (nb, mbk) covers K steps
 // [p S / parts, (p + 1) S / parts) and writes its partial outputs to
-// workspace slot w = (nb * parts + p) * gm + mbk, each wavefront its own.
+// workspace slot (nb * parts + p) * gm + mbk, each wavefront its own.
 // With one piece per workgroup no state lives across pieces, so the larger
 // tiles keep the plain kernel's registers.  Logical ids are XCD-major (as in
-// k_gemm_split): the gm token blocks of one (row block, part) read the same
-// weights at the same K steps on one XCD.
+// k_gemm_split) and run over (part, row block, token block): the gm token
+// blocks of one (row block, part) read the same weights at the same K steps
+// on one XCD, and the row blocks an XCD holds mostly share its parts, so X
+// columns outside them stay out of its L2 (2-5% faster than row block
+// before part, bitwise the same sums).
 template <int B2, int DT, int META, int MB, int STAGES, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds_parts(const uint4* __restrict__ dense,
                                                         const uint4* __restrict__ val,
@@ -1016,13 +1019,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_lds_parts(const uint4* __re
   const int32_t xcd = L % kSplitXcds, per = G / kSplitXcds, extra = G % kSplitXcds;
   const int32_t w = xcd * per + (xcd < extra ? xcd : extra) + L / kSplitXcds;
   const int32_t r = w / gm, mbk = w - r * gm;
-  const int32_t nb = r / parts, part = r - nb * parts;
+  const int32_t gn = int32_t(gridDim.x) / (gm * parts);
+  const int32_t part = r / gn, nb = r - part * gn;
+  const int32_t slot = (nb * parts + part) * gm + mbk;
   const int32_t k0 = int32_t(int64_t(part) * steps / parts), k1 = int32_t(int64_t(part + 1) * steps / parts);
   f32x4_t acc[4][MBW];
   lds_piece<B2, DT, META, MB, STAGES, WAVES>(dense, val, meta, tidx, x, d, nb, mbk, k0, k1, acc);
   const int32_t n0 = nb * 256 + (wave % 4) * 64;
   if (k0 == 0 && d.rank > 0 && n0 < d.n) lr_block<DT, 4, MBW>(acc, d, n0, mbk * 16 * MB + (wave / 4) * MBW * 16, lane);
-  float* out = ws + int64_t(w) * kPart + wave * kWave;
+  float* out = ws + int64_t(slot) * kPart + wave * kWave;
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
