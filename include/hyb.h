@@ -256,6 +256,18 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
                             int64_t ldu, int32_t rank, void* y, int32_t y_dtype, int64_t ldy,
                             void* stream);
 
+/* hyb_gemm_lowrank with a caller-held split-K workspace, as hyb_gemm_ws is
+ * to hyb_gemm (for code under graph capture, where the library allocates
+ * nothing, and callers that manage device memory).  The workspace size is
+ * that of hyb_gemm_workspace_size for the same layout and m (the route does
+ * not depend on the rank); workspace_bytes = 0 runs the same shape unsplit,
+ * a positive size below the need -> HYB_ERR_INVALID_ARG.  Other arguments
+ * and errors as hyb_gemm_lowrank. */
+hyb_status hyb_gemm_lowrank_ws(const hyb_layout* layout, const hyb_packed* w, const void* x,
+                               int32_t m, int64_t ldx, const float* t, int64_t ldt, const void* u,
+                               int64_t ldu, int32_t rank, void* y, int32_t y_dtype, int64_t ldy,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Prefill product for any m >= 0 (PATCH section 2 "Inferenza e Deployment":
  * sparse tiles on the matrix units, dense tiles on dense kernels).  Same
  * arguments as hyb_gemv; m <= 4 runs the decode kernel (also m <= 16 when

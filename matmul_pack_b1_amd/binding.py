@@ -29,7 +29,7 @@ META_CODES = {"idx2": HYB_META_IDX2, "mask4": HYB_META_MASK4, "mask8": HYB_META_
 DTYPE_CODES = {"f16": HYB_F16, "bf16": HYB_BF16}
 
 EXPORTED = ("hyb_plan", "hyb_layout_check", "hyb_pack", "hyb_unpack", "hyb_gemv", "hyb_gemv_grouped", "hyb_lowrank_project",
-            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_ws", "hyb_gemm_workspace_size", "hyb_gemm_noalloc",
+            "hyb_gemv_lowrank", "hyb_gemm_lowrank", "hyb_gemm_lowrank_ws", "hyb_gemm", "hyb_gemm_mfma", "hyb_gemm_ws", "hyb_gemm_workspace_size", "hyb_gemm_noalloc",
             "hyb_gemm_shape",
             "hyb_stream_read",
             "hyb_status_str", "hyb_last_error", "hyb_abi_version")
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I64, P, I64, I32, P,
                       I32, I64, P]
         f.restype = I32
+    L.hyb_gemm_lowrank_ws.argtypes = [ctypes.POINTER(HybLayout), ctypes.POINTER(HybPacked), P, I32, I64, P, I64, P,
+                                      I64, I32, P, I32, I64, P, ctypes.c_size_t, P]
+    L.hyb_gemm_lowrank_ws.restype = I32
     L.hyb_lowrank_project.argtypes = [P, I64, I32, I64, I32, P, I32, I64, P, I64, P]
     L.hyb_lowrank_project.restype = I32
     L.hyb_gemm_shape.argtypes = [ctypes.POINTER(HybLayout), I32, ctypes.POINTER(I32 * 4)]
@@ -468,7 +471,7 @@ def lowrank_project(v, x, out=None):
     return out
 
 
-def _lowrank(fn_name: str, P: PackedWeight, x, t, u, out_dtype, out):
+def _lowrank(fn_name: str, P: PackedWeight, x, t, u, out_dtype, out, workspace=None):
     torch = _torch()
     _check_x(P, x)
     _check_2d(t, "t")
@@ -493,11 +496,22 @@ def _lowrank(fn_name: str, P: PackedWeight, x, t, u, out_dtype, out):
     for name, tt in (("t", t), ("u", u), ("out", out)):
         _check_gpu(tt, name, x.device)
     _check_same_device(P, x.device)
-    st = getattr(lib(), fn_name)(ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
-                                 int(x.stride(0)) if x.numel() else int(k), _ptr(t),
-                                 int(t.stride(0)) if t.numel() else int(rank), _ptr(u),
-                                 int(u.stride(0)) if u.numel() else int(rank), int(rank), _ptr(out), code,
-                                 int(out.stride(0)) if out.numel() else int(n), _stream(x.device))
+    args = [ctypes.byref(P.layout), ctypes.byref(P.packed_struct()), _ptr(x), int(m),
+            int(x.stride(0)) if x.numel() else int(k), _ptr(t), int(t.stride(0)) if t.numel() else int(rank),
+            _ptr(u), int(u.stride(0)) if u.numel() else int(rank), int(rank), _ptr(out), code,
+            int(out.stride(0)) if out.numel() else int(n)]
+    if fn_name == "hyb_gemm_lowrank_ws":
+        # split-K workspace from torch's allocator, as for gemm()
+        if workspace is None:
+            need = workspace_bytes(P, m)
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+        if workspace is not None:
+            _check_gpu(workspace, "workspace", x.device)
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
+        args += [_ptr(workspace) if workspace is not None else None,
+                 workspace.numel() * workspace.element_size() if workspace is not None else 0]
+    st = getattr(lib(), fn_name)(*args, _stream(x.device))
     check(st, fn_name)
     return out
 
@@ -509,8 +523,16 @@ def gemv_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
     return _lowrank("hyb_gemv_lowrank", P, x, t, u, out_dtype, out)
 
 
-def gemm_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None):
-    """Sparse + low-rank product for any number of tokens."""
+def gemm_lowrank(P: PackedWeight, x, t, u, out_dtype=None, out=None, workspace=None):
+    """Sparse + low-rank product for any number of tokens, through
+    hyb_gemm_lowrank_ws: a route that splits K gets its workspace from torch's
+    allocator (so graph capture works) unless `workspace` is given."""
+    return _lowrank("hyb_gemm_lowrank_ws", P, x, t, u, out_dtype, out, workspace)
+
+
+def gemm_lowrank_held(P: PackedWeight, x, t, u, out_dtype=None, out=None):
+    """The same through hyb_gemm_lowrank (workspace held by the library per
+    device and stream)."""
     return _lowrank("hyb_gemm_lowrank", P, x, t, u, out_dtype, out)
 
 

@@ -453,6 +453,33 @@ hyb_status hyb_gemm_lowrank(const hyb_layout* layout, const hyb_packed* w, const
                     "low-rank gemm launch");
 }
 
+hyb_status hyb_gemm_lowrank_ws(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
+                               int64_t ldx, const float* t, int64_t ldt, const void* u, int64_t ldu, int32_t rank,
+                               void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (m >= 0 && m <= hyb::kMaxGemvM && decode_route(layout, m))
+    return gemv_lowrank_decode(layout, w, x, m, ldx, t, ldt, u, ldu, rank, y, y_dtype, ldy, stream);
+  hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);
+  if (st != HYB_OK) return st;
+  if ((st = check_rank(rank)) != HYB_OK) return st;
+  if (workspace_bytes > 0 && (!workspace || !aligned(workspace, 16)))
+    return fail(HYB_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned with workspace_bytes = %zu",
+                workspace_bytes);
+  if (rank == 0)
+    return hyb_gemm_ws(layout, w, x, m, ldx, y, y_dtype, ldy, workspace, workspace_bytes, stream);
+  if (layout->n == 0) return ok();
+  if ((st = check_lowrank(t, ldt, u, ldu, rank)) != HYB_OK) return st;
+  if ((st = check_mfma_limits(m, ldx)) != HYB_OK) return st;
+  const size_t need = hyb::split_workspace_bytes(hyb::gemm_route(*layout, m, hyb::device_cus()));
+  if (workspace_bytes > 0 && workspace_bytes < need)
+    return fail(HYB_ERR_INVALID_ARG, "workspace_bytes = %zu, this product needs %zu (or 0: unsplit)",
+                workspace_bytes, need);
+  return hip_status(hyb::launch_gemm(*layout, *w, x, m, ldx, y, y_dtype, ldy, static_cast<hipStream_t>(stream),
+                                     workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, t, ldt, u, ldu,
+                                     rank),
+                    "low-rank gemm launch");
+}
+
 hyb_status hyb_gemm_mfma(const hyb_layout* layout, const hyb_packed* w, const void* x, int32_t m,
                          int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
   hyb_status st = check_product(layout, w, x, m, ldx, y, y_dtype, ldy, INT32_MAX);

@@ -431,6 +431,25 @@ def test_gemm_ws_rejects_before_launch(L):
     assert fn(*args(FAKE, need.value - 16)) == 1            # below the need
 
 
+def test_gemm_lowrank_ws_rejects_before_launch(L):
+    """hyb_gemm_lowrank_ws: the workspace checks of hyb_gemm_ws (NULL or
+    misaligned with a size, a size below the need) and a NULL t are
+    HYB_ERR_INVALID_ARG, a rank off the multiple-of-8 grid HYB_ERR_SHAPE,
+    all before anything runs."""
+    fn = L.hyb_gemm_lowrank_ws
+    L2, _ = hb.plan(2048, 16384, 128, 128, "bf16", "idx2", np.zeros((16, 128), np.uint8))
+    need = ctypes.c_size_t(0)
+    assert L.hyb_gemm_workspace_size(ctypes.byref(L2), 100, ctypes.byref(need)) == 0 and need.value > 0
+    packed = hb.HybPacked(FAKE, FAKE, FAKE, FAKE)
+    args = lambda ws, nb, t=FAKE, rank=16: (ctypes.byref(L2), ctypes.byref(packed), FAKE, 100, 16384, t, 16, FAKE, 16,
+                                            rank, FAKE, 3, 2048, ws, nb, None)
+    assert fn(*args(None, need.value)) == 1                 # NULL with a size
+    assert fn(*args(FAKE + 8, need.value)) == 1             # misaligned
+    assert fn(*args(FAKE, need.value - 16)) == 1            # below the need
+    assert fn(*args(FAKE, need.value, t=None)) == 1         # t NULL
+    assert fn(*args(FAKE, need.value, rank=12)) == 2        # rank not a multiple of 8: HYB_ERR_SHAPE
+
+
 def test_gemm_shape_rejects(L):
     lay = _layout(1024, 1024, 128)
     out = (ctypes.c_int32 * 4)()

@@ -280,7 +280,8 @@ def test_lds_tail_every_output(case, tail_wgs):
 def test_lds_tail_lowrank_and_bf16_out():
     """On the same route the low-rank rows of the parts launch are those of
     its row blocks (U moves with the view), T U^T is added once, and a bf16
-    y is rounded once."""
+    y is rounded once; the caller-workspace and library-workspace entry
+    points give the same bits, also from a captured graph."""
     torch = _torch()
     n, k, b1, b2, m = 16704, 4096, 64, 128, 1000
     rank = 32
@@ -292,9 +293,32 @@ def test_lds_tail_lowrank_and_bf16_out():
     P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
     expect_route(P, m, "split", 16, 8, 4)
     xt, tt = upload(x, "bf16"), torch.from_numpy(t).to(dev())
-    y = hb.gemm_lowrank(P, xt, tt, upload(u, "bf16"))
+    ut = upload(u, "bf16")
+    y = hb.gemm_lowrank(P, xt, tt, ut)
+    y_held = hb.gemm_lowrank_held(P, xt, tt, ut)
     y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=torch.bfloat16)), "bf16")
+    # captured with the workspace from torch's allocator, the graph runs the
+    # same split launches: three replays give the eager bits
+    yg = torch.empty_like(y)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        g.capture_begin()
+        hb.gemm_lowrank(P, xt, tt, ut, out=yg)
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y_held.view(torch.int32))
+    for i in range(3):
+        yg.fill_(float("nan"))
+        hb.gemm(P, xt[: m // 2])            # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg.view(torch.int32), y.view(torch.int32)), f"replay {i}"
+    del g
     yref, s = oracle_full_lowrank(w, tmap, b1, b2, x, t, u, "bf16")
     assert_close(y.cpu().numpy(), yref, s, what="lds tail lowrank")
     y0ref, s0 = oracle_full(w, tmap, b1, b2, x, "bf16")
