@@ -864,11 +864,12 @@ def sweep(hb, torch, wl, dev, rotate, args):
                 for m in W.batches:
                     x = hb.bits_to_tensor(mat.activation_bits(m), mat.dtype, dev)
                     y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+                    # hyb_gemm through the binding: a route that splits K takes its
+                    # workspace from torch's allocator, which the captured graph
+                    # keeps (the library-held workspace of hyb_gemm_mfma is not
+                    # allocated under capture, so its split routes would run
+                    # unsplit here)
                     fns = [("gemm", lambda P: hb.gemm(P, x, out=y))]
-                    if m > 16:
-                        fns = [("gemm_mfma", lambda P: hb.gemm_mfma(P, x, out=y))]
-                    elif cfg == 5:
-                        fns.append(("gemm_mfma", lambda P: hb.gemm_mfma(P, x, out=y)))
                     for fname, fn in fns:
                         us = timed(fn, copies)
                         results.append({"config": cfg, "matrix": mat.name, "kind": kind, "m": m, "fn": fname,
