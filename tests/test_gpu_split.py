@@ -277,7 +277,8 @@ def test_lds_tail_every_output(case, tail_wgs):
     assert_close(y_plain.cpu().numpy(), yref, s, what=f"plain {case}")
 
 
-def test_lds_tail_lowrank_and_bf16_out():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_lds_tail_lowrank_and_16bit_out(dtype):
     """On the same route the low-rank rows of the parts launch are those of
     its row blocks (U moves with the view), T U^T is added once, and a bf16
     y is rounded once; the caller-workspace and library-workspace entry
@@ -285,18 +286,19 @@ def test_lds_tail_lowrank_and_bf16_out():
     torch = _torch()
     n, k, b1, b2, m = 16704, 4096, 64, 128, 1000
     rank = 32
-    note("lds tail lowrank + bf16 y")
-    w, tmap, x = _case(n, k, b1, b2, m, "bf16", "idx2")
+    note(f"lds tail lowrank + 16-bit y {dtype}")
+    w, tmap, x = _case(n, k, b1, b2, m, dtype, "idx2")
     rng = np.random.default_rng(1000)
     t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
-    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, "bf16")
-    P = pack_gpu(w, tmap, b1, b2, "bf16", "idx2")
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, "idx2")
     expect_route(P, m, "split", 16, 8, 4)
-    xt, tt = upload(x, "bf16"), torch.from_numpy(t).to(dev())
-    ut = upload(u, "bf16")
+    xt, tt = upload(x, dtype), torch.from_numpy(t).to(dev())
+    ut = upload(u, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     y = hb.gemm_lowrank(P, xt, tt, ut)
     y_held = hb.gemm_lowrank_held(P, xt, tt, ut)
-    y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=torch.bfloat16)), "bf16")
+    y16 = oracle.widen(hb.tensor_to_bits(hb.gemm(P, xt, out_dtype=tdt)), dtype)
     # captured with the workspace from torch's allocator, the graph runs the
     # same split launches: three replays give the eager bits
     yg = torch.empty_like(y)
@@ -319,7 +321,10 @@ def test_lds_tail_lowrank_and_bf16_out():
         torch.cuda.synchronize()
         assert torch.equal(yg.view(torch.int32), y.view(torch.int32)), f"replay {i}"
     del g
-    yref, s = oracle_full_lowrank(w, tmap, b1, b2, x, t, u, "bf16")
+    yref, s = oracle_full_lowrank(w, tmap, b1, b2, x, t, u, dtype)
     assert_close(y.cpu().numpy(), yref, s, what="lds tail lowrank")
-    y0ref, s0 = oracle_full(w, tmap, b1, b2, x, "bf16")
-    assert_close(y16, y0ref, s0, extra=np.abs(y0ref) * 2.0 ** -8 + 2.0 ** -133, what="lds tail bf16 y")
+    y0ref, s0 = oracle_full(w, tmap, b1, b2, x, dtype)
+    # half an output ulp of rounding on top of the bound (bf16: 2^-8 relative,
+    # fp16: 2^-11 relative and 2^-25 absolute below its normal range)
+    ulp = (np.abs(y0ref) * 2.0 ** -8 + 2.0 ** -133) if dtype == "bf16" else (np.abs(y0ref) * 2.0 ** -11 + 2.0 ** -25)
+    assert_close(y16, y0ref, s0, extra=ulp, what=f"lds tail {dtype} y")
