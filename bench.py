@@ -55,9 +55,10 @@ HBM_PEAK_GBS = 8000.0
 # readings; the summary, its command and the kernel it covers are in
 # TRAFFIC_PROFILE.  Valid for the kernel as profiled; re-measure after
 # changing it.
-TRAFFIC_BYTES_PER_LAUNCH = 81_902_592
+TRAFFIC_BYTES_PER_LAUNCH = 82_685_952
 TRAFFIC_PROFILE = "profiles/k_gemv_llama8b_up_14336x4096_m1_hbm_traffic.md"
-TRAFFIC_KERNEL = "k_gemv<MT=1, B2=128, bf16, idx2, WAVES=4, STAGES=2, LR=false, XR=true>"
+TRAFFIC_KERNEL = ("k_gemv<MT=1, B2=128, bf16, idx2, WAVES=4, STAGES=2, LR=false, XR=true> "
+                  "(768 whole-slab and 256 half-slab workgroups)")
 MFMA_PEAK_BF16_TFLOPS = 2500.0
 
 

@@ -196,15 +196,31 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2, XR>& st, in
 // additions stays fixed.
 // With XR the wavefront's whole tile range (at most kXrTiles tiles) has its
 // x columns staged once, before the first weight loads.
+// The LDS of one decode workgroup.  The kernel declares it and hands it to
+// gemv_slab, so that two instantiations of gemv_slab in one kernel (the two
+// ring depths of the mixed launch) share one allocation.
+template <int MT, int B2, int META, int WAVES, bool XR>
+struct GemvSmem {
+  static constexpr int XS = XR ? kXrTiles<B2> * B2 : B2;  // x row stride
+  uint4 lut8[META == HYB_META_MASK8 ? 256 : 1];
+  __attribute__((aligned(16))) uint16_t xs[WAVES][MT * XS];
+  float red[WAVES][MT][16];
+};
+
+// half >= 0 takes only rows 8 half .. 8 half + 7 of the slab: the other
+// rows' lanes (the four lanes of a row are all in or all out) get weight
+// offsets past the end of every resource, so they load nothing, and their
+// rows are not stored.  The rows taken see the same loads in the same order
+// as with half < 0, so their results are bitwise equal.  Only with XR,
+// where x does not come through the weight loads.
 template <int MT, int B2, int DT, int META, int WAVES, int STAGES, bool LR = false, bool XR = false>
 __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const uint4* __restrict__ val,
                                           const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
                                           const uint16_t* __restrict__ x, void* __restrict__ y,
-                                          const GemvDims& d, int64_t slab) {
-  constexpr int XS = XR ? kXrTiles<B2> * B2 : B2;  // x row stride in the LDS region
-  __shared__ __attribute__((aligned(16))) uint16_t xs_all[WAVES][MT * XS];
-  __shared__ float red[WAVES][MT][16];
-  __shared__ uint4 lut8[META == HYB_META_MASK8 ? 256 : 1];
+                                          const GemvDims& d, int64_t slab,
+                                          GemvSmem<MT, B2, META, WAVES, XR>& sm, int half = -1) {
+  constexpr int XS = GemvSmem<MT, B2, META, WAVES, XR>::XS;
+  uint4* lut8 = sm.lut8;
   if constexpr (META == HYB_META_MASK8) {
     fill_expand8_lut(lut8);
     __syncthreads();
@@ -218,7 +234,8 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
   const int32_t tk0 = (wave * d.tiles_k) / WAVES;
   const int32_t cnt = ((wave + 1) * d.tiles_k) / WAVES - tk0;
   const int32_t* __restrict__ trow = tidx + tn * d.tiles_k + tk0;
-  uint16_t* xs = xs_all[wave];
+  uint16_t* xs = sm.xs[wave];
+  const int ln = (half < 0 || ((lane & 15) >> 3) == half) ? lane : (1 << 22);
 
   float acc[MT];
 #pragma unroll
@@ -251,7 +268,7 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
     ti[s] = tile_index(s);
-    gemv_load<MT, B2, XR>(st[s], ti[s], tk0 + s, dense, val, meta, x, d, rs, lane);
+    gemv_load<MT, B2, XR>(st[s], ti[s], tk0 + s, dense, val, meta, x, d, rs, ln);
   }
   if constexpr (XR) {
     // the x loads were issued first, so waiting for them does not wait for
@@ -269,7 +286,7 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
       constexpr int kLast = STAGES - 1;
       const int ld = (s + kLast) % STAGES;
       ti[ld] = tiN;
-      gemv_load<MT, B2, XR>(st[ld], tiN, tk0 + i + s + kLast, dense, val, meta, x, d, rs, lane);
+      gemv_load<MT, B2, XR>(st[ld], tiN, tk0 + i + s + kLast, dense, val, meta, x, d, rs, ln);
       tiN = tile_index(i + s + STAGES);
       if (i + s < cnt)
         gemv_compute<MT, B2, DT, META, XR>(st[s], ti[s], XR ? xs + (i + s) * B2 : xs, lut8, d, lane, acc);
@@ -320,15 +337,15 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
   }
   if (lane < 16) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    for (int m = 0; m < MT; ++m) sm.red[wave][m][lane] = acc[m];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < MT * 16; i += blockDim.x) {
     const int m = i >> 4, r = i & 15;
-    if (m < d.m) {
-      float v = red[0][m][r];
+    if (m < d.m && (half < 0 || (r >> 3) == half)) {
+      float v = sm.red[0][m][r];
 #pragma unroll
-      for (int w = 1; w < WAVES; ++w) v += red[w][m][r];
+      for (int w = 1; w < WAVES; ++w) v += sm.red[w][m][r];
       store_out(y, d.ydt, int64_t(m) * d.ldy + slab * 16 + r, v);
     }
   }
@@ -340,8 +357,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ d
                                                      const uint16_t* __restrict__ meta,
                                                      const int32_t* __restrict__ tidx,
                                                      const uint16_t* __restrict__ x,
-                                                     void* __restrict__ y, GemvDims d) {
-  gemv_slab<MT, B2, DT, META, WAVES, STAGES, LR, XR>(dense, val, meta, tidx, x, y, d, blockIdx.x);
+                                                     void* __restrict__ y, GemvDims d, int32_t full) {
+  __shared__ GemvSmem<MT, B2, META, WAVES, XR> sm;
+  const int32_t b = blockIdx.x;
+  if constexpr (XR) {
+    // Workgroups past full are half slabs: slab full + (b - full) / 2, half
+    // (b - full) % 2, with a ring one stage deeper, which keeps as many
+    // weight bytes in flight per workgroup as a whole slab with the
+    // shallower ring.
+    if (b >= full) {
+      gemv_slab<MT, B2, DT, META, WAVES, STAGES + 1, LR, XR>(dense, val, meta, tidx, x, y, d,
+                                                             full + ((b - full) >> 1), sm, (b - full) & 1);
+      return;
+    }
+  }
+  gemv_slab<MT, B2, DT, META, WAVES, STAGES, LR, XR>(dense, val, meta, tidx, x, y, d, b, sm);
 }
 
 // Grouped decode product: one launch multiplies the same x by up to
@@ -372,8 +402,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_grouped(const uint16_t* __r
   d.n_dense = g.n_dense[gi];
   d.n_sparse = g.n_sparse[gi];
   d.b1 = g.b1[gi];
+  __shared__ GemvSmem<MT, B2, META, WAVES, XR> sm;
   gemv_slab<MT, B2, DT, META, WAVES, STAGES, false, XR>(g.dense[gi], g.val[gi], g.meta[gi], g.tidx[gi], x, g.y[gi], d,
-                                              b - g.slab_start[gi]);
+                                                        b - g.slab_start[gi], sm);
 }
 
 }  // namespace
@@ -393,17 +424,17 @@ bool gemv_xr(int64_t tiles_k, int b2, int waves, int m) {
 }
 
 template <int MT, int DT, int META, bool LR, int W, bool XR = false>
-void gemv_b2(int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
+void gemv_b2(int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d, int32_t full = INT32_MAX) {
   const dim3 block(64 * W);
   switch (b2) {
     case 64:
-      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, full);
       break;
     case 128:
-      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, full);
       break;
     default:
-      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d);
+      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, full);
       break;
   }
 }
@@ -411,25 +442,27 @@ void gemv_b2(int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims
 // MT-token variant with the wavefront count of gemv_waves; x staged per
 // wavefront range (XR) where gemv_xr allows it.
 template <int MT, int DT, int META, bool LR>
-void gemv_w(int waves, bool xr, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
+void gemv_w(int waves, bool xr, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d,
+            int32_t full) {
   if constexpr (MT <= 4) {
     if (waves == 8) return gemv_b2<MT, DT, META, LR, 8>(b2, grid, s, q, d);
   } else {
     if (waves == 16) return gemv_b2<MT, DT, META, LR, 16>(b2, grid, s, q, d);
   }
   if constexpr (MT <= kXrMaxM) {
-    if (xr) return gemv_b2<MT, DT, META, LR, kGemvWaves, true>(b2, grid, s, q, d);
+    if (xr) return gemv_b2<MT, DT, META, LR, kGemvWaves, true>(b2, grid, s, q, d, full);
   }
   gemv_b2<MT, DT, META, LR, kGemvWaves>(b2, grid, s, q, d);
 }
 
 template <int DT, int META, bool LR>
-void gemv_mt(int m, int waves, bool xr, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
-  if (m <= 1) gemv_w<1, DT, META, LR>(waves, xr, b2, grid, s, q, d);
-  else if (m <= 2) gemv_w<2, DT, META, LR>(waves, xr, b2, grid, s, q, d);
-  else if (m <= 4) gemv_w<4, DT, META, LR>(waves, xr, b2, grid, s, q, d);
-  else if (m <= 8) gemv_w<8, DT, META, LR>(waves, xr, b2, grid, s, q, d);
-  else gemv_w<16, DT, META, LR>(waves, xr, b2, grid, s, q, d);
+void gemv_mt(int m, int waves, bool xr, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d,
+             int32_t full) {
+  if (m <= 1) gemv_w<1, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
+  else if (m <= 2) gemv_w<2, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
+  else if (m <= 4) gemv_w<4, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
+  else if (m <= 8) gemv_w<8, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
+  else gemv_w<16, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
 }
 
 }  // namespace
@@ -456,17 +489,20 @@ hipError_t launch_gemv_impl(const hyb_layout& L, const hyb_packed& P, const void
   d.u = static_cast<const uint16_t*>(u);
   d.ldu = ldu;
   d.rank = rank;
-  const dim3 grid(unsigned(L.n / 16));
-  const int w = gemv_waves(L.n / 16, m);
+  const int64_t slabs = L.n / 16;
+  const int w = gemv_waves(slabs, m);
   const bool xr = gemv_xr(L.tiles_k, L.b2, w, m);
+  // with x staged per range the last round's slabs may run as halves
+  const int64_t full = xr ? gemv_full_slabs(slabs, device_cus()) : slabs;
+  const dim3 grid(unsigned(full + 2 * (slabs - full)));
   if (L.dtype == HYB_BF16) {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, w, xr, L.b2, grid, s, q, d);
-    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, w, xr, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, w, xr, L.b2, grid, s, q, d);
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
+    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
   } else {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, w, xr, L.b2, grid, s, q, d);
-    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, w, xr, L.b2, grid, s, q, d);
-    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, w, xr, L.b2, grid, s, q, d);
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
+    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
   }
   return hipGetLastError();
 }

@@ -53,6 +53,10 @@ int device_cus();
 // Wavefronts per 16-row slab of the decode kernel for a matrix of `slabs`
 // slabs at m tokens.
 int gemv_waves(int64_t slabs, int m);
+// Slabs the decode kernel runs whole when it cuts the last round's slabs
+// into 8-row halves (all `slabs` where it does not); the launch takes
+// full + 2 (slabs - full) workgroups.
+int64_t gemv_full_slabs(int64_t slabs, int cus);
 // Kernel and workgroup shape of a product (hyb_gemm_shape).
 constexpr int kRouteDecode = 1;    // k_gemv
 constexpr int kRouteRegister = 2;  // k_gemm_rx

@@ -60,6 +60,16 @@ int gemv_waves(int64_t slabs, int m) {
   return m <= 4 ? 8 : 16;
 }
 
+// Whole slabs of the mixed decode launch.  Workgroup b runs on XCD b % 8
+// and the CUs of an XCD take its workgroups in turn, so with S slabs on C
+// CUs the last round leaves r = S mod C CUs a slab more than the rest, and
+// the launch waits on them.  Where 2r <= C those r slabs are cut into 8-row
+// halves, one per CU of the last round, and the other slabs stay whole.
+int64_t gemv_full_slabs(int64_t slabs, int cus) {
+  const int64_t r = cus > 0 ? slabs % cus : 0;
+  return (slabs > cus && r > 0 && 2 * r <= cus) ? slabs - r : slabs;
+}
+
 bool gemv_preferred(const hyb_layout& L, int m) {
   if (m <= kGemvCrossoverM) return true;
   // 5-16 tokens on a matrix of at most one 16-row slab per CU: the decode

@@ -103,7 +103,7 @@ def oracle_full(w_bits, tmap, b1, b2, x_bits, dtype, meta="idx2", chunk_rows=204
     return np.concatenate(ys, axis=1), np.concatenate(ss, axis=1)
 
 
-def oracle_full_lowrank(w_bits, tmap, b1, b2, x_bits, t, u_bits, dtype, chunk_rows=2048):
+def oracle_full_lowrank(w_bits, tmap, b1, b2, x_bits, t, u_bits, dtype, meta="idx2", chunk_rows=2048):
     """oracle.ref_lowrank for every output row, a chunk of tile rows at a
     time (as oracle_full)."""
     n = w_bits.shape[0]
@@ -111,7 +111,7 @@ def oracle_full_lowrank(w_bits, tmap, b1, b2, x_bits, t, u_bits, dtype, chunk_ro
     ys, ss = [], []
     for r0 in range(0, n, step):
         r1 = min(n, r0 + step)
-        sub = oracle.prune(w_bits[r0:r1], tmap[r0 // b1:r1 // b1], b1, b2)
+        sub = oracle.prune(w_bits[r0:r1], tmap[r0 // b1:r1 // b1], b1, b2, meta)
         y, s = oracle.ref_lowrank(sub, x_bits, t, u_bits[r0:r1], dtype)
         ys.append(y)
         ss.append(s)
@@ -307,6 +307,38 @@ def test_gemv_lowrank(rank, m, b1, b2, dtype, meta):
     assert torch.equal(y0, yg)
     yref, s = oracle.ref_lowrank(oracle.prune(w, tmap, b1, b2), x, t, u, dtype)
     assert_close(y.cpu().numpy(), yref, s, what="gemv lowrank")
+
+
+@pytest.mark.parametrize("rem,m,b1,b2,dtype,meta", [(4, 1, 64, 128, "bf16", "idx2"),
+                                                    (64, 2, 64, 256, "f16", "mask4"),
+                                                    (128, 1, 128, 128, "bf16", "idx2"),
+                                                    (132, 2, 64, 64, "bf16", "mask8")])
+def test_gemv_half_slab_last_round(rem, m, b1, b2, dtype, meta):
+    """Decode over 2 C + rem slabs (C = the device's compute units): where
+    2 rem <= C the last round's slabs run as 8-row halves.  Bitwise equal to
+    the grouped launch (whole slabs only), the low-rank entry point with
+    U = 0 bitwise equal too, and both products against the oracle."""
+    torch = _torch()
+    n, k, rank = (2 * device_cus() + rem) * 16, 1024, 16
+    note(f"gemv half slabs n={n} m={m} {b1}x{b2} {dtype} {meta}")
+    w, tmap = random_case(rem * 7 + m, n, k, b1, b2, dtype)
+    rng = np.random.default_rng(rem + 100 * m)
+    x = wl.float32_to_bits(rng.standard_normal((m, k)).astype(np.float32), dtype)
+    t = (rng.standard_normal((m, rank)) * 4).astype(np.float32)
+    u = wl.float32_to_bits(rng.standard_normal((n, rank)).astype(np.float32) * 0.05, dtype)
+    P = pack_gpu(w, tmap, b1, b2, dtype, meta)
+    xt, tt = upload(x, dtype), torch.from_numpy(t).to(dev())
+    y = hb.gemv(P, xt)
+    (yg,) = hb.gemv_grouped([P], xt)
+    y0 = hb.gemv_lowrank(P, xt, tt, upload(np.zeros_like(u), dtype))
+    yl = hb.gemv_lowrank(P, xt, tt, upload(u, dtype))
+    torch.cuda.synchronize()
+    assert torch.equal(y, yg)
+    assert torch.equal(y0, yg)
+    yref, s = oracle_full(w, tmap, b1, b2, x, dtype, meta=meta)
+    assert_close(y.cpu().numpy(), yref, s, what="gemv half slabs")
+    lref, ls = oracle_full_lowrank(w, tmap, b1, b2, x, t, u, dtype, meta=meta)
+    assert_close(yl.cpu().numpy(), lref, ls, what="gemv lowrank half slabs")
 
 
 @pytest.mark.parametrize("rank,k,m,dtype", [(64, 4096, 1, "bf16"), (64, 4096, 16, "bf16"), (1, 72, 3, "f16"),
