@@ -50,14 +50,14 @@ sys.path.insert(0, HERE)
 
 METRIC = "hybrid 2:4/dense GEMV µs + achieved HBM GB/s at 8B MLP shape; speedup vs dense"
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per hybrid k_gemv launch at this workload, from two rocprofv3
+# HBM bytes per hybrid decode launch at this workload, from two rocprofv3
 # --pmc passes (FETCH_SIZE, then WRITE_SIZE) scaled by a plain 128 MiB copy's
 # readings; the summary, its command and the kernel it covers are in
 # TRAFFIC_PROFILE.  Valid for the kernel as profiled; re-measure after
 # changing it.
-TRAFFIC_BYTES_PER_LAUNCH = 82_685_952
+TRAFFIC_BYTES_PER_LAUNCH = 82_676_736
 TRAFFIC_PROFILE = "profiles/k_gemv_llama8b_up_14336x4096_m1_hbm_traffic.md"
-TRAFFIC_KERNEL = ("k_gemv<MT=1, B2=128, bf16, idx2, WAVES=4, STAGES=2, LR=false, XR=true> "
+TRAFFIC_KERNEL = ("k_gemv_mixed<MT=1, B2=128, bf16, idx2, WAVES=4, STAGES=2, LR=false, XR=true> "
                   "(768 whole-slab and 256 half-slab workgroups)")
 MFMA_PEAK_BF16_TFLOPS = 2500.0
 

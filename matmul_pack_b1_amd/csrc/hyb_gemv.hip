@@ -57,7 +57,7 @@ __device__ __forceinline__ void gemv_load(GemvStage<MT, B2, XR>& st, int32_t ti,
                                           const uint4* __restrict__ val,
                                           const uint16_t* __restrict__ meta,
                                           const uint16_t* __restrict__ x, const GemvDims& d,
-                                          int rs, int lane) {
+                                          int rs, int lane, int wl) {
   const bool is_dense = ti >= 0;
   const int32_t slot = is_dense ? ti : ~ti;
   const bool ok = is_dense ? (slot < d.n_dense) : (slot < d.n_sparse);
@@ -69,17 +69,17 @@ __device__ __forceinline__ void gemv_load(GemvStage<MT, B2, XR>& st, int32_t ti,
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, wbytes);
 #pragma unroll
   for (int c = 0; c < B2 / 32; ++c)
-    st.w[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, lane * 16 + c * 1024, 0, HYB_W_AUX));
+    st.w[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, wl * 16 + c * 1024, 0, HYB_W_AUX));
   const char* mbase = reinterpret_cast<const char*>(meta) + (int64_t(slot) * (tile / 16) + int64_t(rs) * B2) * 2;
   const __amdgpu_buffer_rsrc_t mr = make_rsrc(mbase, (ok && !is_dense) ? 2 * B2 : 0);
   if constexpr (B2 == 64) {
     // the aligned dword holding the lane's 16-bit word (a 16-bit load would
     // be zero-extended where it lands, which waits for it there)
-    st.mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mr, (lane * 2) & ~3, 0, HYB_M_AUX) >> (16 * (lane & 1));
+    st.mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mr, (wl * 2) & ~3, 0, HYB_M_AUX) >> (16 * (wl & 1));
   } else if constexpr (B2 == 128) {
-    st.mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mr, lane * 4, 0, HYB_M_AUX);
+    st.mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mr, wl * 4, 0, HYB_M_AUX);
   } else {
-    const auto mm = __builtin_amdgcn_raw_buffer_load_b64(mr, lane * 8, 0, HYB_M_AUX);
+    const auto mm = __builtin_amdgcn_raw_buffer_load_b64(mr, wl * 8, 0, HYB_M_AUX);
     st.mw[0] = mm[0];
     st.mw[1] = mm[1];
   }
@@ -196,6 +196,10 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2, XR>& st, in
 // additions stays fixed.
 // With XR the wavefront's whole tile range (at most kXrTiles tiles) has its
 // x columns staged once, before the first weight loads.
+// Decode kernels that have a mixed launch: one token, four wavefronts per
+// slab.  (At two and four tokens the mixed launch measured no faster.)
+__host__ __device__ constexpr bool gemv_has_halves(int mt, int waves) { return waves == kGemvWaves && mt == 1; }
+
 // The LDS of one decode workgroup.  The kernel declares it and hands it to
 // gemv_slab, so that two instantiations of gemv_slab in one kernel (the two
 // ring depths of the mixed launch) share one allocation.
@@ -211,8 +215,8 @@ struct GemvSmem {
 // rows' lanes (the four lanes of a row are all in or all out) get weight
 // offsets past the end of every resource, so they load nothing, and their
 // rows are not stored.  The rows taken see the same loads in the same order
-// as with half < 0, so their results are bitwise equal.  Only with XR,
-// where x does not come through the weight loads.
+// as with half < 0, so their results are bitwise equal.  x comes through
+// the real lane in either case.
 template <int MT, int B2, int DT, int META, int WAVES, int STAGES, bool LR = false, bool XR = false>
 __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const uint4* __restrict__ val,
                                           const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
@@ -268,7 +272,7 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
     ti[s] = tile_index(s);
-    gemv_load<MT, B2, XR>(st[s], ti[s], tk0 + s, dense, val, meta, x, d, rs, ln);
+    gemv_load<MT, B2, XR>(st[s], ti[s], tk0 + s, dense, val, meta, x, d, rs, lane, ln);
   }
   if constexpr (XR) {
     // the x loads were issued first, so waiting for them does not wait for
@@ -286,7 +290,7 @@ __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const
       constexpr int kLast = STAGES - 1;
       const int ld = (s + kLast) % STAGES;
       ti[ld] = tiN;
-      gemv_load<MT, B2, XR>(st[ld], tiN, tk0 + i + s + kLast, dense, val, meta, x, d, rs, ln);
+      gemv_load<MT, B2, XR>(st[ld], tiN, tk0 + i + s + kLast, dense, val, meta, x, d, rs, lane, ln);
       tiN = tile_index(i + s + STAGES);
       if (i + s < cnt)
         gemv_compute<MT, B2, DT, META, XR>(st[s], ti[s], XR ? xs + (i + s) * B2 : xs, lut8, d, lane, acc);
@@ -357,21 +361,32 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint4* __restrict__ d
                                                      const uint16_t* __restrict__ meta,
                                                      const int32_t* __restrict__ tidx,
                                                      const uint16_t* __restrict__ x,
-                                                     void* __restrict__ y, GemvDims d, int32_t full) {
+                                                     void* __restrict__ y, GemvDims d) {
+  __shared__ GemvSmem<MT, B2, META, WAVES, XR> sm;
+  gemv_slab<MT, B2, DT, META, WAVES, STAGES, LR, XR>(dense, val, meta, tidx, x, y, d, blockIdx.x, sm);
+}
+
+// The mixed launch: workgroups below full take whole slabs as k_gemv does;
+// the others are half slabs, slab full + (b - full) / 2, half (b - full) % 2,
+// with a ring one stage deeper, which keeps as many weight bytes in flight
+// per workgroup as a whole slab with the shallower ring.  A kernel of its
+// own, because the deeper ring's registers would lower k_gemv's occupancy
+// where no slab is split.
+template <int MT, int B2, int DT, int META, int WAVES, int STAGES, bool LR, bool XR>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_mixed(const uint4* __restrict__ dense,
+                                                           const uint4* __restrict__ val,
+                                                           const uint16_t* __restrict__ meta,
+                                                           const int32_t* __restrict__ tidx,
+                                                           const uint16_t* __restrict__ x,
+                                                           void* __restrict__ y, GemvDims d, int32_t full) {
   __shared__ GemvSmem<MT, B2, META, WAVES, XR> sm;
   const int32_t b = blockIdx.x;
-  if constexpr (XR) {
-    // Workgroups past full are half slabs: slab full + (b - full) / 2, half
-    // (b - full) % 2, with a ring one stage deeper, which keeps as many
-    // weight bytes in flight per workgroup as a whole slab with the
-    // shallower ring.
-    if (b >= full) {
-      gemv_slab<MT, B2, DT, META, WAVES, STAGES + 1, LR, XR>(dense, val, meta, tidx, x, y, d,
-                                                             full + ((b - full) >> 1), sm, (b - full) & 1);
-      return;
-    }
+  if (b < full) {
+    gemv_slab<MT, B2, DT, META, WAVES, STAGES, LR, XR>(dense, val, meta, tidx, x, y, d, b, sm);
+  } else {
+    gemv_slab<MT, B2, DT, META, WAVES, STAGES + 1, LR, XR>(dense, val, meta, tidx, x, y, d,
+                                                           full + ((b - full) >> 1), sm, (b - full) & 1);
   }
-  gemv_slab<MT, B2, DT, META, WAVES, STAGES, LR, XR>(dense, val, meta, tidx, x, y, d, b, sm);
 }
 
 // Grouped decode product: one launch multiplies the same x by up to
@@ -423,46 +438,78 @@ bool gemv_xr(int64_t tiles_k, int b2, int waves, int m) {
   return m <= kXrMaxM && waves == kGemvWaves && (tiles_k + waves - 1) / waves <= max_tiles;
 }
 
-template <int MT, int DT, int META, bool LR, int W, bool XR = false>
-void gemv_b2(int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d, int32_t full = INT32_MAX) {
+// Workgroups of k_gemv_mixed one CU holds at once (0 if the query fails),
+// taken once per instantiation: every device this library runs on is gfx950.
+template <int MT, int B2, int DT, int META, int W, bool LR, bool XR>
+int gemv_mixed_per_cu() {
+  static const int n = [] {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &v, reinterpret_cast<const void*>(k_gemv_mixed<MT, B2, DT, META, W, kGemvStages, LR, XR>), 64 * W, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      v = 0;
+    }
+    return v;
+  }();
+  return n;
+}
+
+// One decode launch over `slabs` slabs.  Where full < slabs and the kernel
+// has the half body, the mixed launch (full whole slabs, 2 (slabs - full)
+// halves) runs if all its workgroups are resident at once; otherwise k_gemv
+// over whole slabs.
+template <int MT, int B2, int DT, int META, bool LR, int W, bool XR>
+void gemv_launch(int64_t slabs, int64_t full, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
   const dim3 block(64 * W);
+  if constexpr (gemv_has_halves(MT, W)) {
+    const int64_t wgs = full + 2 * (slabs - full);
+    if (full < slabs && wgs <= int64_t(gemv_mixed_per_cu<MT, B2, DT, META, W, LR, XR>()) * device_cus()) {
+      hipLaunchKernelGGL((k_gemv_mixed<MT, B2, DT, META, W, kGemvStages, LR, XR>), dim3(unsigned(wgs)), block, 0, s,
+                         q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, int32_t(full));
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gemv<MT, B2, DT, META, W, kGemvStages, LR, XR>), dim3(unsigned(slabs)), block, 0, s, q.dense,
+                     q.val, q.meta, q.tidx, q.x, q.y, d);
+}
+
+template <int MT, int DT, int META, bool LR, int W, bool XR = false>
+void gemv_b2(int b2, int64_t slabs, int64_t full, hipStream_t s, const GemvPtrs& q, const GemvDims& d) {
   switch (b2) {
     case 64:
-      hipLaunchKernelGGL((k_gemv<MT, 64, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, full);
-      break;
+      return gemv_launch<MT, 64, DT, META, LR, W, XR>(slabs, full, s, q, d);
     case 128:
-      hipLaunchKernelGGL((k_gemv<MT, 128, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, full);
-      break;
+      return gemv_launch<MT, 128, DT, META, LR, W, XR>(slabs, full, s, q, d);
     default:
-      hipLaunchKernelGGL((k_gemv<MT, 256, DT, META, W, kGemvStages, LR, XR>), grid, block, 0, s, q.dense, q.val, q.meta, q.tidx, q.x, q.y, d, full);
-      break;
+      return gemv_launch<MT, 256, DT, META, LR, W, XR>(slabs, full, s, q, d);
   }
 }
 
 // MT-token variant with the wavefront count of gemv_waves; x staged per
 // wavefront range (XR) where gemv_xr allows it.
 template <int MT, int DT, int META, bool LR>
-void gemv_w(int waves, bool xr, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d,
-            int32_t full) {
+void gemv_w(int waves, bool xr, int b2, int64_t slabs, int64_t full, hipStream_t s, const GemvPtrs& q,
+            const GemvDims& d) {
   if constexpr (MT <= 4) {
-    if (waves == 8) return gemv_b2<MT, DT, META, LR, 8>(b2, grid, s, q, d);
+    if (waves == 8) return gemv_b2<MT, DT, META, LR, 8>(b2, slabs, slabs, s, q, d);
   } else {
-    if (waves == 16) return gemv_b2<MT, DT, META, LR, 16>(b2, grid, s, q, d);
+    if (waves == 16) return gemv_b2<MT, DT, META, LR, 16>(b2, slabs, slabs, s, q, d);
   }
   if constexpr (MT <= kXrMaxM) {
-    if (xr) return gemv_b2<MT, DT, META, LR, kGemvWaves, true>(b2, grid, s, q, d, full);
+    if (xr) return gemv_b2<MT, DT, META, LR, kGemvWaves, true>(b2, slabs, full, s, q, d);
   }
-  gemv_b2<MT, DT, META, LR, kGemvWaves>(b2, grid, s, q, d);
+  gemv_b2<MT, DT, META, LR, kGemvWaves>(b2, slabs, full, s, q, d);
 }
 
 template <int DT, int META, bool LR>
-void gemv_mt(int m, int waves, bool xr, int b2, dim3 grid, hipStream_t s, const GemvPtrs& q, const GemvDims& d,
-             int32_t full) {
-  if (m <= 1) gemv_w<1, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
-  else if (m <= 2) gemv_w<2, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
-  else if (m <= 4) gemv_w<4, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
-  else if (m <= 8) gemv_w<8, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
-  else gemv_w<16, DT, META, LR>(waves, xr, b2, grid, s, q, d, full);
+void gemv_mt(int m, int waves, bool xr, int b2, int64_t slabs, int64_t full, hipStream_t s, const GemvPtrs& q,
+             const GemvDims& d) {
+  if (m <= 1) gemv_w<1, DT, META, LR>(waves, xr, b2, slabs, full, s, q, d);
+  else if (m <= 2) gemv_w<2, DT, META, LR>(waves, xr, b2, slabs, full, s, q, d);
+  else if (m <= 4) gemv_w<4, DT, META, LR>(waves, xr, b2, slabs, full, s, q, d);
+  else if (m <= 8) gemv_w<8, DT, META, LR>(waves, xr, b2, slabs, full, s, q, d);
+  else gemv_w<16, DT, META, LR>(waves, xr, b2, slabs, full, s, q, d);
 }
 
 }  // namespace
@@ -492,17 +539,17 @@ hipError_t launch_gemv_impl(const hyb_layout& L, const hyb_packed& P, const void
   const int64_t slabs = L.n / 16;
   const int w = gemv_waves(slabs, m);
   const bool xr = gemv_xr(L.tiles_k, L.b2, w, m);
-  // with x staged per range the last round's slabs may run as halves
-  const int64_t full = xr ? gemv_full_slabs(slabs, device_cus()) : slabs;
-  const dim3 grid(unsigned(full + 2 * (slabs - full)));
+  // slabs the last round may run as halves (only kernels with the half
+  // body, and only where the mixed launch fits, take them)
+  const int64_t full = gemv_full_slabs(slabs, device_cus());
   if (L.dtype == HYB_BF16) {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
-    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
-    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_BF16, HYB_META_IDX2, LR>(m, w, xr, L.b2, slabs, full, s, q, d);
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_BF16, HYB_META_MASK4, LR>(m, w, xr, L.b2, slabs, full, s, q, d);
+    else gemv_mt<HYB_BF16, HYB_META_MASK8, LR>(m, w, xr, L.b2, slabs, full, s, q, d);
   } else {
-    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
-    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
-    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, w, xr, L.b2, grid, s, q, d, int32_t(full));
+    if (L.meta == HYB_META_IDX2) gemv_mt<HYB_F16, HYB_META_IDX2, LR>(m, w, xr, L.b2, slabs, full, s, q, d);
+    else if (L.meta == HYB_META_MASK4) gemv_mt<HYB_F16, HYB_META_MASK4, LR>(m, w, xr, L.b2, slabs, full, s, q, d);
+    else gemv_mt<HYB_F16, HYB_META_MASK8, LR>(m, w, xr, L.b2, slabs, full, s, q, d);
   }
   return hipGetLastError();
 }

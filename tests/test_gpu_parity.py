@@ -312,10 +312,13 @@ def test_gemv_lowrank(rank, m, b1, b2, dtype, meta):
 @pytest.mark.parametrize("rem,m,b1,b2,dtype,meta", [(4, 1, 64, 128, "bf16", "idx2"),
                                                     (64, 2, 64, 256, "f16", "mask4"),
                                                     (128, 1, 128, 128, "bf16", "idx2"),
-                                                    (132, 2, 64, 64, "bf16", "mask8")])
+                                                    (132, 2, 64, 64, "bf16", "mask8"),
+                                                    (64, 4, 64, 128, "bf16", "idx2"),
+                                                    (128, 3, 128, 256, "f16", "mask4")])
 def test_gemv_half_slab_last_round(rem, m, b1, b2, dtype, meta):
     """Decode over 2 C + rem slabs (C = the device's compute units): where
-    2 rem <= C the last round's slabs run as 8-row halves.  Bitwise equal to
+    2 rem <= C (and the mixed launch fits on the CUs at once) the last
+    round's slabs run as 8-row halves.  Bitwise equal to
     the grouped launch (whole slabs only), the low-rank entry point with
     U = 0 bitwise equal too, and both products against the oracle."""
     torch = _torch()
