@@ -344,6 +344,56 @@ def test_gemv_half_slab_last_round(rem, m, b1, b2, dtype, meta):
     assert_close(yl.cpu().numpy(), lref, ls, what="gemv lowrank half slabs")
 
 
+_CAPTURE_FIRST = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+from matmul_pack_b1_amd import binding as hb
+from matmul_pack_b1_amd import workloads as wl
+cus = torch.cuda.get_device_properties(0).multi_processor_count
+n, k, b1, b2 = (2 * cus + 96) * 16, 2048, 64, 256
+rng = np.random.default_rng(5)
+w_bits = wl.float32_to_bits(rng.standard_normal((n, k)).astype(np.float32) * 0.02, "f16")
+tmap = (rng.random((n // b1, k // b2)) < 0.6).astype(np.uint8)
+dev = torch.device("cuda:0")
+w = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.float16)
+P = hb.pack(w, tmap, b1, b2, "mask8")
+x = torch.from_numpy(rng.standard_normal((1, k)).astype(np.float32)).to(dev).half()
+out = torch.empty(1, n, device=dev)
+torch.cuda.synchronize()
+s = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=s):
+    hb.gemv(P, x, out=out)
+reps = []
+for _ in range(3):
+    g.replay()
+    torch.cuda.synchronize()
+    reps.append(out.clone())
+    out.zero_()
+    torch.cuda.synchronize()
+ye = hb.gemv(P, x)
+torch.cuda.synchronize()
+assert all(torch.equal(r, ye) for r in reps), "replay differs from the eager product"
+assert bool(torch.isfinite(ye).all())
+print("capture-first ok", flush=True)
+"""
+
+
+def test_gemv_mixed_launch_first_call_under_capture():
+    """The mixed decode launch looks up its occupancy on its first call; in a
+    fresh process that first call is made under graph capture (fp16 weights,
+    mask8 codes, b2 = 256, 2 C + 96 slabs).  Three replays, with eager work
+    between them, equal the eager product bitwise."""
+    import os
+    import subprocess
+    note("gemv mixed launch, first call under graph capture (subprocess)")
+    repo = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, repo], capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and "capture-first ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
+
+
 @pytest.mark.parametrize("rank,k,m,dtype", [(64, 4096, 1, "bf16"), (64, 4096, 16, "bf16"), (1, 72, 3, "f16"),
                                              (256, 5120, 40, "bf16"), (8, 2056, 17, "f16"), (20, 5120, 300, "bf16"),
                                              (64, 1024, 2048, "f16")])
