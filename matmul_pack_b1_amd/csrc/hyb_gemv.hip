@@ -187,15 +187,6 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<MT, B2, XR>& st, in
   }
 }
 
-// The product of one 16-row slab (the whole work of one workgroup).  With
-// LR the slab also adds the low-rank term sum_j T[m][j] U[row][j] (3BASiL,
-// gist.science, section 1: W ~ S + L with L of rank r, here L = U V^T and
-// T = X V given): wavefront 0's lanes take row L%16 and every fourth
-// 8-column chunk of the rank, and add their partial dot products into the
-// row sums before the lane and wavefront reduction, so the order of the
-// additions stays fixed.
-// With XR the wavefront's whole tile range (at most kXrTiles tiles) has its
-// x columns staged once, before the first weight loads.
 // Decode kernels that have a mixed launch: one token, four wavefronts per
 // slab.  (At two and four tokens the mixed launch measured no faster.)
 __host__ __device__ constexpr bool gemv_has_halves(int mt, int waves) { return waves == kGemvWaves && mt == 1; }
@@ -211,12 +202,21 @@ struct GemvSmem {
   float red[WAVES][MT][16];
 };
 
-// half >= 0 takes only rows 8 half .. 8 half + 7 of the slab: the other
-// rows' lanes (the four lanes of a row are all in or all out) get weight
-// offsets past the end of every resource, so they load nothing, and their
-// rows are not stored.  The rows taken see the same loads in the same order
-// as with half < 0, so their results are bitwise equal.  x comes through
-// the real lane in either case.
+// The product of one 16-row slab (the whole work of one workgroup).  With
+// LR the slab also adds the low-rank term sum_j T[m][j] U[row][j] (3BASiL,
+// gist.science, section 1: W ~ S + L with L of rank r, here L = U V^T and
+// T = X V given): wavefront 0's lanes take row L%16 and every fourth
+// 8-column chunk of the rank, and add their partial dot products into the
+// row sums before the lane and wavefront reduction, so the order of the
+// additions stays fixed.
+// With XR the wavefront's whole tile range (at most kXrTiles tiles) has its
+// x columns staged once, before the first weight loads.
+// With half >= 0 the call takes only rows 8 half .. 8 half + 7 of the
+// slab: the other rows' lanes (the four lanes of a row are all in or all
+// out) get weight offsets past the end of every resource, so they load
+// nothing, and their rows are not stored.  The rows taken see the same
+// loads in the same order as with half < 0, so their results are bitwise
+// equal.  x comes through the real lane in either case.
 template <int MT, int B2, int DT, int META, int WAVES, int STAGES, bool LR = false, bool XR = false>
 __device__ __forceinline__ void gemv_slab(const uint4* __restrict__ dense, const uint4* __restrict__ val,
                                           const uint16_t* __restrict__ meta, const int32_t* __restrict__ tidx,
